@@ -1,0 +1,260 @@
+"""Plain CPU oracle for the forward pass of a capacity-limited Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check of the
+entry module and the CPU-baseline leg of the benchmark may import or call this module.
+The product path (the HIP library and its Python binding) never touches it, and this
+module imports nothing from the product package.
+
+Everything here is written from the pages' description of the method, in float64,
+in the order the pages give the steps, with no blocking, fusion or reordering beyond
+what a library primitive (matmul, sort) does internally:
+
+  * "Expert Networks > Worked Example: Expert Specialization" (mbrenndoerfer.com):
+    top-1 routing of 8 tokens to 4 experts, capacity from the capacity factor
+    rounded down, the lowest-confidence token of an overloaded expert dropped, the
+    expert FFN as up-projection, SiLU, down-projection, and the output of a kept
+    token as the residual plus the confidence-weighted expert output; a dropped
+    token leaves the layer unchanged.
+  * "Some Tokens Do Not Get In" (getbasislab.com), sections "Why there is a buffer"
+    and "Past the edge": t*k token slots, one fixed buffer per expert sized by the
+    capacity factor, tokens placed in some order, overflow tokens take the residual
+    path and reach the next layer exactly as they entered.
+  * "Dynamic Token Routing AI" (freenetmedia.pl), "How it works": a gating network
+    scores each token and selects the expert(s).
+
+Where the pages leave a step open, the reading taken is stated in the docstring of
+the function that takes it (softmax over all experts, unrenormalised top-k gates,
+fill order gate-descending then token then choice, float64 logits of exact products).
+
+Every floating-point input is taken as float64 holding the exact value of the stored
+(bf16 or fp32) number; the caller does that conversion.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "capacity",
+    "router_logits",
+    "softmax",
+    "gates_fp32",
+    "top_k",
+    "route",
+    "dispatch",
+    "silu",
+    "expert_ffn",
+    "expert_ffn_slots",
+    "combine",
+    "forward",
+    "forward_with_routing",
+]
+
+
+def capacity(T: int, top_k: int, n_experts: int, capacity_factor: float) -> int:
+    """Per-expert slot budget: floor(C * T * k / E), computed as an exact rational.
+
+    Worked Example (capacity paragraph): C = 1.25, 8 tokens over 4 experts gives 2.5,
+    which is rounded down to 2.  "Some Tokens Do Not Get In", "Why there is a buffer":
+    the number of slots to fill is t times k, spread over the experts with slack set by
+    the capacity factor.  No lower clamp: the budget may be 0.
+    """
+    if T < 0 or top_k < 1 or n_experts < 1 or capacity_factor < 0:
+        raise ValueError("bad capacity arguments")
+    return math.floor(Fraction(capacity_factor) * T * top_k / n_experts)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, b_router: np.ndarray | None) -> np.ndarray:
+    """Router scores L[t, e] = sum_j x[t, j] * W_r[e, j] + b_r[e], in float64.
+
+    "Dynamic Token Routing AI", "How it works": the gating network scores each token.
+    The pages leave the score function open; it is read as a linear map plus an
+    optional per-expert bias.  Products of two bf16 or two fp32 values are exact in
+    float64, so only the summation rounds.
+    """
+    L = np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+    if b_router is not None:
+        L = L + np.asarray(b_router, dtype=np.float64)[None, :]
+    return L
+
+
+def softmax(L: np.ndarray) -> np.ndarray:
+    """Row-wise softmax over all experts, float64: exp(L - max) / sum(exp(L - max)).
+
+    The pages call the gate a router confidence (Worked Example, trace of token 0); it is
+    read as the softmax probability over all E experts.
+    """
+    m = L.max(axis=1, keepdims=True)
+    z = np.exp(L - m)
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def gates_fp32(p: np.ndarray) -> np.ndarray:
+    """Round the float64 probabilities once to float32 (round to nearest even)."""
+    return p.astype(np.float32)
+
+
+def top_k(g32: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Pick the k experts with the largest fp32 gate; ties go to the lower expert index.
+
+    Choice c = 0 is the largest gate.  The gate values are returned as they are, with no
+    renormalisation over the chosen k (the Worked Example scales the expert output by the
+    router confidence itself).
+    """
+    T, E = g32.shape
+    if not 1 <= k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    e_idx = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: last key is primary -> descending gate, then ascending expert index
+    order = np.lexsort((e_idx, -g32.astype(np.float64)), axis=1)
+    ids = order[:, :k].astype(np.int32)
+    gates = np.take_along_axis(g32, ids, axis=1).astype(np.float32)
+    return ids, gates
+
+
+def route(x, w_router, b_router, k):
+    """Router step: logits, softmax probabilities, fp32 gates, top-k ids and gates."""
+    L = router_logits(x, w_router, b_router)
+    p = softmax(L)
+    g32 = gates_fp32(p)
+    ids, gates = top_k(g32, k)
+    return {"logits": L, "probs": p, "gates_all": g32, "ids": ids, "gates": gates}
+
+
+def dispatch(ids: np.ndarray, gates: np.ndarray, n_experts: int, cap: int) -> dict:
+    """Fill each expert's fixed buffer and mark the overflow as dropped.
+
+    Worked Example (capacity paragraph): the token with the lowest router confidence among
+    an overloaded expert's tokens is the one that does not fit.  "Some Tokens Do Not Get
+    In", "Past the edge": tokens take their expert's slots in some order and the first one
+    to find the buffer full is turned away.  The order is read as: gate descending, then
+    token index ascending, then choice rank ascending, over all choice ranks together.
+
+    Slots are numbered compactly: expert e owns slots [off[e], off[e] + kept[e]) with
+    off[e] = sum of kept[e'] for e' < e, and the assignment of rank r gets slot off[e] + r.
+    """
+    T, k = ids.shape
+    per_expert: list[list[tuple[float, int, int]]] = [[] for _ in range(n_experts)]
+    for t in range(T):
+        for c in range(k):
+            e = int(ids[t, c])
+            if not 0 <= e < n_experts:
+                raise ValueError(f"expert id {e} out of range")
+            per_expert[e].append((float(gates[t, c]), t, c))
+
+    counts = np.array([len(a) for a in per_expert], dtype=np.int32)
+    kept = np.minimum(counts, cap).astype(np.int32)
+    offsets = np.zeros(n_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(kept)
+
+    slot_of = np.full((T, k), -1, dtype=np.int32)
+    rank = np.full((T, k), -1, dtype=np.int64)
+    row_token = np.full(int(offsets[-1]), -1, dtype=np.int32)
+    for e in range(n_experts):
+        ordered = sorted(per_expert[e], key=lambda a: (-a[0], a[1], a[2]))
+        for r, (_, t, c) in enumerate(ordered):
+            rank[t, c] = r
+            if r < cap:
+                s = int(offsets[e]) + r
+                slot_of[t, c] = s
+                row_token[s] = t
+    drop_mask = (slot_of < 0).astype(np.uint8)
+    return {
+        "counts": counts,
+        "kept": kept,
+        "offsets": offsets,
+        "slot_of": slot_of,
+        "rank": rank,
+        "row_token": row_token,
+        "drop_mask": drop_mask,
+        "n_kept": int(offsets[-1]),
+    }
+
+
+def silu(h: np.ndarray) -> np.ndarray:
+    """SiLU(h) = h * sigmoid(h), evaluated without overflow for large |h|."""
+    h = np.asarray(h, dtype=np.float64)
+    e = np.exp(-np.abs(h))
+    sig = np.where(h >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return h * sig
+
+
+def expert_ffn(x_rows: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """One expert on a batch of rows: y = W2 . SiLU(W1 . x + b1) + b2, float64.
+
+    Worked Example (trace of token 0): up-projection d_model -> d_ff with bias, SiLU
+    element-wise, down-projection d_ff -> d_model with bias.  W1 is [d_ff, d_model] and W2
+    is [d_model, d_ff], so W1 . x is the matrix-vector product the trace writes.
+    """
+    h = x_rows @ np.asarray(w1, dtype=np.float64).T + np.asarray(b1, dtype=np.float64)[None, :]
+    a = silu(h)
+    return a @ np.asarray(w2, dtype=np.float64).T + np.asarray(b2, dtype=np.float64)[None, :]
+
+
+def expert_ffn_slots(x, row_token, offsets, w1, b1, w2, b2, slots=None) -> np.ndarray:
+    """Expert outputs per slot: Y[s] = FFN_e(x[row_token[s]]) for the expert e owning slot s.
+
+    With `slots` given, only those slots are computed (in the given order); this is what the
+    large configurations use to check sampled rows.  Weights are indexed per expert, so a
+    caller may pass lazily converted per-expert arrays (anything supporting w1[e]).
+    """
+    offsets = np.asarray(offsets)
+    E = len(offsets) - 1
+    n_kept = int(offsets[-1])
+    if slots is None:
+        slots = np.arange(n_kept)
+    slots = np.asarray(slots, dtype=np.int64)
+    d = x.shape[1]
+    out = np.zeros((len(slots), d), dtype=np.float64)
+    expert_of = np.searchsorted(offsets, slots, side="right") - 1
+    for e in range(E):
+        sel = np.nonzero(expert_of == e)[0]
+        if len(sel) == 0:
+            continue
+        rows = np.asarray(x, dtype=np.float64)[np.asarray(row_token)[slots[sel]]]
+        out[sel] = expert_ffn(rows, w1[e], b1[e], w2[e], b2[e])
+    return out
+
+
+def combine(x: np.ndarray, gates: np.ndarray, slot_of: np.ndarray, Y: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """out[t] = x[t] + sum over kept choices c (ascending) of gates[t, c] * Y[slot_of[t, c]].
+
+    Worked Example: a kept token's output is its residual plus the confidence-scaled
+    expert output; the dropped token's output is its input plus nothing.  With k > 1 the
+    kept choices are summed and the gates are not renormalised when some choice drops.
+    Returns the float64 output and a mask of tokens with no kept choice; for those rows
+    the layer output is the input itself, bit for bit ("Past the edge": the token reaches
+    the next layer exactly as it entered).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    out = x64.copy()
+    T, k = slot_of.shape
+    for c in range(k):
+        kept = slot_of[:, c] >= 0
+        if np.any(kept):
+            out[kept] = out[kept] + gates[kept, c].astype(np.float64)[:, None] * Y[slot_of[kept, c]]
+    all_dropped = np.all(slot_of < 0, axis=1)
+    return out, all_dropped
+
+
+def forward_with_routing(x, ids, gates, cap, n_experts, w1, b1, w2, b2) -> dict:
+    """Layer forward from a given routing (ids, gates): dispatch, expert FFN, combine."""
+    disp = dispatch(ids, gates, n_experts, cap)
+    Y = expert_ffn_slots(x, disp["row_token"], disp["offsets"], w1, b1, w2, b2)
+    out, all_dropped = combine(x, gates, disp["slot_of"], Y)
+    res = dict(disp)
+    res.update({"ids": ids, "gates": gates, "cap": cap, "Y": Y, "out": out, "all_dropped": all_dropped})
+    return res
+
+
+def forward(x, w_router, b_router, w1, b1, w2, b2, k: int, capacity_factor: float) -> dict:
+    """Whole layer: route, capacity, dispatch, expert FFN, combine."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    cap = capacity(T, k, E, capacity_factor)
+    res = forward_with_routing(x, r["ids"], r["gates"], cap, E, w1, b1, w2, b2)
+    res.update({"logits": r["logits"], "probs": r["probs"], "gates_all": r["gates_all"]})
+    return res

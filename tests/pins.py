@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each check takes the oracle module as its argument, so the same checks run against the
+real oracle (tests/test_oracle_pins.py) and against copies with planted mistakes
+(tests/test_oracle_mutations.py), which must each fail at least one check.
+
+What pins what:
+  * the worked example's printed numbers (tests/golden/worked_example.json, cited to
+    "Expert Networks > Worked Example: Expert Specialization"): capacity 2, expert 0's
+    overflow drops token 4, the kept batches, dropped output equal to the input;
+  * closed forms: softmax of (0, ln2, ln3, ln4) is (0.1, 0.2, 0.3, 0.4); one expert gives
+    gate 1; equal logits give 1/E; SiLU(ln 3) = 0.75 ln 3; exact-rational capacities;
+  * library routines: torch float64 linear/SiLU for the expert FFN and the dense
+    special case, scipy's softmax;
+  * brute force: integer-valued router logits summed exactly in Python integers; top-k by
+    enumerating all k-subsets; slot ranks by an independent counting definition;
+  * invariants: counts sum to T*k, slot map is a bijection, kept gates dominate dropped
+    gates, permutation equivariance, capacity 0 returns the input.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)["facts"]
+
+
+# Gates for the worked example's forced assignment.  The page fixes the assignment, the
+# value 0.87 for token 0 and that token 4 has the lowest confidence on expert 0; the other
+# values are a choice consistent with those facts.
+FORCED_GATES = [0.87, 0.62, 0.71, 0.55, 0.48, 0.66, 0.59, 0.93]
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _torch_ffn(x_rows, w1, b1, w2, b2):
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    h = F.linear(t(x_rows), t(w1), t(b1))
+    return F.linear(F.silu(h), t(w2), t(b2)).numpy()
+
+
+def _rand_weights(rng, E, d, f, scale=1.0):
+    w1 = rng.standard_normal((E, f, d)) * scale / math.sqrt(d)
+    b1 = rng.standard_normal((E, f)) * 0.1
+    w2 = rng.standard_normal((E, d, f)) * scale / math.sqrt(f)
+    b2 = rng.standard_normal((E, d)) * 0.1
+    return w1, b1, w2, b2
+
+
+# ----------------------------------------------------------------------------- capacity
+def check_capacity_page(o):
+    g = golden()
+    L = g["layer"]
+    assert o.capacity(L["T"], L["top_k"], L["n_experts"], g["capacity_factor"]["value"]) == g["capacity"]["value"]
+
+
+def check_capacity_closed_forms(o):
+    # floor(C*T*k/E) for the four bf16 workloads
+    assert o.capacity(4096, 2, 8, 1.25) == 1280
+    assert o.capacity(16384, 6, 64, 1.0) == 1536
+    assert o.capacity(64, 2, 8, 4.0) == 64
+    assert o.capacity(32768, 2, 8, 2.0) == 16384
+    # small budgets round down to zero, no lower clamp
+    assert o.capacity(4, 1, 8, 0.1) == 0
+    assert o.capacity(7, 1, 8, 1.0) == 0
+    assert o.capacity(8, 1, 8, 1.0) == 1
+    # exact rational value of the stored double: 0.7 is stored slightly below 7/10, so
+    # 0.7 * 10 / 7 is just under 1 and floors to 0 (double arithmetic would give 1)
+    assert Fraction(0.7) < Fraction(7, 10)
+    assert o.capacity(10, 1, 7, 0.7) == 0
+    # 1.1 is stored slightly above 11/10
+    assert o.capacity(10, 1, 1, 1.1) == 11
+    # brute-force definition: the largest n with n * E <= C*T*k
+    rng = _rng(11)
+    for _ in range(200):
+        T = int(rng.integers(0, 5000)); k = int(rng.integers(1, 9)); E = int(rng.integers(1, 300))
+        C = float(rng.choice([0.5, 0.75, 1.0, 1.25, 1.5, 2.0, 3.3, 0.1]))
+        n = o.capacity(T, k, E, C)
+        assert n >= 0
+        assert Fraction(n) * E <= Fraction(C) * T * k < Fraction(n + 1) * E
+
+
+# ----------------------------------------------------------------------------- routing
+def check_softmax_closed_forms(o):
+    L = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    p = o.softmax(L)
+    assert np.max(np.abs(p - np.array([[0.1, 0.2, 0.3, 0.4]]))) < 4e-16
+    assert o.softmax(np.array([[3.7]]))[0, 0] == 1.0
+    p = o.softmax(np.full((1, 5), -2.25))
+    assert np.all(np.abs(p - 0.2) < 1e-16)
+    # shift invariance at large magnitude (no overflow)
+    p = o.softmax(np.array([[1000.0, 1001.0]]))
+    assert abs(p[0, 0] - 1.0 / (1.0 + math.e)) < 1e-15 and abs(p[0, 1] - math.e / (1.0 + math.e)) < 1e-15
+    from scipy.special import softmax as sp_softmax
+    Lr = _rng(3).standard_normal((50, 13)) * 4
+    assert np.max(np.abs(o.softmax(Lr) - sp_softmax(Lr, axis=1))) < 1e-15
+
+
+def check_router_logits_exact(o):
+    """Integer-valued inputs: every partial sum is an exactly representable integer."""
+    rng = _rng(5)
+    for (T, d, E) in [(6, 4, 4), (5, 7, 3), (3, 33, 9)]:
+        x = rng.integers(-50, 50, size=(T, d)).astype(np.float64)
+        w = rng.integers(-50, 50, size=(E, d)).astype(np.float64)
+        b = rng.integers(-9, 9, size=E).astype(np.float64)
+        L = o.router_logits(x, w, b)
+        for t in range(T):
+            for e in range(E):
+                want = sum(int(x[t, j]) * int(w[e, j]) for j in range(d)) + int(b[e])
+                assert L[t, e] == want
+
+
+def _topk_brute(g_row, k):
+    E = len(g_row)
+    beats = lambda a, b: (g_row[a] > g_row[b]) or (g_row[a] == g_row[b] and a < b)
+    winners = []
+    for S in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in S]
+        if all(beats(a, b) for a in S for b in rest):
+            winners.append(S)
+    assert len(winners) == 1
+    chosen = list(winners[0])
+    # order inside the chosen set: by how many chosen elements beat it (0 for the first)
+    return sorted(chosen, key=lambda e: sum(bool(beats(o2, e)) for o2 in chosen))
+
+
+def check_topk_bruteforce(o):
+    rng = _rng(7)
+    vals = np.array([0.125, 0.25, 0.25, 0.375, 0.5], dtype=np.float32)
+    for E in range(1, 7):
+        for k in range(1, E + 1):
+            for _ in range(25):
+                g = vals[rng.integers(len(vals), size=(1, E))]
+                ids, gates = o.top_k(g, k)
+                want = _topk_brute(g[0], k)
+                assert list(ids[0]) == want, (g, k, ids, want)
+                assert np.array_equal(gates[0], g[0, want])
+
+
+def check_gates_unrenormalised(o):
+    """Top-k gates are the softmax probabilities themselves (scipy), rounded to fp32."""
+    from scipy.special import softmax as sp_softmax
+    rng = _rng(9)
+    x = rng.standard_normal((40, 16))
+    w = rng.standard_normal((6, 16)) / 4
+    r = o.route(x, w, None, 2)
+    p = sp_softmax(x @ w.T, axis=1)
+    for t in range(40):
+        for c in range(2):
+            assert abs(float(r["gates"][t, c]) - p[t, r["ids"][t, c]]) <= 6e-8 * p[t, r["ids"][t, c]] + 1e-30
+        assert r["gates"][t, 0] >= r["gates"][t, 1]
+        assert r["ids"][t, 0] == int(np.argmax(p[t]))
+    # with 6 experts the two chosen gates cannot sum to one
+    assert np.all(r["gates"].astype(np.float64).sum(axis=1) < 1.0)
+
+
+# ----------------------------------------------------------------------------- dispatch
+def _counting_ranks(ids, gates, E, cap):
+    """Independent definition: rank = number of same-expert assignments ahead in the order
+    (larger gate, or equal gate and smaller token, or same token and smaller choice)."""
+    T, k = ids.shape
+    rank = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for c in range(k):
+            e = ids[t, c]; g = float(gates[t, c])
+            r = 0
+            for t2 in range(T):
+                for c2 in range(k):
+                    if ids[t2, c2] != e or (t2, c2) == (t, c):
+                        continue
+                    g2 = float(gates[t2, c2])
+                    if g2 > g or (g2 == g and (t2, c2) < (t, c)):
+                        r += 1
+            rank[t, c] = r
+    counts = np.array([(ids == e).sum() for e in range(E)])
+    kept = np.minimum(counts, cap)
+    off = np.concatenate([[0], np.cumsum(kept)])
+    slot = np.where(rank < cap, off[ids] + rank, -1)
+    return rank, slot, counts, off
+
+
+def check_worked_example_dispatch(o):
+    g = golden()
+    ids = np.array(g["assignment"]["ids"], dtype=np.int32)[:, None]
+    gates = np.array(FORCED_GATES, dtype=np.float32)[:, None]
+    cap = g["capacity"]["value"]
+    d = o.dispatch(ids, gates, 4, cap)
+    assert d["counts"][0] == g["expert0_load"]["value"]
+    assert list(np.nonzero(d["drop_mask"][:, 0])[0]) == [g["dropped_token"]["value"]]
+    kept_sets = []
+    for e in range(4):
+        s0, s1 = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        kept_sets.append(sorted(int(t) for t in d["row_token"][s0:s1]))
+    assert kept_sets == [sorted(b) for b in g["kept_batches"]["value"]]
+    assert max(e1 - e0 for e0, e1 in zip(d["offsets"][:-1], d["offsets"][1:])) == g["slowest_expert_rows"]["value"]
+
+
+def check_dispatch_exhaustive(o):
+    vals = [0.25, 0.5, 0.75]
+    # k = 1: every id pattern and every gate pattern for T = 4 tokens over E = 3 experts
+    for T, E in [(3, 2), (4, 3)]:
+        for id_pat in itertools.product(range(E), repeat=T):
+            ids = np.array(id_pat, dtype=np.int32)[:, None]
+            for g_pat in itertools.product(vals, repeat=T):
+                gates = np.array(g_pat, dtype=np.float32)[:, None]
+                for cap in (0, 1, 2, T):
+                    d = o.dispatch(ids, gates, E, cap)
+                    rank, slot, counts, off = _counting_ranks(ids, gates, E, cap)
+                    assert np.array_equal(d["slot_of"], slot)
+                    assert np.array_equal(d["counts"], counts)
+                    assert np.array_equal(d["offsets"], off)
+    # k = 2: random ordered pairs of distinct experts and tied gates
+    rng = _rng(13)
+    for _ in range(400):
+        T = int(rng.integers(1, 6)); E = int(rng.integers(2, 5)); k = 2
+        ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32)
+        gates = np.array(vals, dtype=np.float32)[rng.integers(3, size=(T, k))]
+        cap = int(rng.integers(0, T + 1))
+        d = o.dispatch(ids, gates, E, cap)
+        rank, slot, counts, off = _counting_ranks(ids, gates, E, cap)
+        assert np.array_equal(d["slot_of"], slot)
+        assert np.array_equal(d["drop_mask"], (slot < 0).astype(np.uint8))
+
+
+def check_dispatch_invariants(o):
+    rng = _rng(17)
+    for trial in range(30):
+        T = int(rng.integers(1, 300)); E = int(rng.integers(1, 12)); k = int(rng.integers(1, E + 1))
+        ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32)
+        gates = rng.choice(np.array([0.1, 0.2, 0.3, 0.7], dtype=np.float32), size=(T, k)) if trial % 2 \
+            else rng.random((T, k)).astype(np.float32)
+        cap = int(rng.integers(0, max(2, T * k // E + 3)))
+        d = o.dispatch(ids, gates, E, cap)
+        assert d["counts"].sum() == T * k
+        assert d["n_kept"] == int(np.minimum(d["counts"], cap).sum())
+        s = d["slot_of"][d["slot_of"] >= 0]
+        assert np.array_equal(np.sort(s), np.arange(d["n_kept"]))
+        for t in range(T):
+            for c in range(k):
+                if d["slot_of"][t, c] >= 0:
+                    sl = d["slot_of"][t, c]
+                    assert d["row_token"][sl] == t
+                    assert d["offsets"][ids[t, c]] <= sl < d["offsets"][ids[t, c] + 1]
+        for e in range(E):
+            m = ids == e
+            kept_g = gates[m & (d["slot_of"] >= 0)]
+            drop_g = gates[m & (d["slot_of"] < 0)]
+            if len(kept_g) and len(drop_g):
+                assert kept_g.min() >= drop_g.max()
+            # within an expert, slots run in the fill order (gate descending)
+            sl = d["slot_of"][m & (d["slot_of"] >= 0)]
+            g_by_slot = gates[m & (d["slot_of"] >= 0)][np.argsort(sl)]
+            assert np.all(np.diff(g_by_slot.astype(np.float64)) <= 0)
+
+
+def check_permutation_equivariance(o):
+    rng = _rng(19)
+    T, d, f, E, k = 40, 8, 12, 5, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    cap = o.capacity(T, k, E, 1.0)
+    a = o.forward(x, w, None, w1, b1, w2, b2, k, 1.0)
+    perm = rng.permutation(T)
+    b = o.forward(x[perm], w, None, w1, b1, w2, b2, k, 1.0)
+    assert a["cap"] == cap == b["cap"]
+    assert np.array_equal(a["drop_mask"][perm], b["drop_mask"])
+    assert np.max(np.abs(a["out"][perm] - b["out"])) < 1e-12
+
+
+# ----------------------------------------------------------------------------- FFN + combine
+def check_silu_closed_forms(o):
+    import torch
+    import torch.nn.functional as F
+    h = np.array([-800.0, -30.0, -1.5, -0.0, 0.0, 0.3, 2.0, 40.0, 800.0])
+    s = o.silu(h)
+    assert np.all(np.isfinite(s))
+    assert np.max(np.abs(s - F.silu(torch.as_tensor(h)).numpy())) < 1e-15
+    assert abs(o.silu(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15
+    assert o.silu(np.array([800.0]))[0] == 800.0
+
+
+def check_expert_ffn_vs_torch(o):
+    rng = _rng(23)
+    E, d, f = 3, 6, 10
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    xr = rng.standard_normal((7, d))
+    for e in range(E):
+        got = o.expert_ffn(xr, w1[e], b1[e], w2[e], b2[e])
+        assert np.max(np.abs(got - _torch_ffn(xr, w1[e], b1[e], w2[e], b2[e]))) < 1e-13
+
+
+def check_worked_example_outputs(o):
+    """Forced routing of the worked example: out_0 = x_0 + 0.87 y_0, out_4 = x_4 bit for bit."""
+    g = golden()
+    L = g["layer"]
+    rng = _rng(29)
+    T, d, f, E = L["T"], L["d_model"], L["d_ff"], L["n_experts"]
+    x = rng.standard_normal((T, d))
+    x[0] = g["x0"]["value"]
+    x[4, 1] = -0.0  # a negative zero must survive the residual path
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    ids = np.array(g["assignment"]["ids"], dtype=np.int32)[:, None]
+    gates = np.array(FORCED_GATES, dtype=np.float32)[:, None]
+    assert gates[0, 0] == np.float32(g["gate0"]["value"])
+    res = o.forward_with_routing(x, ids, gates, g["capacity"]["value"], E, w1, b1, w2, b2)
+    dropped = g["dropped_token"]["value"]
+    assert res["all_dropped"][dropped]
+    assert np.array_equal(res["out"][dropped], x[dropped])
+    assert np.signbit(res["out"][dropped, 1])
+    for t in range(T):
+        if t == dropped:
+            continue
+        e = ids[t, 0]
+        y = _torch_ffn(x[t:t + 1], w1[e], b1[e], w2[e], b2[e])[0]
+        want = x[t] + float(gates[t, 0]) * y
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+
+
+def check_dense_special_case(o):
+    """One expert, top-1, room for every token: gate is exactly 1 and the layer is a dense
+    residual FFN, out = x + FFN(x)."""
+    rng = _rng(31)
+    T, d, f = 9, 5, 7
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((1, d))
+    w1, b1, w2, b2 = _rand_weights(rng, 1, d, f)
+    res = o.forward(x, w, None, w1, b1, w2, b2, 1, 1.0)
+    assert np.all(res["gates"] == 1.0)
+    want = x + _torch_ffn(x, w1[0], b1[0], w2[0], b2[0])
+    assert np.max(np.abs(res["out"] - want)) < 1e-13
+
+
+def check_dropless_per_token(o):
+    """Capacity >= T: nothing drops and each token gets the gate-weighted sum of its k
+    experts (a per-token loop with torch's linear layers, independent of dispatch)."""
+    rng = _rng(37)
+    T, d, f, E, k = 12, 6, 9, 4, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    b = rng.standard_normal(E)
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    res = o.forward(x, w, b, w1, b1, w2, b2, k, float(E))
+    assert res["cap"] >= T
+    assert not res["drop_mask"].any()
+    for t in range(T):
+        want = x[t].copy()
+        for c in range(k):
+            e = res["ids"][t, c]
+            want = want + float(res["gates"][t, c]) * _torch_ffn(x[t:t + 1], w1[e], b1[e], w2[e], b2[e])[0]
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+
+
+def check_all_experts(o):
+    """k = E: every token uses every expert; with room for all, the gates sum to ~1 and
+    out = x + sum_e p_e FFN_e(x)."""
+    rng = _rng(41)
+    T, d, f, E = 6, 4, 5, 3
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    res = o.forward(x, w, None, w1, b1, w2, b2, E, 1.0)
+    assert res["cap"] == T
+    assert np.all(np.sort(res["ids"], axis=1) == np.arange(E))
+    assert np.all(np.abs(res["gates"].astype(np.float64).sum(axis=1) - 1.0) < 1e-6)
+    for t in range(T):
+        want = x[t] + sum(float(res["gates"][t, c]) * _torch_ffn(x[t:t + 1], *(a[res["ids"][t, c]] for a in (w1, b1, w2, b2)))[0]
+                          for c in range(E))
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+
+
+def check_capacity_zero(o):
+    rng = _rng(43)
+    T, d, f, E = 10, 4, 6, 8
+    x = rng.standard_normal((T, d)); x[3, 2] = -0.0
+    w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    res = o.forward(x, w, None, w1, b1, w2, b2, 1, 0.5)  # floor(0.5*10/8) = 0
+    assert res["cap"] == 0 and res["n_kept"] == 0
+    assert res["all_dropped"].all()
+    assert np.array_equal(res["out"], x) and np.signbit(res["out"][3, 2])
+
+
+ALL_CHECKS = [
+    check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
+    check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
+    check_worked_example_dispatch, check_dispatch_exhaustive, check_dispatch_invariants,
+    check_permutation_equivariance, check_silu_closed_forms, check_expert_ffn_vs_torch,
+    check_worked_example_outputs, check_dense_special_case, check_dropless_per_token,
+    check_all_experts, check_capacity_zero,
+]

@@ -1,0 +1,185 @@
+"""Plant plausible mistakes in copies of the oracle's steps; each must fail some pin.
+
+This shows the pins in tests/pins.py are strong enough that a dropped term, a wrong sign,
+a wrong index or a transposed operand in the oracle would not go unnoticed.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+import pins
+
+_orig = {name: getattr(O, name) for name in O.__all__}
+
+
+def _cap_ceil(T, k, E, C):
+    return math.ceil(Fraction(C) * T * k / E)
+
+
+def _cap_no_k(T, k, E, C):
+    return math.floor(Fraction(C) * T / E)
+
+
+def _cap_float(T, k, E, C):
+    return math.floor(C * T * k / E)
+
+
+def _logits_transposed(x, w, b):
+    L = np.asarray(x, np.float64) @ np.asarray(w, np.float64)
+    return L + np.asarray(b)[None, :] if b is not None else L
+
+
+def _logits_no_bias(x, w, b):
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def _softmax_no_norm(L):
+    return np.exp(L - L.max(axis=1, keepdims=True))
+
+
+def _softmax_wrong_axis(L):
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    return z / z.sum(axis=0, keepdims=True)
+
+
+def _topk_tie_high(g32, k):
+    T, E = g32.shape
+    e_idx = np.broadcast_to(-np.arange(E), (T, E))
+    order = np.lexsort((e_idx, -g32.astype(np.float64)), axis=1)
+    ids = order[:, :k].astype(np.int32)
+    return ids, np.take_along_axis(g32, ids, axis=1)
+
+
+def _topk_renorm(g32, k):
+    ids, gates = _orig["top_k"](g32, k)
+    return ids, (gates / gates.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _topk_ascending(g32, k):
+    T, E = g32.shape
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), g32.astype(np.float64)), axis=1)
+    ids = order[:, :k].astype(np.int32)
+    return ids, np.take_along_axis(g32, ids, axis=1)
+
+
+def _make_dispatch(sort_key=None, offsets_from_counts=False, keep_rule=None):
+    def dispatch(ids, gates, n_experts, cap):
+        T, k = ids.shape
+        per = [[] for _ in range(n_experts)]
+        for t in range(T):
+            for c in range(k):
+                per[int(ids[t, c])].append((float(gates[t, c]), t, c))
+        counts = np.array([len(a) for a in per], dtype=np.int32)
+        kept = np.minimum(counts, cap)
+        offsets = np.zeros(n_experts + 1, dtype=np.int32)
+        offsets[1:] = np.cumsum(counts if offsets_from_counts else kept)
+        slot_of = np.full((T, k), -1, dtype=np.int32)
+        row_token = np.full(int(offsets[-1]), -1, dtype=np.int32)
+        for e in range(n_experts):
+            ordered = sorted(per[e], key=sort_key or (lambda a: (-a[0], a[1], a[2])))
+            for r, (_, t, c) in enumerate(ordered):
+                if (keep_rule or (lambda r, cap: r < cap))(r, cap):
+                    s = int(offsets[e]) + r
+                    slot_of[t, c] = s
+                    if s < len(row_token):
+                        row_token[s] = t
+        return {"counts": counts, "kept": kept, "offsets": offsets, "slot_of": slot_of,
+                "rank": None, "row_token": row_token, "drop_mask": (slot_of < 0).astype(np.uint8),
+                "n_kept": int(offsets[-1])}
+    return dispatch
+
+
+def _silu_sigmoid(h):
+    return 1.0 / (1.0 + np.exp(-np.asarray(h, np.float64)))
+
+
+def _silu_relu(h):
+    return np.maximum(np.asarray(h, np.float64), 0.0)
+
+
+def _silu_sign(h):
+    h = np.asarray(h, np.float64)
+    return h / (1.0 + np.exp(h))
+
+
+def _ffn_no_b1(x, w1, b1, w2, b2):
+    return O.silu(x @ np.asarray(w1).T) @ np.asarray(w2).T + np.asarray(b2)[None, :]
+
+
+def _ffn_no_b2(x, w1, b1, w2, b2):
+    return O.silu(x @ np.asarray(w1).T + np.asarray(b1)[None, :]) @ np.asarray(w2).T
+
+
+def _ffn_act_after_down(x, w1, b1, w2, b2):
+    return O.silu((x @ np.asarray(w1).T + np.asarray(b1)[None, :]) @ np.asarray(w2).T + np.asarray(b2)[None, :])
+
+
+def _combine_no_residual(x, gates, slot_of, Y):
+    out, dropped = _orig["combine"](np.zeros_like(np.asarray(x, np.float64)), gates, slot_of, Y)
+    out[dropped] = np.asarray(x, np.float64)[dropped]
+    return out, dropped
+
+
+def _combine_first_gate(x, gates, slot_of, Y):
+    g = np.repeat(gates[:, :1], gates.shape[1], axis=1)
+    return _orig["combine"](x, g, slot_of, Y)
+
+
+def _combine_no_gate(x, gates, slot_of, Y):
+    return _orig["combine"](x, np.ones_like(gates), slot_of, Y)
+
+
+def _combine_signed(x, gates, slot_of, Y):
+    return _orig["combine"](x, -gates, slot_of, Y)
+
+
+def _combine_plus_zero(x, gates, slot_of, Y):
+    out, dropped = _orig["combine"](x, gates, slot_of, Y)
+    return out + 0.0, dropped  # turns -0.0 into +0.0 on the residual path
+
+
+MUTATIONS = {
+    "capacity_ceil": {"capacity": _cap_ceil},
+    "capacity_without_k": {"capacity": _cap_no_k},
+    "capacity_float_arith": {"capacity": _cap_float},
+    "router_transposed_operand": {"router_logits": _logits_transposed},
+    "router_dropped_bias": {"router_logits": _logits_no_bias},
+    "softmax_no_denominator": {"softmax": _softmax_no_norm},
+    "softmax_wrong_axis": {"softmax": _softmax_wrong_axis},
+    "topk_ties_to_higher_expert": {"top_k": _topk_tie_high},
+    "topk_renormalised": {"top_k": _topk_renorm},
+    "topk_smallest": {"top_k": _topk_ascending},
+    "fill_ascending_gate": {"dispatch": _make_dispatch(sort_key=lambda a: (a[0], a[1], a[2]))},
+    "fill_ties_late_token_first": {"dispatch": _make_dispatch(sort_key=lambda a: (-a[0], -a[1], a[2]))},
+    "fill_choice_before_token": {"dispatch": _make_dispatch(sort_key=lambda a: (-a[0], a[2], a[1]))},
+    "fill_token_order_only": {"dispatch": _make_dispatch(sort_key=lambda a: (a[1], a[2]))},
+    "offsets_from_counts": {"dispatch": _make_dispatch(offsets_from_counts=True)},
+    "keep_off_by_one": {"dispatch": _make_dispatch(keep_rule=lambda r, cap: r <= cap)},
+    "silu_is_sigmoid": {"silu": _silu_sigmoid},
+    "silu_is_relu": {"silu": _silu_relu},
+    "silu_sign_flip": {"silu": _silu_sign},
+    "ffn_dropped_b1": {"expert_ffn": _ffn_no_b1},
+    "ffn_dropped_b2": {"expert_ffn": _ffn_no_b2},
+    "ffn_activation_misplaced": {"expert_ffn": _ffn_act_after_down},
+    "combine_no_residual": {"combine": _combine_no_residual},
+    "combine_first_gate_for_all": {"combine": _combine_first_gate},
+    "combine_ignores_gate": {"combine": _combine_no_gate},
+    "combine_negated_gate": {"combine": _combine_signed},
+    "combine_plus_zero": {"combine": _combine_plus_zero},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    for attr, fn in MUTATIONS[name].items():
+        monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(O)
+        except Exception:  # an assertion or a crash: either way the mistake shows
+            failed.append(check.__name__)
+    assert failed, f"planted mistake {name!r} passed every pin"
