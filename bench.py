@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the capacity-limited MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward over a batch of synthetic input already resident in HBM:
+router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), expert GEMM 2
+(+bias), combine.  Prints ONE JSON line:
+  value          tokens/s of the whole layer (T / wall-clock time per step)
+  roofline       the dominant kernel (the larger expert GEMM) against the bf16 MFMA peak,
+                 from HIP events recorded on the launch stream around it in the timed steps
+  cpu_baseline   the CPU oracle timed on this host on the same workload (a baseline only)
+Workload: the mid-size layer (T 4096, d_model 2048, d_ff 8192, 8 experts, top-2, capacity
+factor 1.25) unless --config names another.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer tokens/s; expert GEMM TFLOP/s as % of MI355X bf16 peak"
+STAGES = ["route", "dispatch", "expert_up", "expert_down", "combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(kernel_tag: str, config_key: str, n_units: float):
+    """HBM bytes per launch of the dominant kernel from a committed counter summary, scaled by
+    the copy-kernel calibration, or None if no summary matches the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{config_key}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = {k: re.search(rf"^{k}\s*=\s*(\S+)", text, re.M) for k in
+         ("source_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_scale")}
+    if not all(m.values()):
+        return None
+    src = open(os.path.join(ROOT, "capacity_routing_expert_amd", "csrc", "gemm_bf16.hip"), "rb").read()
+    if hashlib.sha256(src).hexdigest() != m["source_sha256"].group(1):
+        return None  # the kernel changed since the counters were taken
+    kib = float(m["fetch_kib_per_dispatch"].group(1)) + float(m["write_kib_per_dispatch"].group(1))
+    return kib * 1024.0 * float(m["copy_scale"].group(1))
+
+
+def cpu_baseline(inp, wl, cap):
+    """The oracle on this host: the whole layer on the same workload, once."""
+    import oracle.moe_oracle as O
+    from capacity_routing_expert_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    dt = inp["dtype"]
+    x = W.to_float64(inp["x"], dt)
+    wr = W.to_float64(inp["w_router"], dt)
+
+    class F64:
+        def __init__(self, a):
+            self.a = a
+
+        def __getitem__(self, e):
+            return W.to_float64(self.a[e], dt)
+
+    t0 = time.perf_counter()
+    r = O.route(x, wr, inp["b_router"], wl.top_k)
+    res = O.forward_with_routing(x, r["ids"], r["gates"], cap, wl.n_experts, F64(inp["w1"]),
+                                 F64(inp["b1"]), F64(inp["w2"]), F64(inp["b2"]))
+    t = time.perf_counter() - t0
+    # the per-expert float64 weight conversion is inside the timed region: it is part of
+    # what the oracle does to evaluate the layer
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole layer on the full {wl.name} batch ({wl.T} tokens), 1 run, "
+                      f"{t:.2f} s, float64 NumPy/BLAS", "seconds": round(t, 3),
+            "n_kept": int(res["n_kept"])}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mid", help="worked_example | mid | fine | decode | collapse")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from capacity_routing_expert_amd import binding as B
+    from capacity_routing_expert_amd import layer as L
+    from capacity_routing_expert_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.config]
+    cap = B.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
+    log(f"[bench] generating {wl.name}")
+    inp = W.make_inputs(wl)
+    d = L.upload(inp, dev)
+    shape = L.shape_of(d, wl.top_k, cap)
+    ws = L.workspace(shape, dev)
+    out = torch.empty_like(d["x"])
+    counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events):
+        B.moe_layer_forward_profiled(shape, d["x"], d["w_router"], d["b_router"], d["w1"], d["b1"],
+                                     d["w2"], d["b2"], out, events, expert_counts=counts, ws=ws)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for ev in evs:
+            ev.record(stream)  # creates the underlying hipEvent_t
+        return evs
+
+    log(f"[bench] warmup {args.warmup}")
+    warm = new_events()
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    evsets = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evsets[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    stage_ms = {s: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in evsets]))
+                for j, s in enumerate(STAGES)}
+    step_ms = float(np.mean([evs[0].elapsed_time(evs[5]) for evs in evsets]))
+    c = counts.cpu().numpy()
+    n_kept = int(np.minimum(c, cap).sum())
+    dm, ff = wl.d_model, wl.d_ff
+    gemm_flop = 2.0 * n_kept * dm * ff  # each of the two expert GEMMs, kept rows only
+    expert_s = (stage_ms["expert_up"] + stage_ms["expert_down"]) / 1e3
+    dom = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
+    dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
+                  "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
+    achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
+    traffic = traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2", args.config, 1.0)
+
+    route_bytes = wl.T * dm * inp["x"].itemsize + wl.n_experts * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
+    combine_bytes = (2 * wl.T + n_kept) * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": wl.T / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": dm, "d_ff": ff,
+                   "n_experts": wl.n_experts, "top_k": wl.top_k,
+                   "capacity_factor": wl.capacity_factor, "capacity": cap},
+        "expert_gemm_tflops": 2 * gemm_flop / expert_s / 1e12,
+        "expert_gemm_frac_of_bf16_peak": 2 * gemm_flop / expert_s / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "units_per_launch": f"{n_kept} kept rows x 2*{dm}*{ff} FLOP"},
+        "stages_ms": stage_ms,
+        "event_step_ms": step_ms,
+        "route_GBps": route_bytes / (stage_ms["route"] / 1e3) / 1e9,
+        "combine_GBps": combine_bytes / (stage_ms["combine"] / 1e3) / 1e9,
+        "n_kept": n_kept,
+        "drop_rate": 1.0 - n_kept / (wl.T * wl.top_k),
+        "expert_rows": [int(v) for v in np.minimum(c, cap)],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(inp, wl, cap)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""Thin ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module only turns torch tensors into
+device pointers, picks torch's current stream, checks dtypes/devices/shapes of the tensors
+it is handed, and raises on a non-OK status.  torch is imported before the library is
+loaded so that both use torch's HIP runtime (one runtime per process).
+
+The library is loaded on first use; if it has not been built the call raises, there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_DEVICE"}
+
+EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_status_string",
+           "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+           "moe_layer_forward", "moe_layer_forward_profiled")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m capacity_routing_expert_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        SP = ctypes.POINTER(MoeShape)
+        L.moe_capacity.argtypes = [I64, I32, I32, ctypes.c_double]
+        L.moe_capacity.restype = I32
+        L.moe_workspace_bytes.argtypes = [SP]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_max_kept_rows.argtypes = [SP]
+        L.moe_max_kept_rows.restype = I64
+        L.moe_status_string.argtypes = [I32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_route.argtypes = [SP, P, P, P, P, P, P, P, SZ, P]
+        L.moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_ffn.argtypes = [SP, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_combine.argtypes = [SP, P, P, P, P, P, P]
+        L.moe_layer_forward.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_layer_forward_profiled.argtypes = L.moe_layer_forward.argtypes + [P]
+        for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                     "moe_layer_forward", "moe_layer_forward_profiled"):
+            getattr(L, name).restype = I32
+        _lib = L
+    return _lib
+
+
+def make_shape(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, capacity: int,
+               dtype: int) -> MoeShape:
+    return MoeShape(int(T), int(d_model), int(d_ff), int(n_experts), int(top_k), int(capacity),
+                    int(dtype))
+
+
+def capacity(T: int, top_k: int, n_experts: int, capacity_factor: float) -> int:
+    return int(lib().moe_capacity(int(T), int(top_k), int(n_experts), float(capacity_factor)))
+
+
+def workspace_bytes(shape: MoeShape) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def max_kept_rows(shape: MoeShape) -> int:
+    return int(lib().moe_max_kept_rows(ctypes.byref(shape)))
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None, device=None) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where, last_error())
+
+
+def _dtype_of(shape: MoeShape):
+    return torch.bfloat16 if shape.dtype == MOE_BF16 else torch.float32
+
+
+def moe_route(shape, x, w_router, b_router, topk_ids, topk_gates, logits, ws, stream=None):
+    dt = _dtype_of(shape)
+    _check(lib().moe_route(ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
+                           _ptr(b_router, "b_router", torch.float32),
+                           _ptr(topk_ids, "topk_ids", torch.int32),
+                           _ptr(topk_gates, "topk_gates", torch.float32),
+                           _ptr(logits, "logits", torch.float32), _ptr(ws, "ws", torch.uint8),
+                           ws.numel(), _stream(stream)), "moe_route")
+
+
+def moe_dispatch(shape, topk_ids, topk_gates, expert_counts, expert_offsets, slot_of, row_token,
+                 drop_mask, ws, stream=None):
+    _check(lib().moe_dispatch(ctypes.byref(shape), _ptr(topk_ids, "topk_ids", torch.int32),
+                              _ptr(topk_gates, "topk_gates", torch.float32),
+                              _ptr(expert_counts, "expert_counts", torch.int32),
+                              _ptr(expert_offsets, "expert_offsets", torch.int32),
+                              _ptr(slot_of, "slot_of", torch.int32),
+                              _ptr(row_token, "row_token", torch.int32) if row_token.numel() else None,
+                              _ptr(drop_mask, "drop_mask", torch.uint8),
+                              _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+           "moe_dispatch")
+
+
+def moe_expert_ffn(shape, x, row_token, expert_offsets, w1, b1, w2, b2, y_rows, ws, stream=None):
+    dt = _dtype_of(shape)
+    _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x, "x", dt),
+                                _ptr(row_token, "row_token", torch.int32) if row_token.numel() else None,
+                                _ptr(expert_offsets, "expert_offsets", torch.int32),
+                                _ptr(w1, "w1", dt), _ptr(b1, "b1", dt), _ptr(w2, "w2", dt),
+                                _ptr(b2, "b2", dt),
+                                _ptr(y_rows, "y_rows", dt) if y_rows.numel() else None,
+                                _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(shape, x, topk_gates, slot_of, y_rows, out, stream=None):
+    dt = _dtype_of(shape)
+    _check(lib().moe_combine(ctypes.byref(shape), _ptr(x, "x", dt),
+                             _ptr(topk_gates, "topk_gates", torch.float32),
+                             _ptr(slot_of, "slot_of", torch.int32),
+                             _ptr(y_rows, "y_rows", dt) if y_rows.numel() else None,
+                             _ptr(out, "out", dt), _stream(stream)), "moe_combine")
+
+
+def _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                  slot_of, drop_mask, expert_counts, ws):
+    dt = _dtype_of(shape)
+    return [ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
+            _ptr(b_router, "b_router", torch.float32), _ptr(w1, "w1", dt), _ptr(b1, "b1", dt),
+            _ptr(w2, "w2", dt), _ptr(b2, "b2", dt), _ptr(out, "out", dt),
+            _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_gates, "topk_gates", torch.float32),
+            _ptr(slot_of, "slot_of", torch.int32), _ptr(drop_mask, "drop_mask", torch.uint8),
+            _ptr(expert_counts, "expert_counts", torch.int32), _ptr(ws, "ws", torch.uint8),
+            ws.numel()]
+
+
+def moe_layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
+                      topk_gates=None, slot_of=None, drop_mask=None, expert_counts=None, ws=None,
+                      stream=None):
+    args = _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                         slot_of, drop_mask, expert_counts, ws)
+    _check(lib().moe_layer_forward(*args, _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_profiled(shape, x, w_router, b_router, w1, b1, w2, b2, out, events,
+                               topk_ids=None, topk_gates=None, slot_of=None, drop_mask=None,
+                               expert_counts=None, ws=None, stream=None):
+    """`events`: 6 torch.cuda.Event(enable_timing=True) objects, already recorded once (so the
+    underlying hipEvent_t exists)."""
+    handles = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+    args = _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                         slot_of, drop_mask, expert_counts, ws)
+    _check(lib().moe_layer_forward_profiled(*args, _stream(stream), handles),
+           "moe_layer_forward_profiled")

@@ -1,0 +1,373 @@
+// C interface of libmoe: argument checks, workspace layout and launch order.  The operations
+// and their sources are described in include/moe.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status device_error(hipError_t err, const char* where) {
+  return fail(MOE_ERR_DEVICE, "%s: %s", where, hipGetErrorString(err));
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)s->T);
+  if (s->d_model < 1 || s->d_ff < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "d_model = %d, d_ff = %d must be >= 1", s->d_model, s->d_ff);
+  if (s->n_experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d < 1", s->n_experts);
+  if (s->n_experts > 256)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts = %d > 256", s->n_experts);
+  if (s->top_k < 1 || s->top_k > s->n_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "top_k = %d not in [1, n_experts = %d]", s->top_k,
+                s->n_experts);
+  if (s->capacity < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "capacity = %d < 0", s->capacity);
+  if (s->T * (int64_t)s->top_k >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * top_k = %lld >= 2^31", (long long)(s->T * s->top_k));
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype %d unknown", s->dtype);
+  if (s->dtype == MOE_BF16 && (s->d_model % 8 != 0 || s->d_ff % 8 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model (%d) and d_ff (%d) multiples of 8",
+                s->d_model, s->d_ff);
+  return MOE_OK;
+}
+
+size_t elem_bytes(const moe_shape& s) { return s.dtype == MOE_BF16 ? 2 : 4; }
+
+// Data pointers of the dtype: 16-byte alignment for bf16 (vector loads), 4 for fp32.
+moe_status check_data_ptr(const moe_shape& s, const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  const size_t a = s.dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(p, a)) return fail(MOE_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", name, a);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, size_t a, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, a)) return fail(MOE_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", name, a);
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(s).total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  if (need && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    moe_status _st = (expr);     \
+    if (_st != MOE_OK) return _st; \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+int64_t max_rows(const moe_shape& s) {
+  const int64_t a = s.T * (int64_t)s.top_k;
+  const int64_t b = (int64_t)s.n_experts * s.capacity;
+  return a < b ? a : b;
+}
+
+Workspace layout(const moe_shape& s) {
+  Workspace w;
+  const int64_t N = s.T * (int64_t)s.top_k;
+  const int64_t E = s.n_experts;
+  const int64_t nb = (N + kDispatchChunk - 1) / kDispatchChunk;
+  const int64_t rows = max_rows(s);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = align256(o + bytes);
+    return at_;
+  };
+  w.w64 = take((size_t)E * s.d_model * 8);
+  w.ids = take((size_t)N * 4);
+  w.gates = take((size_t)N * 4);
+  w.slot_of = take((size_t)N * 4);
+  w.drop = take((size_t)N);
+  w.counts = take((size_t)E * 4);
+  w.offsets = take((size_t)(E + 1) * 4);
+  w.seg_start = take((size_t)(E + 2) * 4);
+  w.blk_hist = take((size_t)nb * (E + 1) * 4);
+  w.keys = take((size_t)N * 8);
+  w.row_token = take((size_t)rows * 4);
+  w.h = take((size_t)rows * s.d_ff * elem_bytes(s));
+  w.y = take((size_t)rows * s.d_model * elem_bytes(s));
+  w.total = o;
+  return w;
+}
+
+namespace {
+
+moe_status do_route(const moe_shape& s, const void* x, const void* w_router, const float* b_router,
+                    int32_t* ids, float* gates, float* logits, void* ws, hipStream_t st) {
+  const Workspace L = layout(s);
+  hipError_t err = launch_route(s, x, w_router, b_router, ids, gates, logits, at<double>(ws, L.w64), st);
+  return err == hipSuccess ? MOE_OK : device_error(err, "route");
+}
+
+moe_status do_dispatch(const moe_shape& s, const int32_t* ids, const float* gates, int32_t* counts,
+                       int32_t* offsets, int32_t* slot_of, int32_t* row_token, uint8_t* drop,
+                       void* ws, hipStream_t st) {
+  const Workspace L = layout(s);
+  hipError_t err = launch_dispatch(s, ids, gates, counts, offsets, slot_of, row_token, drop,
+                                   at<int32_t>(ws, L.seg_start), at<int32_t>(ws, L.blk_hist),
+                                   at<uint64_t>(ws, L.keys), st);
+  return err == hipSuccess ? MOE_OK : device_error(err, "dispatch");
+}
+
+moe_status check_forward_args(const moe_shape* shape, const void* x, const void* w_router,
+                              const float* b_router, const void* w1, const void* b1,
+                              const void* w2, const void* b2, void* out, void* ws,
+                              size_t ws_bytes) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  MOE_TRY(check_data_ptr(s, w_router, "w_router"));
+  if (b_router) MOE_TRY(check_ptr(b_router, 4, "b_router"));
+  MOE_TRY(check_data_ptr(s, w1, "w1"));
+  MOE_TRY(check_data_ptr(s, b1, "b1"));
+  MOE_TRY(check_data_ptr(s, w2, "w2"));
+  MOE_TRY(check_data_ptr(s, b2, "b2"));
+  MOE_TRY(check_data_ptr(s, out, "out"));
+  if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
+  MOE_TRY(check_ws(s, ws, ws_bytes));
+  return MOE_OK;
+}
+
+moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_router,
+                         const float* b_router, const void* w1, const void* b1, const void* w2,
+                         const void* b2, void* out, int32_t* topk_ids, float* topk_gates,
+                         int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts, void* ws,
+                         size_t ws_bytes, hipStream_t st, moe_event_t const* events) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  auto rec = [&](int i) -> moe_status {
+    if (!events) return MOE_OK;
+    hipError_t err = hipEventRecord((hipEvent_t)events[i], st);
+    return err == hipSuccess ? MOE_OK : device_error(err, "hipEventRecord");
+  };
+  if (s.T == 0) {  // empty batch: nothing to check or enqueue
+    for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
+    return MOE_OK;
+  }
+  MOE_TRY(check_forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, ws, ws_bytes));
+  if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  if (slot_of) MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  if (expert_counts) MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
+  const Workspace L = layout(s);
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
+  int32_t* slots = slot_of ? slot_of : at<int32_t>(ws, L.slot_of);
+  uint8_t* drop = drop_mask ? drop_mask : at<uint8_t>(ws, L.drop);
+  int32_t* counts = expert_counts ? expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  void* h = at<void>(ws, L.h);
+  void* y = at<void>(ws, L.y);
+
+  MOE_TRY(rec(0));
+  MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, ws, st));
+  MOE_TRY(rec(1));
+  MOE_TRY(do_dispatch(s, ids, gates, counts, offsets, slots, row_token, drop, ws, st));
+  MOE_TRY(rec(2));
+  hipError_t err = launch_ffn_up(s, x, row_token, offsets, w1, b1, h, st);
+  if (err != hipSuccess) return device_error(err, "expert up-projection");
+  MOE_TRY(rec(3));
+  err = launch_ffn_down(s, h, offsets, w2, b2, y, st);
+  if (err != hipSuccess) return device_error(err, "expert down-projection");
+  MOE_TRY(rec(4));
+  err = launch_combine(s, x, gates, slots, y, out, st);
+  if (err != hipSuccess) return device_error(err, "combine");
+  MOE_TRY(rec(5));
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_capacity(int64_t T, int32_t top_k, int32_t n_experts, double capacity_factor) {
+  if (T < 0 || top_k < 1 || n_experts < 1 || !(capacity_factor >= 0.0) || !isfinite(capacity_factor))
+    return -1;
+  if (capacity_factor == 0.0 || T == 0) return 0;
+  if (T > ((int64_t)1 << 40)) return -1;
+  // capacity_factor = m * 2^ex exactly, m a 53-bit integer
+  int ex = 0;
+  const double mant = frexp(capacity_factor, &ex);
+  const int64_t m = (int64_t)ldexp(mant, 53);
+  ex -= 53;
+  const __int128 num = (__int128)m * T * top_k;  // < 2^53 * 2^40 * 2^31
+  if (ex >= 0) return -1;  // C >= 2^52: no capacity of that size fits in int32
+  const int sh = -ex;
+  // floor(floor(a / 2^sh) / E) = floor(a / (E * 2^sh)) for non-negative integers
+  const __int128 q = sh >= 127 ? 0 : (num >> sh) / n_experts;
+  if (q > (__int128)INT32_MAX) return -1;
+  return (int32_t)q;
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return layout(*shape).total;
+}
+
+int64_t moe_max_kept_rows(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return max_rows(*shape);
+}
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    default: return "MOE_STATUS_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router,
+                     const float* b_router, int32_t* topk_ids, float* topk_gates, float* logits,
+                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  MOE_TRY(check_data_ptr(s, w_router, "w_router"));
+  if (b_router) MOE_TRY(check_ptr(b_router, 4, "b_router"));
+  MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  if (logits) MOE_TRY(check_ptr(logits, 4, "logits"));
+  MOE_TRY(check_ws(s, ws, ws_bytes));
+  return do_route(s, x, w_router, b_router, topk_ids, topk_gates, logits, ws, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const float* topk_gates,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_of,
+                        int32_t* row_token, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                        moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  if (max_rows(s) > 0) MOE_TRY(check_ptr(row_token, 4, "row_token"));
+  MOE_TRY(check_ptr(drop_mask, 1, "drop_mask"));
+  MOE_TRY(check_ws(s, ws, ws_bytes));
+  return do_dispatch(s, topk_ids, topk_gates, expert_counts, expert_offsets, slot_of, row_token,
+                     drop_mask, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* row_token,
+                          const int32_t* expert_offsets, const void* w1, const void* b1,
+                          const void* w2, const void* b2, void* y_rows, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  if (max_rows(s) > 0) {
+    MOE_TRY(check_ptr(row_token, 4, "row_token"));
+    MOE_TRY(check_data_ptr(s, y_rows, "y_rows"));
+  }
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_data_ptr(s, w1, "w1"));
+  MOE_TRY(check_data_ptr(s, b1, "b1"));
+  MOE_TRY(check_data_ptr(s, w2, "w2"));
+  MOE_TRY(check_data_ptr(s, b2, "b2"));
+  MOE_TRY(check_ws(s, ws, ws_bytes));
+  if (max_rows(s) == 0) return MOE_OK;
+  const Workspace L = layout(s);
+  hipStream_t st = (hipStream_t)stream;
+  void* h = at<void>(ws, L.h);
+  hipError_t err = launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, st);
+  if (err != hipSuccess) return device_error(err, "expert up-projection");
+  err = launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, st);
+  if (err != hipSuccess) return device_error(err, "expert down-projection");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* x, const float* topk_gates,
+                       const int32_t* slot_of, const void* y_rows, void* out,
+                       moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  if (max_rows(s) > 0) MOE_TRY(check_data_ptr(s, y_rows, "y_rows"));
+  MOE_TRY(check_data_ptr(s, out, "out"));
+  if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
+  hipError_t err = launch_combine(s, x, topk_gates, slot_of, y_rows, out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(err, "combine");
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router,
+                             const float* b_router, const void* w1, const void* b1,
+                             const void* w2, const void* b2, void* out, int32_t* topk_ids,
+                             float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                             int32_t* expert_counts, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
+  return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                       slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
+                       nullptr);
+}
+
+moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
+                                      const void* w_router, const float* b_router,
+                                      const void* w1, const void* b1, const void* w2,
+                                      const void* b2, void* out, int32_t* topk_ids,
+                                      float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                                      int32_t* expert_counts, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream, moe_event_t const* events) {
+  if (!events) return fail(MOE_ERR_INVALID_ARGUMENT, "events is NULL");
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                       slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
+                       events);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the HIP sources of libmoe (not part of the C interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 stored as its bit pattern
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest, ties to even (inputs here are finite)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float load_as_f32(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
+
+// ---------------------------------------------------------------- workspace layout
+// One workspace buffer serves every call; each sub-buffer starts on a 256-byte boundary.
+struct Workspace {
+  size_t w64;        // router weights widened to fp64            [E, d]
+  size_t ids;        // top-k expert ids (layer_forward)          [T*k] int32
+  size_t gates;      // top-k gates                               [T*k] f32
+  size_t slot_of;    // slot per assignment                       [T*k] int32
+  size_t drop;       // drop mask                                 [T*k] u8
+  size_t counts;     // per-expert assignment counts              [E] int32
+  size_t offsets;    // kept-slot offsets                         [E+1] int32
+  size_t seg_start;  // start of each expert's bucket in `keys`   [E+2] int32
+  size_t blk_hist;   // per-block expert histograms               [nb, E+1] int32
+  size_t keys;       // bucketed sort keys                        [T*k] u64
+  size_t row_token;  // token per slot                            [max_rows] int32
+  size_t h;          // activation between the GEMMs              [max_rows, d_ff]
+  size_t y;          // expert outputs per slot                   [max_rows, d_model]
+  size_t total;
+};
+
+constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
+constexpr int kRankChunk = 4096;      // keys sorted per block in the rank kernels
+
+int64_t max_rows(const moe_shape& s);
+Workspace layout(const moe_shape& s);
+
+// ---------------------------------------------------------------- launchers (return hipError_t)
+hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
+                        const float* b_router, int32_t* ids, float* gates, float* logits,
+                        double* w64, hipStream_t st);
+
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
+                           int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                           int32_t* row_token, uint8_t* drop, int32_t* seg_start,
+                           int32_t* blk_hist, uint64_t* keys, hipStream_t st);
+
+hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
+                         const int32_t* offsets, const void* w1, const void* b1, void* h,
+                         hipStream_t st);
+hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
+                           const void* w2, const void* b2, void* y, hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* x, const float* gates,
+                          const int32_t* slot_of, const void* y, void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,106 @@
+"""Device-side convenience around the C interface: upload a workload, allocate outputs and
+workspace with torch, and call the staged or whole-layer entry points.  Allocation and
+marshalling only; all layer arithmetic runs in libmoe."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def to_device(arr: np.ndarray | None, dtype: str, device) -> torch.Tensor | None:
+    """bf16 bit patterns (uint16) become torch.bfloat16; float32 stays float32."""
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    if arr.dtype == np.int32:
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def upload(inputs: dict, device="cuda:0") -> dict:
+    dt = inputs["dtype"]
+    return {k: to_device(inputs[k], dt if k != "b_router" else "f32", device)
+            for k in ("x", "w_router", "b_router", "w1", "b1", "w2", "b2")}
+
+
+def shape_of(dev: dict, top_k: int, capacity: int) -> B.MoeShape:
+    x, w1 = dev["x"], dev["w1"]
+    dtype = B.MOE_BF16 if x.dtype == torch.bfloat16 else B.MOE_F32
+    return B.make_shape(x.shape[0], x.shape[1], w1.shape[1], w1.shape[0], top_k, capacity, dtype)
+
+
+def workspace(shape: B.MoeShape, device="cuda:0") -> torch.Tensor:
+    return torch.empty(max(B.workspace_bytes(shape), 256), dtype=torch.uint8, device=device)
+
+
+def layer_forward(dev: dict, top_k: int, capacity: int, ws: torch.Tensor | None = None,
+                  events=None) -> dict:
+    """Whole layer in one call; returns out and the routing/dispatch outputs."""
+    shape = shape_of(dev, top_k, capacity)
+    device = dev["x"].device
+    T, E = shape.T, shape.n_experts
+    ws = workspace(shape, device) if ws is None else ws
+    res = {
+        "out": torch.empty_like(dev["x"]),
+        "ids": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "slot_of": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "drop_mask": torch.empty((T, top_k), dtype=torch.uint8, device=device),
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+    }
+    args = (shape, dev["x"], dev["w_router"], dev["b_router"], dev["w1"], dev["b1"], dev["w2"],
+            dev["b2"], res["out"])
+    kw = dict(topk_ids=res["ids"], topk_gates=res["gates"], slot_of=res["slot_of"],
+              drop_mask=res["drop_mask"], expert_counts=res["counts"], ws=ws)
+    if events is None:
+        B.moe_layer_forward(*args, **kw)
+    else:
+        B.moe_layer_forward_profiled(*args, events, **kw)
+    return res
+
+
+def route(dev: dict, top_k: int, capacity: int, ws=None, want_logits=False) -> dict:
+    shape = shape_of(dev, top_k, capacity)
+    device = dev["x"].device
+    T, E = shape.T, shape.n_experts
+    ws = workspace(shape, device) if ws is None else ws
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=device)
+    gates = torch.empty((T, top_k), dtype=torch.float32, device=device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=device) if want_logits else None
+    B.moe_route(shape, dev["x"], dev["w_router"], dev["b_router"], ids, gates, logits, ws)
+    return {"ids": ids, "gates": gates, "logits": logits}
+
+
+def dispatch(shape: B.MoeShape, ids: torch.Tensor, gates: torch.Tensor, ws=None) -> dict:
+    device = ids.device
+    T, k, E = shape.T, shape.top_k, shape.n_experts
+    ws = workspace(shape, device) if ws is None else ws
+    res = {
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+        "offsets": torch.empty((E + 1,), dtype=torch.int32, device=device),
+        "slot_of": torch.empty((T, k), dtype=torch.int32, device=device),
+        "row_token": torch.empty((max(B.max_kept_rows(shape), 0),), dtype=torch.int32, device=device),
+        "drop_mask": torch.empty((T, k), dtype=torch.uint8, device=device),
+    }
+    B.moe_dispatch(shape, ids, gates, res["counts"], res["offsets"], res["slot_of"],
+                   res["row_token"], res["drop_mask"], ws)
+    return res
+
+
+def expert_ffn(shape: B.MoeShape, dev: dict, row_token, offsets, ws=None) -> torch.Tensor:
+    device = dev["x"].device
+    ws = workspace(shape, device) if ws is None else ws
+    y = torch.empty((max(B.max_kept_rows(shape), 0), shape.d_model), dtype=dev["x"].dtype,
+                    device=device)
+    B.moe_expert_ffn(shape, dev["x"], row_token, offsets, dev["w1"], dev["b1"], dev["w2"],
+                     dev["b2"], y, ws)
+    return y
+
+
+def combine(shape: B.MoeShape, x, gates, slot_of, y_rows) -> torch.Tensor:
+    out = torch.empty_like(x)
+    B.moe_combine(shape, x, gates, slot_of, y_rows, out)
+    return out

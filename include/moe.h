@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C interface of the capacity-limited Mixture-of-Experts layer forward pass,
+ * hand-written HIP for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The layer (one token row x of width d_model, E experts, top-k routing, capacity factor C):
+ *   1. route     : router logits L = W_r x + b_r, softmax over all E experts, the k largest
+ *                  gates, unrenormalised.
+ *   2. dispatch  : each expert owns a fixed buffer of `capacity` = floor(C*T*k/E) slots; the
+ *                  assignments of an expert fill it in the order (gate descending, token
+ *                  index ascending, choice rank ascending); the rest are dropped.
+ *   3. expert FFN: y = W2 SiLU(W1 x + b1) + b2 for every kept assignment, as a grouped
+ *                  GEMM over the routed rows.
+ *   4. combine   : out[t] = x[t] + sum over kept choices of gate * y; a token with no kept
+ *                  choice leaves the layer bit for bit as it entered.
+ * Sources: "Expert Networks > Worked Example: Expert Specialization" (the whole worked
+ * example: configuration, capacity paragraph, trace of token 0, trace of token 4);
+ * "Some Tokens Do Not Get In", sections "Why there is a buffer" and "Past the edge";
+ * "Dynamic Token Routing AI", section "How it works" (the gating network).
+ *
+ * Conventions for every call below:
+ *   - All array arguments are DEVICE pointers (hipMalloc'd or from a caching allocator),
+ *     row-major and contiguous.  In the bf16 dtype, x, weights, biases, y_rows and out
+ *     must be 16-byte aligned.  The library never allocates device memory and never
+ *     frees a caller's pointer; the caller owns every buffer, including the workspace.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL is the null stream) and
+ *     return; there is no host synchronisation and no device-to-host copy inside, so a
+ *     device fault shows up at the caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is enqueued; on any non-OK status
+ *     no output has been touched.  moe_last_error() then gives a one-line reason.
+ *   - T == 0 is valid and enqueues nothing.
+ *   - Calls that share a workspace must not overlap (same stream, or ordered by events).
+ *   - Layouts: W_r [E, d_model]; W1 [E, d_ff, d_model]; b1 [E, d_ff]; W2 [E, d_model, d_ff];
+ *     b2 [E, d_model]; x and out [T, d_model]; per-assignment arrays [T, top_k], with
+ *     choice 0 the largest gate.  Biases have the weight dtype; the router bias is fp32.
+ *   - Limits: 1 <= top_k <= n_experts <= 256; capacity >= 0; T * top_k < 2^31;
+ *     bf16 needs d_model and d_ff multiples of 8.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* hipStream_t */
+typedef struct ihipEvent_t* moe_event_t;   /* hipEvent_t  */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad sizes, k > E, capacity < 0 */
+  MOE_ERR_UNSUPPORTED = 2,      /* misaligned pointer, d not a multiple of 8 for bf16, E > 256 */
+  MOE_ERR_WORKSPACE = 3,        /* ws_bytes < moe_workspace_bytes(shape) */
+  MOE_ERR_DEVICE = 4            /* a HIP call failed; moe_last_error() has its text */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem shape.  `capacity` is the per-expert slot count, normally moe_capacity(...). */
+typedef struct {
+  int64_t T;         /* tokens */
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts; /* E */
+  int32_t top_k;     /* k */
+  int32_t capacity;  /* slots per expert */
+  int32_t dtype;     /* moe_dtype of x, weights, biases, y_rows, out */
+} moe_shape;
+
+/* floor(C * T * k / E), evaluated exactly on the binary value of C (no rounding of the
+ * product).  Worked Example, capacity paragraph: 1.25 * 8 * 1 / 4 = 2.5, rounded down to 2.
+ * Returns -1 if T < 0, k < 1, E < 1, C < 0 or not finite, or the result exceeds INT32_MAX. */
+int32_t moe_capacity(int64_t T, int32_t top_k, int32_t n_experts, double capacity_factor);
+
+/* Bytes of device workspace every call below needs for this shape (one buffer serves all
+ * of them).  0 for an invalid shape.  The workspace holds no state between calls. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Upper bound on the number of kept rows: min(T * k, E * capacity).  y_rows needs this
+ * many rows.  -1 for an invalid shape. */
+int64_t moe_max_kept_rows(const moe_shape* shape);
+
+const char* moe_status_string(int32_t status);
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Step 1, router.  "Dynamic Token Routing AI", "How it works": a gating network scores each
+ * token and selects its experts; Worked Example, trace of token 0: the chosen expert's
+ * output is scaled by the router's confidence.
+ *   x          [T, d_model]  dtype
+ *   w_router   [E, d_model]  dtype
+ *   b_router   [E] fp32, or NULL for no bias
+ *   topk_ids   [T, k] int32  out: expert of choice c, c = 0 the largest gate
+ *   topk_gates [T, k] fp32   out: softmax probability over all E experts (not renormalised)
+ *   logits     [T, E] fp32 or NULL   out (diagnostic): the logits rounded to fp32
+ * Logits are accumulated in fp64 from exact products, the softmax is evaluated in fp64 and
+ * rounded once to fp32; top-k compares the fp32 gates, ties going to the lower expert. */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router,
+                     const float* b_router, int32_t* topk_ids, float* topk_gates,
+                     float* logits, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Step 2, capacity and slot assignment.  Worked Example, capacity paragraph: an expert that
+ * receives more tokens than its capacity keeps the most confident ones and drops the rest;
+ * "Some Tokens Do Not Get In", "Past the edge": tokens are placed in some order until the
+ * buffer is full.  Order used: gate descending, then token ascending, then choice ascending.
+ *   topk_ids, topk_gates [T, k]  in (from moe_route, or any caller-made routing; gates must
+ *                                not be NaN; an id outside [0, E) is dropped and not counted)
+ *   expert_counts  [E]    int32 out: assignments per expert before the capacity cut
+ *   expert_offsets [E+1]  int32 out: expert e owns slots [off[e], off[e+1]),
+ *                         off[e+1] - off[e] = min(count[e], capacity); off[E] = N_kept
+ *   slot_of        [T, k] int32 out: slot of the assignment, or -1 if dropped
+ *   row_token      [moe_max_kept_rows] int32 out: token of each slot (first N_kept valid)
+ *   drop_mask      [T, k] uint8 out: 1 if dropped
+ * Within an expert, slot off[e] + r holds the assignment of rank r in the fill order. */
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const float* topk_gates,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_of,
+                        int32_t* row_token, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                        moe_stream_t stream);
+
+/* Step 3, expert FFN over the routed rows.  Worked Example, trace of token 0: h = W1 x + b1,
+ * a = SiLU(h), y = W2 a + b2.  Fused-MoE flow diagram (moe-vllm flow), GEMM 1 box: the first
+ * GEMM gathers its token rows itself; here through row_token.
+ *   x [T, d_model]; row_token, expert_offsets from moe_dispatch (device)
+ *   w1 [E, d_ff, d_model], b1 [E, d_ff], w2 [E, d_model, d_ff], b2 [E, d_model]
+ *   y_rows [moe_max_kept_rows, d_model] out: y of slot s in row s (first N_kept rows valid)
+ * bf16: products accumulate in fp32 on the matrix cores; the activation between the two
+ * GEMMs is stored as bf16; y_rows is bf16.  f32: fp32 throughout. */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* row_token,
+                          const int32_t* expert_offsets, const void* w1, const void* b1,
+                          const void* w2, const void* b2, void* y_rows, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
+
+/* Step 4, combine with the residual.  Worked Example, traces of tokens 0 and 4: a kept token
+ * leaves as x + gate * y, a dropped one as x unchanged.  With k > 1 the kept choices are
+ * summed (fp32, one rounding to the dtype); the gates of the kept choices are not
+ * renormalised when another choice dropped.  A token with no kept choice gets a bit copy of
+ * x ("Past the edge": it reaches the next layer exactly as it entered).
+ *   x [T, d_model]; topk_gates, slot_of [T, k]; y_rows from moe_expert_ffn; out [T, d_model]
+ * out must not alias x. */
+moe_status moe_combine(const moe_shape* shape, const void* x, const float* topk_gates,
+                       const int32_t* slot_of, const void* y_rows, void* out,
+                       moe_stream_t stream);
+
+/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine on one stream.
+ * topk_ids, topk_gates, slot_of, drop_mask, expert_counts are optional outputs (NULL keeps
+ * them in the workspace).  Same kernels as the four calls above. */
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router,
+                             const float* b_router, const void* w1, const void* b1,
+                             const void* w2, const void* b2, void* out, int32_t* topk_ids,
+                             float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                             int32_t* expert_counts, void* ws, size_t ws_bytes,
+                             moe_stream_t stream);
+
+/* moe_layer_forward, also recording caller-created events on the stream at the stage
+ * boundaries, so the cost of each stage can be read back (the pages ask for the routing
+ * decision's own overhead to be watched):
+ *   events[0] before routing, [1] after routing, [2] after dispatch, [3] after the first
+ *   expert GEMM (up-projection + SiLU), [4] after the second (down-projection), [5] after
+ *   the combine.  `events` must hold 6 valid hipEvent_t. */
+moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
+                                      const void* w_router, const float* b_router,
+                                      const void* w1, const void* b1, const void* w2,
+                                      const void* b2, void* out, int32_t* topk_ids,
+                                      float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                                      int32_t* expert_counts, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream, moe_event_t const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

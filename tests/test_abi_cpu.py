@@ -1,0 +1,85 @@
+"""The C-ABI library builds, loads and exports every symbol include/moe.h declares; its
+host-only entry points (capacity, workspace size, argument checks) work without a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+from capacity_routing_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from capacity_routing_expert_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert declared == sorted(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_capacity_matches_oracle(lib):
+    assert B.capacity(8, 1, 4, 1.25) == 2
+    rng = np.random.Generator(np.random.PCG64(3))
+    for _ in range(2000):
+        T = int(rng.integers(0, 200000)); k = int(rng.integers(1, 9)); E = int(rng.integers(1, 257))
+        C = float(rng.choice([0.1, 0.7, 1.0, 1.1, 1.25, 1.5, 2.0, 3.3, 4.0, 0.3333333333333333]))
+        assert B.capacity(T, k, E, C) == O.capacity(T, k, E, C), (T, k, E, C)
+    assert B.capacity(10, 1, 7, 0.7) == 0
+    assert B.capacity(-1, 1, 1, 1.0) == -1
+    assert B.capacity(1, 0, 1, 1.0) == -1
+    assert B.capacity(1, 1, 1, float("nan")) == -1
+    assert B.capacity(1, 1, 1, -0.5) == -1
+
+
+def test_workspace_and_max_rows(lib):
+    s = B.make_shape(4096, 2048, 8192, 8, 2, 1280, B.MOE_BF16)
+    assert B.max_kept_rows(s) == min(4096 * 2, 8 * 1280)
+    ws = B.workspace_bytes(s)
+    # at least H and Y for the largest possible number of kept rows
+    assert ws >= 8192 * 8192 * 2 + 8192 * 2048 * 2
+    assert ws % 256 == 0
+    bad = B.make_shape(16, 64, 64, 4, 5, 4, B.MOE_BF16)  # k > E
+    assert B.workspace_bytes(bad) == 0 and B.max_kept_rows(bad) == -1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 0, 1), ("top_k", 9, 1), ("n_experts", 0, 1), ("n_experts", 300, 2),
+    ("capacity", -1, 1), ("T", -5, 1), ("d_model", 12, 2), ("dtype", 7, 2),
+])
+def test_shape_errors_before_any_launch(lib, field, value, status):
+    s = B.make_shape(16, 64, 64, 8, 2, 4, B.MOE_BF16)
+    setattr(s, field, value)
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc = lib.moe_route(ctypes.byref(s), p, p, None, p, p, None, p, 1 << 30, None)
+    assert rc == status, (rc, B.last_error())
+    assert B.last_error()
+
+
+def test_pointer_errors_before_any_launch(lib):
+    s = B.make_shape(16, 64, 64, 8, 2, 4, B.MOE_BF16)
+    p = ctypes.c_void_p(4096)
+    assert lib.moe_route(ctypes.byref(s), None, p, None, p, p, None, p, 1 << 30, None) == 1
+    assert "x is NULL" in B.last_error()
+    assert lib.moe_route(ctypes.byref(s), ctypes.c_void_p(4098), p, None, p, p, None, p, 1 << 30, None) == 2
+    assert "aligned" in B.last_error()
+    assert lib.moe_route(ctypes.byref(s), p, p, None, p, p, None, p, 16, None) == 3
+    assert "workspace" in B.last_error()
+    assert lib.moe_combine(ctypes.byref(s), p, p, p, p, p, None) == 1  # out aliases x
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"

@@ -1,0 +1,360 @@
+"""Parity of the HIP path (through the C interface) against the CPU oracle, on the GPU."""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+import parity as P
+import pins
+from capacity_routing_expert_amd import binding as B
+from capacity_routing_expert_amd import layer as L
+from capacity_routing_expert_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    B.lib()  # loud failure if the library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+class F64:
+    """Per-expert float64 view of a stored weight array, converted on access."""
+
+    def __init__(self, arr, dt):
+        self.arr, self.dt = arr, dt
+
+    def __getitem__(self, e):
+        return W.to_float64(self.arr[e], self.dt)
+
+
+_CACHE: dict = {}
+
+
+def case(key):
+    if key not in _CACHE:
+        say(f"[case] generating {key}")
+        inp = W.make_inputs(key)
+        wl = inp["workload"]
+        dt = inp["dtype"]
+        ref = O.route(W.to_float64(inp["x"], dt), W.to_float64(inp["w_router"], dt),
+                      inp["b_router"], wl.top_k)
+        cap = O.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
+        _CACHE.clear()  # keep one large case in memory at a time
+        _CACHE[key] = (inp, ref, cap)
+    return _CACHE[key]
+
+
+def check_sampled_outputs(inp, out_gpu, ids, gates, dref, n_sample=192, seed=0):
+    """out[t] = x[t] + sum_c kept g * FFN_e(x[t]) on sampled tokens; all-dropped rows bitwise."""
+    dt = inp["dtype"]
+    x = inp["x"]
+    T, k = ids.shape
+    slot_of = dref["slot_of"]
+    kept_any = np.any(slot_of >= 0, axis=1)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cand = np.nonzero(kept_any)[0]
+    sample = np.unique(np.concatenate([
+        rng.choice(cand, size=min(n_sample, len(cand)), replace=False) if len(cand) else np.zeros(0, int),
+        cand[:1], cand[-1:]]).astype(np.int64))
+    if len(sample):
+        slots = slot_of[sample][slot_of[sample] >= 0]
+        y = O.expert_ffn_slots(W.to_float64(x, dt), dref["row_token"], dref["offsets"],
+                               F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
+                               F64(inp["b2"], dt), slots=slots)
+        ymap = {int(s): y[i] for i, s in enumerate(slots)}
+        x64 = W.to_float64(x[sample], dt)
+        ref = x64.copy()
+        for i, t in enumerate(sample):
+            for c in range(k):
+                s = slot_of[t, c]
+                if s >= 0:
+                    ref[i] = ref[i] + float(gates[t, c]) * ymap[int(s)]
+        got = P.to_np(out_gpu[torch.as_tensor(sample, device=out_gpu.device)])
+        err = P.max_abs_rel(got, ref)
+        say(f"    sampled out max-abs-rel {err:.3e} over {len(sample)} tokens")
+        assert err <= P.TOL[dt], err
+    # tokens with every choice dropped: bit copy of x
+    dropped = np.nonzero(~kept_any)[0]
+    if len(dropped):
+        xb = L.to_device(x, dt, DEV)
+        idx = torch.as_tensor(dropped, device=DEV)
+        assert np.array_equal(P.bits(out_gpu[idx]), P.bits(xb[idx])), "dropped rows differ from x"
+    return len(dropped)
+
+
+def check_sampled_y(inp, y_gpu, dref, seed=1):
+    dt = inp["dtype"]
+    off = dref["offsets"]
+    E = len(off) - 1
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slots = []
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            slots += [a, b - 1] + list(rng.integers(a, b, size=min(4, b - a)))
+            slots += [s for s in range(a + 255, b, 256)][:4]  # tile boundaries
+    slots = np.unique(np.asarray(slots, dtype=np.int64))
+    if len(slots) == 0:
+        return
+    ref = O.expert_ffn_slots(W.to_float64(inp["x"], dt), dref["row_token"], off,
+                             F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
+                             F64(inp["b2"], dt), slots=slots)
+    got = P.to_np(y_gpu[torch.as_tensor(slots, device=y_gpu.device)])
+    err = P.max_abs_rel(got, ref)
+    say(f"    sampled Y max-abs-rel {err:.3e} over {len(slots)} slots")
+    assert err <= P.TOL[dt], err
+
+
+# --------------------------------------------------------------------------- worked example
+def test_worked_example_forced_dispatch():
+    g = pins.golden()
+    ids = torch.tensor(g["assignment"]["ids"], dtype=torch.int32, device=DEV)[:, None].contiguous()
+    gates = torch.tensor(pins.FORCED_GATES, dtype=torch.float32, device=DEV)[:, None].contiguous()
+    shape = B.make_shape(8, 4, 8, 4, 1, g["capacity"]["value"], B.MOE_F32)
+    res = L.dispatch(shape, ids, gates)
+    dref = O.dispatch(ids.cpu().numpy(), gates.cpu().numpy(), 4, g["capacity"]["value"])
+    P.compare_dispatch(res, dref)
+    drop = P.to_np(res["drop_mask"])[:, 0]
+    assert list(np.nonzero(drop)[0]) == [g["dropped_token"]["value"]]
+    off = P.to_np(res["offsets"]); rt = P.to_np(res["row_token"])
+    kept = [sorted(rt[off[e]:off[e + 1]].tolist()) for e in range(4)]
+    assert kept == [sorted(b) for b in g["kept_batches"]["value"]]
+
+
+def _forced_routing_inputs():
+    """d = E = 4; router = 4 * permutation so expert e reads feature pi(e); x rows are chosen
+    so routing reproduces the worked example's assignment, token 0 is the page's x_0, and
+    token 4 is the least confident of expert 0's three tokens."""
+    g = pins.golden()
+    pi = [2, 0, 1, 3]
+    w_router = np.zeros((4, 4), np.float32)
+    for e, j in enumerate(pi):
+        w_router[e, j] = 4.0
+    x = np.array([g["x0"]["value"],
+                  [1.2, 0.1, 0.3, -0.2],
+                  [0.1, 0.0, 1.0, -0.5],
+                  [0.2, 1.5, -0.4, 0.1],
+                  [0.3, 0.2, 0.45, -0.0],
+                  [0.9, -0.2, 0.1, 0.4],
+                  [0.1, 0.2, -0.3, 1.1],
+                  [-0.5, 0.3, 0.2, 0.7]], np.float32)
+    inp = W.make_inputs("worked_example")
+    inp["x"], inp["w_router"], inp["b_router"] = x, w_router, None
+    return inp
+
+
+def test_worked_example_forced_end_to_end():
+    g = pins.golden()
+    inp = _forced_routing_inputs()
+    f64 = lambda a: W.to_float64(a, "f32")
+    ref = O.forward(f64(inp["x"]), f64(inp["w_router"]), None, f64(inp["w1"]), f64(inp["b1"]),
+                    f64(inp["w2"]), f64(inp["b2"]), 1, 1.25)
+    assert list(ref["ids"][:, 0]) == g["assignment"]["ids"]
+    assert list(np.nonzero(ref["drop_mask"][:, 0])[0]) == [g["dropped_token"]["value"]]
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, 1, ref["cap"])
+    assert list(P.to_np(res["ids"])[:, 0]) == g["assignment"]["ids"]
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), ref)
+    P.compare_dispatch(res, ref)
+    err = P.max_abs_rel(P.to_np(res["out"]), ref["out"])
+    assert err <= P.TOL["f32"], err
+    t4 = g["dropped_token"]["value"]
+    assert np.array_equal(P.bits(res["out"][t4]), P.bits(dev["x"][t4]))
+    assert np.signbit(P.to_np(res["out"])[t4, 3])
+
+
+def test_worked_example_config_end_to_end():
+    inp, ref, cap = case("worked_example")
+    wl = inp["workload"]
+    f64 = lambda a: W.to_float64(a, "f32")
+    full = O.forward(f64(inp["x"]), f64(inp["w_router"]), None, f64(inp["w1"]), f64(inp["b1"]),
+                     f64(inp["w2"]), f64(inp["b2"]), wl.top_k, wl.capacity_factor)
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, wl.top_k, cap)
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full)
+    P.compare_dispatch(res, full)
+    assert P.max_abs_rel(P.to_np(res["out"]), full["out"]) <= P.TOL["f32"]
+    dropped = np.nonzero(full["all_dropped"])[0]
+    for t in dropped:
+        assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
+
+
+# --------------------------------------------------------------------------- full-size configs
+@pytest.mark.parametrize("key", ["mid", "decode", "fine", "collapse"])
+def test_config_end_to_end(key):
+    inp, ref, cap = case(key)
+    wl = inp["workload"]
+    say(f"[{key}] {wl.name} cap={cap}")
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, wl.top_k, cap)
+    torch.cuda.synchronize()
+    ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
+    info = P.compare_route(ids, gates, ref)
+    say(f"    route: {len(info['mismatched_tokens'])} tokens differ (certified ambiguous)")
+    dref = O.dispatch(ids, gates, wl.n_experts, cap)
+    P.compare_dispatch(res, dref)
+    say(f"    dispatch exact; kept {dref['n_kept']} of {wl.T * wl.top_k}")
+    n_dropped = check_sampled_outputs(inp, res["out"], ids, gates, dref)
+    say(f"    {n_dropped} tokens fully dropped, bitwise equal to x")
+
+    # staged calls: same kernels, bitwise-identical results, and Y rows against the oracle
+    shape = L.shape_of(dev, wl.top_k, cap)
+    st = L.dispatch(shape, res["ids"], res["gates"])
+    P.compare_dispatch(st, dref)
+    y = L.expert_ffn(shape, dev, st["row_token"], st["offsets"])
+    check_sampled_y(inp, y, dref)
+    out2 = L.combine(shape, dev["x"], res["gates"], st["slot_of"], y)
+    assert torch.equal(out2.view(torch.int16), res["out"].view(torch.int16))
+    del dev, res, st, y, out2
+    torch.cuda.empty_cache()
+
+
+def test_determinism_mid():
+    inp, ref, cap = case("mid")
+    wl = inp["workload"]
+    dev = L.upload(inp, DEV)
+    ws = L.workspace(L.shape_of(dev, wl.top_k, cap), DEV)
+    a = L.layer_forward(dev, wl.top_k, cap, ws=ws)
+    ws.fill_(0xA5)  # stale workspace content must not matter
+    b = L.layer_forward(dev, wl.top_k, cap, ws=ws)
+    for name in a:
+        assert np.array_equal(P.bits(a[name]) if a[name].is_floating_point() else P.to_np(a[name]),
+                              P.bits(b[name]) if b[name].is_floating_point() else P.to_np(b[name])), name
+
+
+# --------------------------------------------------------------------------- randomized shapes
+SMALL = [
+    # T, d, f, E, k, C, dtype
+    (1, 64, 64, 1, 1, 1.0, "bf16"),
+    (7, 72, 136, 2, 2, 1.0, "bf16"),
+    (63, 128, 200, 3, 2, 0.5, "bf16"),
+    (65, 264, 328, 8, 2, 1.25, "bf16"),
+    (1000, 136, 72, 8, 3, 1.0, "bf16"),
+    (1000, 64, 520, 64, 6, 1.5, "bf16"),
+    (300, 128, 256, 16, 4, 0.25, "bf16"),
+    (517, 256, 264, 5, 1, 8.0, "bf16"),
+    (1, 4, 8, 4, 1, 1.25, "f32"),
+    (7, 5, 9, 3, 2, 1.0, "f32"),
+    (65, 12, 20, 8, 2, 0.75, "f32"),
+    (333, 24, 40, 64, 8, 1.0, "f32"),
+    (200, 16, 16, 200, 3, 2.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,C,dt", SMALL)
+def test_random_small_shapes(T, d, f, E, k, C, dt):
+    inp = W.make_shape_inputs(T, d, f, E, dt, seed=T * 31 + E, router_bias_std=1.0)
+    f64 = lambda a: W.to_float64(a, dt)
+    full = O.forward(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], f64(inp["w1"]),
+                     f64(inp["b1"]), f64(inp["w2"]), f64(inp["b2"]), k, C)
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, k, full["cap"])
+    ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
+    P.compare_route(ids, gates, full)
+    dref = O.dispatch(ids, gates, E, full["cap"])
+    P.compare_dispatch(res, dref)
+    Y = O.expert_ffn_slots(f64(inp["x"]), dref["row_token"], dref["offsets"], f64(inp["w1"]),
+                           f64(inp["b1"]), f64(inp["w2"]), f64(inp["b2"]))
+    out_ref, all_dropped = O.combine(f64(inp["x"]), gates, dref["slot_of"], Y)
+    assert P.max_abs_rel(P.to_np(res["out"]), out_ref) <= P.TOL[dt]
+    for t in np.nonzero(all_dropped)[0]:
+        assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gate_ties(dt):
+    """Integer-valued x and router weights: many tokens share exactly the same gates, so the
+    fill order's token and choice tie-breaks decide the slots."""
+    T, d, f, E, k = 500, 16, 24, 6, 2
+    inp = W.make_shape_inputs(T, d, f, E, dt, seed=5, x_values=(-1.0, 0.0, 1.0))
+    f64 = lambda a: W.to_float64(a, dt)
+    full = O.forward(f64(inp["x"]), f64(inp["w_router"]), None, f64(inp["w1"]), f64(inp["b1"]),
+                     f64(inp["w2"]), f64(inp["b2"]), k, 0.75)
+    n_tied = len(full["gates"].ravel()) - len(np.unique(full["gates"].ravel()))
+    assert n_tied > 100
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, k, full["cap"])
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full)
+    P.compare_dispatch(res, full)
+    assert P.max_abs_rel(P.to_np(res["out"]), full["out"]) <= P.TOL[dt]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dispatch_forced_patterns(seed):
+    """moe_dispatch on caller-made routings: ties, -0.0, big experts spanning several sort
+    chunks, capacities from 0 to above T, and out-of-range ids (dropped, not counted)."""
+    rng = np.random.Generator(np.random.PCG64(100 + seed))
+    T = [5, 3000, 20000, 70000, 1, 9000][seed]
+    E = [3, 8, 64, 4, 1, 256][seed]
+    k = min(E, [2, 2, 6, 2, 1, 3][seed])
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32) if T < 5000 else \
+        np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    if seed == 3:
+        ids[:, 0] = 0  # one hot expert with T assignments: several sort chunks
+    vals = np.array([0.5, 0.25, -0.0, 0.0, 0.125, 0.75], np.float32)
+    gates = vals[rng.integers(len(vals), size=(T, k))] if seed % 2 == 0 else \
+        rng.random((T, k)).astype(np.float32)
+    bad = np.zeros((T, k), bool)
+    if seed in (1, 5):
+        bad = rng.random((T, k)) < 0.01
+        ids[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+    cap = [0, 400, 1536, 16384, 1, 120][seed]
+    shape = B.make_shape(T, 8, 8, E, k, cap, B.MOE_BF16)
+    res = L.dispatch(shape, torch.from_numpy(ids).to(DEV), torch.from_numpy(gates).to(DEV))
+    # the oracle knows no invalid ids: give them an extra last expert E, which leaves the
+    # valid experts' counts and slots unchanged; their own slots are then ignored
+    dref = O.dispatch(np.where(bad, E, ids).astype(np.int32), gates, E + 1, cap)
+    counts = dref["counts"][:E]
+    assert np.array_equal(P.to_np(res["counts"]), counts)
+    kept = np.minimum(counts, cap)
+    assert np.array_equal(P.to_np(res["offsets"]), np.concatenate([[0], np.cumsum(kept)]))
+    so = dref["slot_of"].copy()
+    so[bad] = -1
+    assert np.array_equal(P.to_np(res["slot_of"]), so)
+    assert np.array_equal(P.to_np(res["drop_mask"]), (so < 0).astype(np.uint8))
+    n = int(kept.sum())
+    assert np.array_equal(P.to_np(res["row_token"])[:n], dref["row_token"][:n])
+
+
+def test_capacity_zero_returns_input():
+    inp = W.make_shape_inputs(100, 64, 64, 8, "bf16", seed=3)
+    inp["x"][5, 3] = 0x8000  # -0.0
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward(dev, 2, 0)
+    assert torch.equal(res["out"].view(torch.int16), dev["x"].view(torch.int16))
+    assert int(res["drop_mask"].sum()) == 200
+
+
+def test_empty_batch_is_a_no_op():
+    inp = W.make_shape_inputs(4, 64, 64, 4, "bf16", seed=3)
+    dev = L.upload(inp, DEV)
+    dev["x"] = dev["x"][:0]
+    res = L.layer_forward(dev, 2, 0)
+    assert res["out"].shape == (0, 64)
+
+
+def test_short_workspace_is_refused():
+    inp = W.make_shape_inputs(64, 64, 64, 4, "bf16", seed=3)
+    dev = L.upload(inp, DEV)
+    shape = L.shape_of(dev, 2, 32)
+    ws = torch.empty(B.workspace_bytes(shape) - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.MoeError) as ei:
+        L.layer_forward(dev, 2, 32, ws=ws)
+    assert ei.value.status == 3
