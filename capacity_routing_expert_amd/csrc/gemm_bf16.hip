@@ -82,7 +82,7 @@ __global__ __launch_bounds__(WN* WM * 64, 1) void k_grouped_gemm(
       if (lane >= off) inc += o;
     }
     const int excl = inc - local;
-    const int total = __shfl(inc, 63, 64);
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
     if (mt >= total) return;  // same decision in every wave of the block
     const uint64_t bal = __ballot(mt >= excl && mt < inc);
     const int owner = __ffsll((long long)bal) - 1;
@@ -95,56 +95,48 @@ __global__ __launch_bounds__(WN* WM * 64, 1) void k_grouped_gemm(
       }
       run += te[j];
     }
-    e = __shfl(esel, owner, 64) - 1;
-    tstart = __shfl(tstart, owner, 64);
+    // the same in every lane: make it scalar so the buffer resources live in SGPRs
+    e = __builtin_amdgcn_readfirstlane(__shfl(esel, owner, 64) - 1);
+    tstart = __builtin_amdgcn_readfirstlane(__shfl(tstart, owner, 64));
     row0 = offsets[e] + (mt - tstart) * TM;
     rows = min(TM, offsets[e + 1] - row0);
   }
 
-  // ---- per-thread load plan (rows are fixed for the whole K loop)
-  const bf16_t* wptr[kWPer];
-  bool wok[kWPer];
-  int wdst[kWPer], wcol[kWPer];
+  // ---- per-thread load plan.  Thread tid moves 16-byte chunk c = tid % 8 of rows
+  // tid / 8 + r * kRowStep (r = 0 .. kWPer-1 / kXPer-1) of each operand tile.  Loads go through
+  // buffer resources whose range covers only the valid rows: an out-of-range offset reads as
+  // zero, so ragged tiles need no branches; chunks past K are sent out of range too.
+  constexpr int kRowStep = kThreads / 8;
+  const int c8 = (tid & 7) * 8;           // first K element of this thread's chunk
+  const int trow = tid >> 3;              // first tile row of this thread
+  const uint32_t kOut = 0x80000000u;      // an offset beyond every buffer range used here
+  const int n0 = nt * TN;
+  const int wrows = min(TN, N - n0);
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + ((int64_t)e * N + n0) * K), (short)0, wrows * K * 2, 0x00020000);
+  const uint32_t woff = (uint32_t)(trow * K + c8) * 2u;
+  const uint32_t wstep = (uint32_t)kRowStep * K * 2u;
+  __amdgpu_buffer_rsrc_t xsrc;
+  uint32_t xoff[kXPer];
+  if (GATHER) {
+    // x rows of the tile's tokens; the whole x is one resource (T * K * 2 < 2^31, checked on host)
+    xsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-  for (int r = 0; r < kWPer; ++r) {
-    const int q = tid + r * kThreads, row = q >> 3, c = q & 7;
-    const int n = nt * TN + row;
-    wok[r] = n < N;
-    wptr[r] = W + ((int64_t)e * N + (wok[r] ? n : 0)) * K + c * 8;
-    wdst[r] = row * 8 + (c ^ (row & 7));
-    wcol[r] = c * 8;
-  }
-  const bf16_t* xptr[kXPer];
-  bool xok[kXPer];
-  int xdst[kXPer], xcol[kXPer];
+    for (int r = 0; r < kXPer; ++r) {
+      const int row = trow + r * kRowStep;
+      xoff[r] = row < rows ? (uint32_t)(row_token[row0 + row] * K + c8) * 2u : kOut;
+    }
+  } else {
+    xsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)row0 * K), (short)0, rows * K * 2,
+                                             0x00020000);
 #pragma unroll
-  for (int r = 0; r < kXPer; ++r) {
-    const int q = tid + r * kThreads, row = q >> 3, c = q & 7;
-    xok[r] = row < rows;
-    int src = 0;
-    if (xok[r]) src = GATHER ? row_token[row0 + row] : row0 + row;
-    xptr[r] = A + (int64_t)src * K + c * 8;
-    xdst[r] = row * 8 + (c ^ (row & 7));
-    xcol[r] = c * 8;
+    for (int r = 0; r < kXPer; ++r) xoff[r] = (uint32_t)((trow + r * kRowStep) * K + c8) * 2u;
   }
+  // LDS destinations: chunk c of row `row` lives at row * 8 + (c ^ (row & 7)); row & 7 is the
+  // same for all r because kRowStep is a multiple of 8
+  const int sdst = trow * 8 + ((tid & 7) ^ (trow & 7));
 
   uint4 rw[kWPer], rx[kXPer];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int kt) {
-    const int k0 = kt * 64;
-#pragma unroll
-    for (int r = 0; r < kWPer; ++r)
-      rw[r] = (wok[r] && k0 + wcol[r] < K) ? *reinterpret_cast<const uint4*>(wptr[r] + k0) : zero;
-#pragma unroll
-    for (int r = 0; r < kXPer; ++r)
-      rx[r] = (xok[r] && k0 + xcol[r] < K) ? *reinterpret_cast<const uint4*>(xptr[r] + k0) : zero;
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < kWPer; ++r) sW[buf * TN * 8 + wdst[r]] = rw[r];
-#pragma unroll
-    for (int r = 0; r < kXPer; ++r) sX[buf * TM * 8 + xdst[r]] = rx[r];
-  };
 
   f32x16_t acc[FN][FM];
 #pragma unroll
@@ -155,36 +147,54 @@ __global__ __launch_bounds__(WN* WM * 64, 1) void k_grouped_gemm(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = (K + 63) / 64;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int r32 = lane & 31, half = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint4* bw = sW + buf * TN * 8;
-    const uint4* bx = sX + buf * TM * 8;
+  for (int kt = -1; kt < nk; ++kt) {
+    // global loads of stage kt + 1 (in flight while stage kt computes)
+    if (kt + 1 < nk) {
+      const int k0 = (kt + 1) * 64;
+      const bool kin = k0 + c8 < K;
+      const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = kk * 2 + half;
-      bf16x8_t a[FN], b[FM];
+      for (int r = 0; r < kWPer; ++r)
+        rw[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    wsrc, kin ? woff + r * wstep + kb : kOut, 0, 0));
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * (TN / WN) + i * 32 + r32;
-        a[i] = as_bf16x8(bw[row * 8 + (ch ^ (row & 7))]);
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * (TM / WM) + j * 32 + r32;
-        b[j] = as_bf16x8(bx[row * 8 + (ch ^ (row & 7))]);
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int r = 0; r < kXPer; ++r)
+        rx[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    xsrc, (kin && xoff[r] != kOut) ? xoff[r] + kb : kOut, 0, 0));
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt >= 0) {
+      const int buf = kt & 1;
+      const uint4* bw = sW + buf * TN * 8;
+      const uint4* bx = sX + buf * TM * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = kk * 2 + half;
+        bf16x8_t a[FN], b[FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int row = wn * (TN / WN) + i * 32 + r32;
+          a[i] = as_bf16x8(bw[row * 8 + (ch ^ (row & 7))]);
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int row = wm * (TM / WM) + j * 32 + r32;
+          b[j] = as_bf16x8(bx[row * 8 + (ch ^ (row & 7))]);
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) {
+      const int buf = (kt + 1) & 1;
+#pragma unroll
+      for (int r = 0; r < kWPer; ++r) sW[buf * TN * 8 + sdst + r * kRowStep * 8] = rw[r];
+#pragma unroll
+      for (int r = 0; r < kXPer; ++r) sX[buf * TM * 8 + sdst + r * kRowStep * 8] = rx[r];
+    }
     __syncthreads();
   }
 
