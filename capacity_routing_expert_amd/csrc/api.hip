@@ -111,7 +111,8 @@ Workspace layout(const moe_shape& s) {
     o = align256(o + bytes);
     return at_;
   };
-  w.w64 = take((size_t)E * s.d_model * 8);
+  const int64_t G = route_emax((int)E);
+  w.w64 = take((size_t)((E + G - 1) / G) * G * s.d_model * 8);
   w.ids = take((size_t)N * 4);
   w.gates = take((size_t)N * 4);
   w.slot_of = take((size_t)N * 4);
@@ -121,6 +122,7 @@ Workspace layout(const moe_shape& s) {
   w.seg_start = take((size_t)(E + 2) * 4);
   w.blk_hist = take((size_t)nb * (E + 1) * 4);
   w.keys = take((size_t)N * 8);
+  w.rank = take((size_t)N * 4);
   w.row_token = take((size_t)rows * 4);
   w.h = take((size_t)rows * s.d_ff * elem_bytes(s));
   w.y = take((size_t)rows * s.d_model * elem_bytes(s));
@@ -143,7 +145,7 @@ moe_status do_dispatch(const moe_shape& s, const int32_t* ids, const float* gate
   const Workspace L = layout(s);
   hipError_t err = launch_dispatch(s, ids, gates, counts, offsets, slot_of, row_token, drop,
                                    at<int32_t>(ws, L.seg_start), at<int32_t>(ws, L.blk_hist),
-                                   at<uint64_t>(ws, L.keys), st);
+                                   at<uint64_t>(ws, L.keys), at<int32_t>(ws, L.rank), st);
   return err == hipSuccess ? MOE_OK : device_error(err, "dispatch");
 }
 

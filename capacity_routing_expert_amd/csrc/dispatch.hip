@@ -17,13 +17,13 @@
 //                      base), then scatters its keys stably into per-expert buckets using
 //                      the same ballot match for the in-wave rank; block 0 publishes the
 //                      counts, the kept-slot offsets and the bucket starts;
-//   k_dispatch_rank    one block per kRankChunk keys of one expert bucket: bitonic sort in
-//                      LDS; a bucket that fits one chunk has its ranks right there and emits
-//                      slot_of / drop_mask / row_token; larger buckets write the sorted chunk;
-//   k_dispatch_merge   only for buckets spanning several chunks: rank = position in own
-//                      chunk + lower bounds in the bucket's other sorted chunks (staged
-//                      through LDS), then emit.
-// No floating-point atomics, no order-dependent reductions: the result is deterministic.
+//   k_dispatch_tilesort each 256-key tile of a bucket is sorted in LDS (bitonic network);
+//   k_dispatch_rank    rank of a key = number of smaller keys of its bucket: its position in
+//                      its own sorted tile plus a binary search in every other tile of the
+//                      bucket; blocks take (tile, group of 16 other tiles) work items and add
+//                      their partial counts with integer atomics (exact and order-free);
+//   k_dispatch_emit    slot_of / drop_mask / row_token from the ranks and the capacity.
+// Integer results only, no order-dependent reductions: the output is deterministic.
 #include "moe_internal.h"
 
 namespace moe {
@@ -103,10 +103,10 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
     const int32_t* __restrict__ ids, const float* __restrict__ gates, int64_t N, int E, int cap,
     int nb, const int32_t* __restrict__ blk_hist, uint64_t* __restrict__ keys,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ seg_start,
-    int32_t* __restrict__ slot_of, uint8_t* __restrict__ drop) {
+    int32_t* __restrict__ rank, int32_t* __restrict__ slot_of, uint8_t* __restrict__ drop) {
   __shared__ int s_cnt[260], s_run[260], s_kept[260];
   __shared__ int wcnt[4][260];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int e = tid; e <= E; e += 256) {
     int tot = 0, pre = 0;
     for (int b = 0; b < nb; ++b) {
@@ -143,12 +143,13 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
     int e = valid ? ids[i] : 0;
     if (e < 0 || e >= E) e = E;
     const uint64_t peers = match_key(e, valid);
-    const int rank = __popcll(peers & lanemask_lt());
-    if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
+    const int wrank = __popcll(peers & lanemask_lt());
+    if (valid && wrank == 0) wcnt[wave][e] = __popcll(peers);
     __syncthreads();
     if (valid) {
-      int pos = s_run[e] + rank;
+      int pos = s_run[e] + wrank;
       for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      rank[pos] = 0;
       if (e < E) {
         keys[pos] = sort_key(gates[i], (uint32_t)i);
       } else {
@@ -168,59 +169,126 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
 
 namespace {
 
-constexpr int kRankThreads = 512;
+constexpr int kTile = 256;        // keys per sorted tile (one per thread)
+constexpr int kTilesPerItem = 16;  // other tiles one rank work item searches
 
-// Which (expert, chunk) this block serves; returns false if the block has no chunk.
-// Called by every thread of the block (contains barriers).
-__device__ bool find_chunk(const int32_t* __restrict__ counts, int E, int* s_pref, int* out_e,
-                           int* out_j) {
-  __shared__ int s_e, s_j, s_ok;
-  for (int e = threadIdx.x; e <= E; e += blockDim.x)
-    s_pref[e] = e < E ? (counts[e] + kRankChunk - 1) / kRankChunk : 0;
+__device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
+
+// s_pre[e] = exclusive prefix over experts of f(counts[e]), s_pre[E] = total; every thread calls.
+template <typename F>
+__device__ void expert_prefix(const int32_t* __restrict__ counts, int E, int* s_pre, F f) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) s_pre[e] = e < E ? f(counts[e]) : 0;
   __syncthreads();
-  if ((threadIdx.x >> 6) == 0) wave_exclusive_scan(s_pref, E + 1, nullptr);
+  if ((threadIdx.x >> 6) == 0) wave_exclusive_scan(s_pre, E + 1, nullptr);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int b = blockIdx.x;
-    s_ok = 0;
-    for (int e = 0; e < E; ++e) {
-      if (b >= s_pref[e] && b < s_pref[e + 1]) {
-        s_e = e;
-        s_j = b - s_pref[e];
-        s_ok = 1;
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  *out_e = s_e;
-  *out_j = s_j;
-  return s_ok != 0;
 }
 
-__device__ void bitonic_sort(uint64_t* a, int P) {
-  for (int size = 2; size <= P; size <<= 1) {
+// the e with s_pre[e] <= w < s_pre[e+1] (s_pre non-decreasing, w < s_pre[E])
+__device__ __forceinline__ int find_expert(const int* s_pre, int E, int w) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kTile) void k_dispatch_tilesort(uint64_t* __restrict__ keys,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ seg_start,
+                                                             int E) {
+  __shared__ int s_pre[260];
+  __shared__ uint64_t sk[kTile];
+  expert_prefix(counts, E, s_pre, [](int n) { return tiles_of(n); });
+  const int w = blockIdx.x;
+  if (w >= s_pre[E]) return;  // uniform
+  const int e = find_expert(s_pre, E, w);
+  const int a = w - s_pre[e];
+  const int n = counts[e];
+  const int m = min(kTile, n - a * kTile);
+  const int64_t base = (int64_t)seg_start[e] + (int64_t)a * kTile;
+  const int t = threadIdx.x;
+  sk[t] = t < m ? keys[base + t] : ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= kTile; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int idx = threadIdx.x; idx < (P >> 1); idx += kRankThreads) {
-        const int lo = 2 * idx - (idx & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t x = a[lo], y = a[hi];
-        if ((x > y) == up) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
+      const int partner = t ^ stride;
+      const uint64_t mine = sk[t], other = sk[partner];
+      const bool up = (t & size) == 0;
+      const bool lower = t < partner;
+      // keep the smaller key at the lower index of an ascending pair, the larger otherwise
+      const uint64_t keep = (lower == up) ? (mine < other ? mine : other) : (mine < other ? other : mine);
+      __syncthreads();
+      sk[t] = keep;
       __syncthreads();
     }
   }
+  if (t < m) keys[base + t] = sk[t];
 }
 
-__device__ __forceinline__ void emit(uint64_t key, int r, int e, int k, int cap,
-                                     const int32_t* __restrict__ offsets,
-                                     int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token,
-                                     uint8_t* __restrict__ drop) {
+__global__ __launch_bounds__(kTile) void k_dispatch_rank(const uint64_t* __restrict__ keys,
+                                                         const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ seg_start,
+                                                         int E, int32_t* __restrict__ rank) {
+  __shared__ int s_pre[260];
+  __shared__ uint64_t sk[kTile];
+  // work items of expert e: (own tile a, group g of kTilesPerItem tiles)
+  expert_prefix(counts, E, s_pre, [](int n) {
+    const int nt = tiles_of(n);
+    return nt * ((nt + kTilesPerItem - 1) / kTilesPerItem);
+  });
+  const int total = s_pre[E];
+  const int t = threadIdx.x;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int e = find_expert(s_pre, E, w);
+    const int n = counts[e];
+    const int nt = tiles_of(n);
+    const int ng = (nt + kTilesPerItem - 1) / kTilesPerItem;
+    const int a = (w - s_pre[e]) / ng, g = (w - s_pre[e]) % ng;
+    const int64_t seg = seg_start[e];
+    const int own_pos = a * kTile + t;
+    const uint64_t mine = own_pos < n ? keys[seg + own_pos] : ~0ull;
+    int cnt = 0;
+    const int b_end = min(nt, (g + 1) * kTilesPerItem);
+    for (int b = g * kTilesPerItem; b < b_end; ++b) {
+      if (b == a) {
+        cnt += t;  // sorted own tile: t keys are smaller
+        continue;
+      }
+      const int mb = min(kTile, n - b * kTile);
+      __syncthreads();
+      sk[t] = t < mb ? keys[seg + (int64_t)b * kTile + t] : ~0ull;
+      __syncthreads();
+      int lo = 0, hi = mb;  // first index with sk[idx] >= mine
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sk[mid] < mine) lo = mid + 1; else hi = mid;
+      }
+      cnt += lo;
+    }
+    if (own_pos < n && cnt) atomicAdd(&rank[seg + own_pos], cnt);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_emit(const uint64_t* __restrict__ keys,
+                                                       const int32_t* __restrict__ rank,
+                                                       const int32_t* __restrict__ seg_start,
+                                                       const int32_t* __restrict__ offsets, int E,
+                                                       int k, int cap, int32_t* __restrict__ slot_of,
+                                                       int32_t* __restrict__ row_token,
+                                                       uint8_t* __restrict__ drop) {
+  __shared__ int s_seg[260];
+  for (int e = threadIdx.x; e <= E; e += 256) s_seg[e] = seg_start[e];
+  __syncthreads();
+  const int pos = blockIdx.x * 256 + threadIdx.x;
+  if (pos >= s_seg[E]) return;  // past the valid buckets
+  const int e = find_expert(s_seg, E, pos);
+  const uint64_t key = keys[pos];
   const uint32_t i = (uint32_t)(key & 0xFFFFFFFFull);
+  const int r = rank[pos];
   if (r < cap) {
     const int s = offsets[e] + r;
     slot_of[i] = s;
@@ -232,94 +300,23 @@ __device__ __forceinline__ void emit(uint64_t key, int r, int e, int k, int cap,
   }
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kRankThreads) void k_dispatch_rank(
-    uint64_t* __restrict__ keys, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ seg_start, int E, int k,
-    int cap, int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token,
-    uint8_t* __restrict__ drop) {
-  __shared__ uint64_t sk[kRankChunk];
-  __shared__ int s_pref[260];
-  int e, j;
-  if (!find_chunk(counts, E, s_pref, &e, &j)) return;
-  const int n = counts[e];
-  const int64_t start = (int64_t)seg_start[e] + (int64_t)j * kRankChunk;
-  const int m = min(kRankChunk, n - j * kRankChunk);
-  int P = 64;
-  while (P < m) P <<= 1;
-  for (int p = threadIdx.x; p < P; p += kRankThreads) sk[p] = p < m ? keys[start + p] : ~0ull;
-  __syncthreads();
-  bitonic_sort(sk, P);
-  if (n <= kRankChunk) {
-    for (int p = threadIdx.x; p < m; p += kRankThreads)
-      emit(sk[p], p, e, k, cap, offsets, slot_of, row_token, drop);
-  } else {
-    for (int p = threadIdx.x; p < m; p += kRankThreads) keys[start + p] = sk[p];
-  }
-}
-
-__global__ __launch_bounds__(kRankThreads) void k_dispatch_merge(
-    const uint64_t* __restrict__ keys, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ seg_start, int E, int k,
-    int cap, int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token,
-    uint8_t* __restrict__ drop) {
-  __shared__ uint64_t sk[kRankChunk];
-  __shared__ int s_pref[260];
-  constexpr int PER = kRankChunk / kRankThreads;
-  int e, j;
-  if (!find_chunk(counts, E, s_pref, &e, &j)) return;
-  const int n = counts[e];
-  if (n <= kRankChunk) return;
-  const int nch = (n + kRankChunk - 1) / kRankChunk;
-  const int64_t seg = seg_start[e];
-  const int m = min(kRankChunk, n - j * kRankChunk);
-  uint64_t mine[PER];
-  int rank[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int p = threadIdx.x + u * kRankThreads;
-    mine[u] = p < m ? keys[seg + (int64_t)j * kRankChunk + p] : ~0ull;
-    rank[u] = p;
-  }
-  for (int jj = 0; jj < nch; ++jj) {
-    if (jj == j) continue;
-    const int mm = min(kRankChunk, n - jj * kRankChunk);
-    __syncthreads();
-    for (int p = threadIdx.x; p < mm; p += kRankThreads) sk[p] = keys[seg + (int64_t)jj * kRankChunk + p];
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      int lo = 0, hi = mm;  // first position with sk[pos] >= mine (keys are unique)
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sk[mid] < mine[u]) lo = mid + 1; else hi = mid;
-      }
-      rank[u] += lo;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int p = threadIdx.x + u * kRankThreads;
-    if (p < m) emit(mine[u], rank[u], e, k, cap, offsets, slot_of, row_token, drop);
-  }
-}
-
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
-                           int32_t* blk_hist, uint64_t* keys, hipStream_t st) {
+                           int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st) {
   const int64_t N = s.T * (int64_t)s.top_k;
   const int E = s.n_experts;
   const int nb = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
   hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, blk_hist);
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(nb), dim3(256), 0, st, ids, gates, N, E, s.capacity,
-                     nb, blk_hist, keys, counts, offsets, seg_start, slot_of, drop);
-  const int grid = (int)((N + kRankChunk - 1) / kRankChunk) + E;
-  hipLaunchKernelGGL(k_dispatch_rank, dim3(grid), dim3(kRankThreads), 0, st, keys, counts, offsets,
-                     seg_start, E, s.top_k, s.capacity, slot_of, row_token, drop);
-  hipLaunchKernelGGL(k_dispatch_merge, dim3(grid), dim3(kRankThreads), 0, st, keys, counts,
-                     offsets, seg_start, E, s.top_k, s.capacity, slot_of, row_token, drop);
+                     nb, blk_hist, keys, counts, offsets, seg_start, rank, slot_of, drop);
+  const int tiles_ub = (int)((N + kTile - 1) / kTile) + E;  // >= sum over experts of tiles
+  hipLaunchKernelGGL(k_dispatch_tilesort, dim3(tiles_ub), dim3(kTile), 0, st, keys, counts,
+                     seg_start, E);
+  hipLaunchKernelGGL(k_dispatch_rank, dim3(1024), dim3(kTile), 0, st, keys, counts, seg_start, E,
+                     rank);
+  hipLaunchKernelGGL(k_dispatch_emit, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, keys,
+                     rank, seg_start, offsets, E, s.top_k, s.capacity, slot_of, row_token, drop);
   return hipGetLastError();
 }
 

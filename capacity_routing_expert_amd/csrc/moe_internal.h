@@ -26,7 +26,7 @@ __device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
 // ---------------------------------------------------------------- workspace layout
 // One workspace buffer serves every call; each sub-buffer starts on a 256-byte boundary.
 struct Workspace {
-  size_t w64;        // router weights widened to fp64            [E, d]
+  size_t w64;        // router weights widened to fp64    [ceil(E/G) * G, d], G = route_emax(E)
   size_t ids;        // top-k expert ids (layer_forward)          [T*k] int32
   size_t gates;      // top-k gates                               [T*k] f32
   size_t slot_of;    // slot per assignment                       [T*k] int32
@@ -36,6 +36,7 @@ struct Workspace {
   size_t seg_start;  // start of each expert's bucket in `keys`   [E+2] int32
   size_t blk_hist;   // per-block expert histograms               [nb, E+1] int32
   size_t keys;       // bucketed sort keys                        [T*k] u64
+  size_t rank;       // rank of each bucketed key in its expert   [T*k] int32
   size_t row_token;  // token per slot                            [max_rows] int32
   size_t h;          // activation between the GEMMs              [max_rows, d_ff]
   size_t y;          // expert outputs per slot                   [max_rows, d_model]
@@ -43,9 +44,9 @@ struct Workspace {
 };
 
 constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
-constexpr int kRankChunk = 4096;      // keys sorted per block in the rank kernels
 
 int64_t max_rows(const moe_shape& s);
+int route_emax(int E);  // experts per register group of the router kernel
 Workspace layout(const moe_shape& s);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
@@ -56,7 +57,7 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
-                           int32_t* blk_hist, uint64_t* keys, hipStream_t st);
+                           int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st);
 
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const void* w1, const void* b1, void* h,

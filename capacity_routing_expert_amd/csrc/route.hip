@@ -22,16 +22,19 @@
 
 namespace moe {
 
-// Router weights widened to fp64 and transposed to [d][E], so that the E weights of one
-// column are contiguous (wide scalar loads).
+// Router weights widened to fp64 and laid out [group][d][EMAX] (experts g*EMAX .. g*EMAX +
+// EMAX-1 of one column contiguous, zero-padded past E), so a column's weights are one aligned
+// run of EMAX doubles: wide unconditional scalar loads.
 template <typename TIn>
-__global__ void k_router_weights_f64(const TIn* __restrict__ w, double* __restrict__ w64t,
-                                     int d, int E) {
-  const int64_t n = (int64_t)d * E;
+__global__ void k_router_weights_f64(const TIn* __restrict__ w, double* __restrict__ w64,
+                                     int d, int E, int EMAX) {
+  const int G = (E + EMAX - 1) / EMAX;
+  const int64_t n = (int64_t)G * d * EMAX;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t j = i / E, e = i % E;
-    w64t[i] = (double)load_as_f32(w + e * d + j);
+    const int64_t g = i / ((int64_t)d * EMAX), rem = i % ((int64_t)d * EMAX);
+    const int64_t j = rem / EMAX, e = g * EMAX + rem % EMAX;
+    w64[i] = e < E ? (double)load_as_f32(w + e * d + j) : 0.0;
   }
 }
 
@@ -39,10 +42,12 @@ template <typename TIn>
 struct VecLoad;
 template <>
 struct VecLoad<bf16_t> {
-  static constexpr int VW = 8;
-  __device__ __forceinline__ static void load(const bf16_t* p, double* v) {
-    uint4 q = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  static constexpr int VW = 8;  // columns per 16-byte chunk
+  __device__ __forceinline__ static uint4 raw(const bf16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ static void widen(uint4 q, double* v) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = (double)__uint_as_float(w[i] << 16);
@@ -53,9 +58,12 @@ struct VecLoad<bf16_t> {
 template <>
 struct VecLoad<float> {
   static constexpr int VW = 4;
-  __device__ __forceinline__ static void load(const float* p, double* v) {
-    float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  __device__ __forceinline__ static uint4 raw(const float* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ static void widen(uint4 q, double* v) {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
   }
 };
 
@@ -77,7 +85,10 @@ __global__ __launch_bounds__(RouteBounds<EMAX>::kThreads) void k_route(
   extern __shared__ double lds[];  // partials [S][EMAX][64]; then logits/gates [E][64]
   constexpr int VW = VecLoad<TIn>::VW;
   constexpr int TB = 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform by construction; readfirstlane tells the compiler, so addresses built from
+  // it (the router weights) are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t tok0 = (int64_t)blockIdx.x * TB;
   const int64_t t = tok0 + lane;
   const bool tok_ok = t < T;
@@ -87,26 +98,41 @@ __global__ __launch_bounds__(RouteBounds<EMAX>::kThreads) void k_route(
   for (int g = 0; g < n_groups; ++g) {
     const int e0 = g * EMAX;
     const int eg = min(EMAX, E - e0);
+    const double* wg = w64 + (int64_t)g * d * EMAX;  // this group's [d][EMAX] weights
     double acc[EMAX];
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
 
     if (d % VW == 0) {
+      // chunks c = wave, wave + S, ...; four chunk loads in flight before their FMAs
+      constexpr int PF = 4;
       const int nchunk = d / VW;
-      for (int c = wave; c < nchunk; c += S) {
-        double xv[VW];
-        if (tok_ok) {
-          VecLoad<TIn>::load(xrow + (int64_t)c * VW, xv);
-        } else {
+      int c = wave;
+      for (; c + (PF - 1) * S < nchunk; c += PF * S) {
+        uint4 q[PF];
 #pragma unroll
-          for (int v = 0; v < VW; ++v) xv[v] = 0.0;
+        for (int u = 0; u < PF; ++u)
+          q[u] = tok_ok ? VecLoad<TIn>::raw(xrow + (int64_t)(c + u * S) * VW) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          double xv[VW];
+          VecLoad<TIn>::widen(q[u], xv);
+#pragma unroll
+          for (int v = 0; v < VW; ++v) {
+            const double* wc = wg + ((int64_t)(c + u * S) * VW + v) * EMAX;
+#pragma unroll
+            for (int e = 0; e < EMAX; ++e) acc[e] = fma(xv[v], wc[e], acc[e]);
+          }
         }
+      }
+      for (; c < nchunk; c += S) {
+        double xv[VW];
+        VecLoad<TIn>::widen(tok_ok ? VecLoad<TIn>::raw(xrow + (int64_t)c * VW) : make_uint4(0, 0, 0, 0), xv);
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
-          const double* wc = w64 + ((int64_t)c * VW + v) * E + e0;
+          const double* wc = wg + ((int64_t)c * VW + v) * EMAX;
 #pragma unroll
-          for (int e = 0; e < EMAX; ++e)
-            if (e < eg) acc[e] = fma(xv[v], wc[e], acc[e]);
+          for (int e = 0; e < EMAX; ++e) acc[e] = fma(xv[v], wc[e], acc[e]);
         }
       }
     } else {
@@ -114,8 +140,7 @@ __global__ __launch_bounds__(RouteBounds<EMAX>::kThreads) void k_route(
       for (int j = wave; j < d; j += S) {
         const double xv = tok_ok ? (double)load_as_f32(xrow + j) : 0.0;
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e)
-          if (e < eg) acc[e] = fma(xv, w64[(int64_t)j * E + e0 + e], acc[e]);
+        for (int e = 0; e < EMAX; ++e) acc[e] = fma(xv, wg[(int64_t)j * EMAX + e], acc[e]);
       }
     }
 
@@ -221,15 +246,18 @@ hipError_t route_impl(const moe_shape& s, const TIn* x, const float* b_router, i
 }
 }  // namespace
 
+int route_emax(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
+
 hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
                         const float* b_router, int32_t* ids, float* gates, float* logits,
                         double* w64, hipStream_t st) {
-  const int64_t nw = (int64_t)s.n_experts * s.d_model;
+  const int64_t nw = (int64_t)(s.n_experts + route_emax(s.n_experts) - 1) / route_emax(s.n_experts) *
+                    route_emax(s.n_experts) * s.d_model;
   const int cblocks = (int)((nw + 255) / 256 < 1024 ? (nw + 255) / 256 : 1024);
   const int E = s.n_experts, d = s.d_model;
   if (s.dtype == MOE_BF16) {
     hipLaunchKernelGGL(k_router_weights_f64<bf16_t>, dim3(cblocks), dim3(256), 0, st,
-                       (const bf16_t*)w_router, w64, d, E);
+                       (const bf16_t*)w_router, w64, d, E, route_emax(E));
     const bf16_t* xp = (const bf16_t*)x;
     if (E <= 8) return route_impl<bf16_t, 8>(s, xp, b_router, ids, gates, logits, w64, st);
     if (E <= 16) return route_impl<bf16_t, 16>(s, xp, b_router, ids, gates, logits, w64, st);
@@ -237,7 +265,7 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
     return route_impl<bf16_t, 64>(s, xp, b_router, ids, gates, logits, w64, st);
   } else {
     hipLaunchKernelGGL(k_router_weights_f64<float>, dim3(cblocks), dim3(256), 0, st,
-                       (const float*)w_router, w64, d, E);
+                       (const float*)w_router, w64, d, E, route_emax(E));
     const float* xp = (const float*)x;
     if (E <= 8) return route_impl<float, 8>(s, xp, b_router, ids, gates, logits, w64, st);
     if (E <= 16) return route_impl<float, 16>(s, xp, b_router, ids, gates, logits, w64, st);
