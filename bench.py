@@ -36,7 +36,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_from_profiles(kernel_tag: str, config_key: str, n_units: float):
+def traffic_from_profiles(kernel_tag: str, config_key: str):
     """HBM bytes per launch of the dominant kernel from a committed counter summary, scaled by
     the copy-kernel calibration, or None if no summary matches the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{config_key}_counters.txt")
@@ -44,14 +44,16 @@ def traffic_from_profiles(kernel_tag: str, config_key: str, n_units: float):
         return None
     text = open(path).read()
     m = {k: re.search(rf"^{k}\s*=\s*(\S+)", text, re.M) for k in
-         ("source_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_scale")}
+         ("source_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch", "fetch_scale",
+          "write_scale")}
     if not all(m.values()):
         return None
     src = open(os.path.join(ROOT, "capacity_routing_expert_amd", "csrc", "gemm_bf16.hip"), "rb").read()
     if hashlib.sha256(src).hexdigest() != m["source_sha256"].group(1):
         return None  # the kernel changed since the counters were taken
-    kib = float(m["fetch_kib_per_dispatch"].group(1)) + float(m["write_kib_per_dispatch"].group(1))
-    return kib * 1024.0 * float(m["copy_scale"].group(1))
+    kib = (float(m["fetch_kib_per_dispatch"].group(1)) * float(m["fetch_scale"].group(1)) +
+           float(m["write_kib_per_dispatch"].group(1)) * float(m["write_scale"].group(1)))
+    return kib * 1024.0
 
 
 def cpu_baseline(inp, wl, cap):
@@ -161,7 +163,7 @@ def main():
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
     achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
-    traffic = traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2", args.config, 1.0)
+    traffic = traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2", args.config)
 
     route_bytes = wl.T * dm * inp["x"].itemsize + wl.n_experts * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
     combine_bytes = (2 * wl.T + n_kept) * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
