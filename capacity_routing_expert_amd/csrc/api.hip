@@ -120,6 +120,8 @@ Workspace layout(const moe_shape& s) {
   };
   const int64_t G = route_emax((int)E);
   w.w64 = take((size_t)((E + G - 1) / G) * G * s.d_model * 8);
+  const RoutePlan rp = route_plan(s);
+  w.route_part = take(rp.P > 1 ? (size_t)rp.G * rp.P * E * 64 * 8 : 0);
   w.ids = take((size_t)N * 4);
   w.gates = take((size_t)N * 4);
   w.slot_of = take((size_t)N * 4);
@@ -142,7 +144,8 @@ namespace {
 moe_status do_route(const moe_shape& s, const void* x, const void* w_router, const float* b_router,
                     int32_t* ids, float* gates, float* logits, void* ws, hipStream_t st) {
   const Workspace L = layout(s);
-  hipError_t err = launch_route(s, x, w_router, b_router, ids, gates, logits, at<double>(ws, L.w64), st);
+  hipError_t err = launch_route(s, x, w_router, b_router, ids, gates, logits, at<double>(ws, L.w64),
+                                at<double>(ws, L.route_part), st);
   return err == hipSuccess ? MOE_OK : device_error(err, "route");
 }
 
