@@ -16,16 +16,21 @@
 // MFMA blocks with fp32 accumulators in AGPRs.  The weights are the MFMA "A" operand, the
 // token rows the "B" operand.
 //
-// K pipeline: stages of 32 K; a ring of 4 stage buffers in LDS (32 KiB each for 256 x 256)
-// filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) issued 3 stages ahead, so
-// HBM / L2 latency is covered by three stages of MFMA work and the data never passes through
-// VGPRs.  Each wave waits for its own loads of the next stage (vmcnt), then one barrier per
-// stage publishes it; MFMA fragments are double-buffered in registers per 16-K step, so LDS
-// reads of the next step overlap the MFMAs of the current one.  Row r of a stage buffer is
-// 64 bytes (4 chunks of 16 B); chunk c is stored at c ^ ((r >> 2) & 3), which spreads the 16
-// rows read by 16 consecutive lanes over all 64 LDS banks.  Loads go through buffer resources
-// whose range covers only the tile's valid rows: out-of-range lanes (ragged rows, K tail)
-// write zeros into LDS, so no branch guards a load.
+// K pipeline: stages of BK = 32 K (64-byte rows) in a ring of NS = 4 stage buffers in LDS
+// (32 KiB each for 256 x 256), filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ...
+// lds), so the data never passes through VGPRs.  Stage kt+NS is issued right after the barrier
+// that ends the reads of stage kt, into the slot that barrier freed: each stage has three
+// stages of MFMA work to arrive.  Its loads are spread one by one between the MFMAs of the
+// following 16-K step, so a wave never waits on the load queue with an empty matrix pipe.  The
+// loop body is the same on every step (stages past the last are issued as all-out-of-range
+// loads that only write zeros), which keeps the vmcnt bookkeeping a constant.  MFMA fragments
+// are double-buffered in registers per 16-K step, so LDS reads of the next step overlap the
+// MFMAs of the current one.  Chunk c of row r of a stage buffer is stored at c ^ swz(r), which
+// spreads the 16 rows read by 16 consecutive lanes over all 64 LDS banks.  Loads go through
+// buffer resources whose range covers only the tile's valid rows: out-of-range lanes (ragged
+// rows, K tail) write zeros into LDS, so no branch guards a load.  The kernel is templated on
+// the tile, the stage depth (32 or 64) and the ring depth; 256 x 256 with 32-deep stages and a
+// 4-deep ring measured fastest on the layer shapes here.
 //
 // Epilogue: bias + activation + bf16 rounding per 16-accumulator group into an LDS tile, then
 // coalesced 16-byte stores of whole output rows.
@@ -79,30 +84,37 @@ __device__ __forceinline__ void lds_dma16(i32x4_t srd, uint32_t lds_base, uint32
       : "memory", "m0");
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-#define MOE_WAIT_VMCNT_16() __builtin_amdgcn_s_waitcnt(0x4F70)
-#define MOE_WAIT_VMCNT_8() __builtin_amdgcn_s_waitcnt(0x0F78)
-#define MOE_WAIT_VMCNT_0() __builtin_amdgcn_s_waitcnt(0x0F70)
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding and leaves
+// the other counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 }  // namespace
 
-template <int TN, int TM, bool GATHER, bool SILU>
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm(
+// TN x TM tile, NS-deep ring; MINB blocks share a compute unit (1: 256 x 256 tiles with 256
+// accumulators per wave; 2: a second block's main loop covers this one's barriers and epilogue).
+template <int TN, int TM, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER, bool SILU>
+__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, int E, int N, int K, int a_rows) {
   constexpr int WN = 2, WM = 2;              // waves along features / slots
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
-  constexpr int BK = 32;                     // K per stage
-  constexpr int NS = 4;                      // LDS ring depth (stages)
+  constexpr int KS = BK / 16;                // 16-K MFMA steps per stage
+  constexpr int kChunks = BK / 8;            // 16-byte chunks per row of a stage
   constexpr int FN = TN / WN / 32;           // 32x32 blocks per wave along features
   constexpr int FM = TM / WM / 32;           // ... along slots
-  constexpr int kRowsPerLoad = 16;           // one 1 KiB wave load = 16 rows x 64 B
+  constexpr int kRowsPerLoad = 64 / kChunks; // rows of one 1 KiB wave load
   constexpr int kWLoads = TN / kRowsPerLoad / kWaves;  // weight loads per wave per stage
   constexpr int kXLoads = TM / kRowsPerLoad / kWaves;  // token-row loads per wave per stage
+  constexpr int kLoads = kWLoads + kXLoads;
   constexpr int kStageBytes = (TN + TM) * BK * 2;
-  static_assert(kWLoads + kXLoads == 8, "the vmcnt waits below assume 8 loads per stage");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(FN >= 1 && FM >= 1 && kWLoads >= 1 && kXLoads >= 1, "tile too small");
+  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
+  // Physical chunk of logical chunk c in row r is c ^ swz(r): the 16 rows read by 16
+  // consecutive lanes then fall on distinct 16-byte bank groups (64 banks = 16 groups).
+  auto swz = [](int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; };
   extern __shared__ uint4 smem[];
 
   const int lane = threadIdx.x & 63;
@@ -156,43 +168,61 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
   const int n0 = nt * TN;
   const int wrows = min(TN, N - n0);
 
-  // ---- load plan.  Lane i of a 1 KiB wave load fills row i/4 (of its 16), physical chunk i%4,
-  // with logical chunk cch = (i%4) ^ ((row >> 2) & 3); (row >> 2) & 3 equals (i/16) & 3.
-  const int lrow = lane >> 2;
-  const int cch = (lane & 3) ^ ((lane >> 4) & 3);
+  // ---- load plan.  A 1 KiB wave load fills kRowsPerLoad rows of kChunks 16-byte chunks: lane i
+  // writes row i / kChunks, physical chunk p = i % kChunks, which holds logical chunk
+  // p ^ swz(row) of that row.  The swizzle depends on the row's place in the stage buffer, so
+  // the logical chunk of a lane can differ from one load of the stage to the next.
+  const int lrow = lane / kChunks;
+  const int pch = lane % kChunks;
   const i32x4_t wsrc = make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
   i32x4_t xsrc;
-  uint32_t xoff[kXLoads];
+  uint32_t xoff[kXLoads];  // byte offset of the lane's chunk in stage 0, or kOutOfRange
   if (GATHER) {
     xsrc = make_srd(A, (uint32_t)a_rows * (uint32_t)K * 2u);  // whole x (< 2 GiB, host-checked)
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
       const int row = (wave * kXLoads + j) * kRowsPerLoad + lrow;
-      xoff[j] = row < rows ? (uint32_t)(row_token[row0 + row] * K + cch * 8) * 2u : kOutOfRange;
+      const int c = pch ^ swz(row);
+      xoff[j] = row < rows && c * 8 < K ? (uint32_t)(row_token[row0 + row] * K + c * 8) * 2u
+                                        : kOutOfRange;
     }
   } else {
     xsrc = make_srd(A + (int64_t)row0 * K, (uint32_t)(rows * K * 2));
 #pragma unroll
-    for (int j = 0; j < kXLoads; ++j)
-      xoff[j] = (uint32_t)(((wave * kXLoads + j) * kRowsPerLoad + lrow) * K + cch * 8) * 2u;
+    for (int j = 0; j < kXLoads; ++j) {
+      const int row = (wave * kXLoads + j) * kRowsPerLoad + lrow;
+      const int c = pch ^ swz(row);
+      xoff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
+    }
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
   const int nk = (K + BK - 1) / BK;
 
+// Load q of stage S (q < kWLoads: weight rows, else token rows), with k0_, kb_ and sb_ from
+// MOE_STAGE_BASE.  A chunk at or past K (K tail, stages past the last) reads as zeros.
+#define MOE_STAGE_BASE(S)                                                                      \
+  const int k0_ = (S) * BK;                                                                    \
+  const uint32_t kb_ = (uint32_t)k0_ * 2u;                                                     \
+  const uint32_t sb_ = lds0 + (uint32_t)(((S) % NS) * kStageBytes)
+#define MOE_ISSUE_LOAD(q)                                                                      \
+  do {                                                                                         \
+    if ((q) < kWLoads) {                                                                       \
+      const int g_ = wave * kWLoads + (q);                                                     \
+      const int row_ = g_ * kRowsPerLoad + lrow;                                               \
+      const int c_ = pch ^ swz(row_);                                                          \
+      lds_dma16(wsrc, sb_ + (uint32_t)(g_ * 1024),                                             \
+                k0_ + c_ * 8 < K ? (uint32_t)((row_ * K + c_ * 8) * 2) + kb_ : kOutOfRange);   \
+    } else {                                                                                   \
+      const int j_ = (q) - kWLoads;                                                            \
+      const int c_ = pch ^ swz((wave * kXLoads + j_) * kRowsPerLoad + lrow);                   \
+      lds_dma16(xsrc, sb_ + (uint32_t)(TN * BK * 2 + (wave * kXLoads + j_) * 1024),            \
+                (k0_ + c_ * 8 < K && xoff[j_] != kOutOfRange) ? xoff[j_] + kb_ : kOutOfRange); \
+    }                                                                                          \
+  } while (0)
 #define MOE_ISSUE_STAGE(S)                                                                     \
   do {                                                                                         \
-    const int k0_ = (S) * BK;                                                                  \
-    const bool kin_ = k0_ + cch * 8 < K;                                                       \
-    const uint32_t kb_ = (uint32_t)k0_ * 2u;                                                   \
-    const uint32_t sb_ = lds0 + (uint32_t)(((S) % NS) * kStageBytes);                          \
-    _Pragma("unroll") for (int j_ = 0; j_ < kWLoads; ++j_) {                                   \
-      const int row_ = (wave * kWLoads + j_) * kRowsPerLoad + lrow;                            \
-      lds_dma16(wsrc, sb_ + (uint32_t)((wave * kWLoads + j_) * kRowsPerLoad * 64),             \
-                kin_ ? (uint32_t)((row_ * K + cch * 8) * 2) + kb_ : kOutOfRange);              \
-    }                                                                                          \
-    _Pragma("unroll") for (int j_ = 0; j_ < kXLoads; ++j_)                                     \
-      lds_dma16(xsrc, sb_ + (uint32_t)(TN * 64 + (wave * kXLoads + j_) * kRowsPerLoad * 64),   \
-                (kin_ && xoff[j_] != kOutOfRange) ? xoff[j_] + kb_ : kOutOfRange);             \
+    MOE_STAGE_BASE(S);                                                                         \
+    _Pragma("unroll") for (int q_ = 0; q_ < kLoads; ++q_) MOE_ISSUE_LOAD(q_);                  \
   } while (0)
 
 #define MOE_READ_FRAGS(S, KK, F)                                                               \
@@ -201,11 +231,11 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
     const int ch_ = (KK) * 2 + half;                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < FN; ++i_) {                                        \
       const int row_ = wn * (TN / WN) + i_ * 32 + r32;                                         \
-      fa[F][i_] = as_bf16x8(sb_[row_ * 4 + (ch_ ^ ((row_ >> 2) & 3))]);                        \
+      fa[F][i_] = as_bf16x8(sb_[row_ * kChunks + (ch_ ^ swz(row_))]);                          \
     }                                                                                          \
     _Pragma("unroll") for (int j_ = 0; j_ < FM; ++j_) {                                        \
       const int row_ = wm * (TM / WM) + j_ * 32 + r32;                                         \
-      fb[F][j_] = as_bf16x8(sb_[TN * 4 + row_ * 4 + (ch_ ^ ((row_ >> 2) & 3))]);               \
+      fb[F][j_] = as_bf16x8(sb_[TN * kChunks + row_ * kChunks + (ch_ ^ swz(row_))]);           \
     }                                                                                          \
   } while (0)
 
@@ -217,6 +247,22 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
                                                               acc[i_][j_], 0, 0, 0);           \
   } while (0)
 
+// MFMA step F with the loads of stage S spread between the MFMAs (load q after MFMA
+// floor(q * FN * FM / kLoads)), so that the wave never stalls on the load queue while its
+// matrix core has nothing queued.  The scheduling barriers keep this order.
+#define MOE_MFMA_STEP_ISSUE(F, S)                                                              \
+  do {                                                                                         \
+    MOE_STAGE_BASE(S);                                                                         \
+    _Pragma("unroll") for (int m_ = 0; m_ < FN * FM; ++m_) {                                   \
+      const int i_ = m_ / FM, j_ = m_ % FM;                                                    \
+      acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i_], fb[F][j_], acc[i_][j_], \
+                                                            0, 0, 0);                          \
+      _Pragma("unroll") for (int q_ = 0; q_ < kLoads; ++q_)                                    \
+        if (q_ * FN * FM / kLoads == m_) MOE_ISSUE_LOAD(q_);                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+    }                                                                                          \
+  } while (0)
+
   bf16x8_t fa[2][FN], fb[2][FM];
   f32x16_t acc[FN][FM];
 #pragma unroll
@@ -226,33 +272,49 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // prologue: stages 0 .. NS-2 in flight; first 16-K step of stage 0 in registers
-  MOE_ISSUE_STAGE(0);
-  if (nk > 1) MOE_ISSUE_STAGE(1);
-  if (nk > 2) MOE_ISSUE_STAGE(2);
-  if (nk >= 3) MOE_WAIT_VMCNT_16();
-  else if (nk == 2) MOE_WAIT_VMCNT_8();
-  else MOE_WAIT_VMCNT_0();
+  // Ring: stage S lives in slot S % NS.  Stages 0 .. NS-1 are issued up front; stage kt+NS is
+  // issued right after the barrier that ends the reads of stage kt, into the slot that barrier
+  // freed, so a stage has NS-1 stages of MFMA work to arrive.  Stages past the last one are
+  // issued too (every lane out of range: they write zeros into a slot no later stage reads),
+  // which keeps the vmcnt bookkeeping the same on every step.
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0) MOE_ISSUE_STAGE(s0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kLoads));
   __syncthreads();
   MOE_READ_FRAGS(0, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    // the slot of stage kt-1 is free: its last fragments were read before the last barrier
-    if (kt + NS - 1 < nk) MOE_ISSUE_STAGE(kt + NS - 1);
-    MOE_READ_FRAGS(kt, 1, 1);
-    MOE_MFMA_STEP(0);
-    // this wave's loads of stage kt+1 are done once at most the later stages' are pending
-    const int pend = min(nk - 1, kt + NS - 1) - (kt + 1);
-    if (pend >= 2) MOE_WAIT_VMCNT_16();
-    else if (pend == 1) MOE_WAIT_VMCNT_8();
-    else MOE_WAIT_VMCNT_0();
+    // 16-K steps 0 .. KS-2 of stage kt; fragments of the next step are read during each
+#pragma unroll
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      if (kk % 2 == 0) {
+        MOE_READ_FRAGS(kt, kk + 1, 1);
+        MOE_MFMA_STEP(0);
+      } else {
+        MOE_READ_FRAGS(kt, kk + 1, 0);
+        MOE_MFMA_STEP(1);
+      }
+    }
+    // this wave's loads of stage kt+1 are done once only the NS-2 later stages are pending;
+    // after the barrier every wave has read all of stage kt
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kLoads));
     __syncthreads();
-    if (kt + 1 < nk) MOE_READ_FRAGS(kt + 1, 0, 0);
-    MOE_MFMA_STEP(1);
+    MOE_READ_FRAGS(kt + 1, 0, 0);  // past the last stage this reads a slot nobody uses
+    if (INTERLEAVE) {
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_MFMA_STEP_ISSUE((KS - 1) % 2, kt + NS);
+    } else {
+      MOE_ISSUE_STAGE(kt + NS);
+      MOE_MFMA_STEP((KS - 1) % 2);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the zero-fill loads land before the LDS reuse
+#undef MOE_STAGE_BASE
+#undef MOE_ISSUE_LOAD
 #undef MOE_ISSUE_STAGE
 #undef MOE_READ_FRAGS
 #undef MOE_MFMA_STEP
+#undef MOE_MFMA_STEP_ISSUE
 
   // ---- epilogue.  Lane (r32, half) holds, for block (i, j), features
   // 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32.  Bias + activation + bf16 go
@@ -286,8 +348,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
           for (int u = 0; u < 4; ++u) v[u] = v[u] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u]));
         }
         uint2 o;
-        o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(stile + tl * kPitch + fl * 2) = o;
       }
     }
@@ -305,15 +367,16 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
 
 namespace {
 
-template <int TN, int TM, bool GATHER, bool SILU>
+template <int TN, int TM, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER, bool SILU>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st) {
   if (rows_ub <= 0) return hipSuccess;
-  constexpr size_t ring = (size_t)4 * (TN + TM) * 32 * 2;
+  constexpr size_t ring = (size_t)NS * (TN + TM) * BK * 2;
   constexpr size_t tile = (size_t)TM * (TN * 2 + 16);
   constexpr size_t lds = ring > tile ? ring : tile;
-  auto kern = k_grouped_gemm<TN, TM, GATHER, SILU>;
+  static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
+  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, INTERLEAVE, GATHER, SILU>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -340,11 +403,21 @@ hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* r
 hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t* offsets,
                                const void* w2, const void* b2, void* y, hipStream_t st);
 
+// Few rows per expert (decode-sized batches): the layer is bound by streaming the expert
+// weights, and 256 x 256 tiles would leave most compute units idle (8 experts x d_model / 256
+// tiles for the down-projection).  64 x 64 tiles with 64-deep stages and two blocks per compute
+// unit put every unit to work on its own weight rows with 48 KiB of loads in flight.
+static bool skinny(const moe_shape& s) { return max_rows(s) <= (int64_t)64 * s.n_experts; }
+
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const void* w1, const void* b1, void* h,
                          hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, st);
-  return launch_grouped_gemm<256, 256, true, true>(
+  if (skinny(s))
+    return launch_grouped_gemm<64, 64, 64, 4, 2, true, true, true>(
+        (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
+        s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
+  return launch_grouped_gemm<256, 256, 32, 4, 1, true, true, true>(
       (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
       s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
 }
@@ -352,7 +425,11 @@ hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_t
 hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
                            const void* w2, const void* b2, void* y, hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, st);
-  return launch_grouped_gemm<256, 256, false, false>(
+  if (skinny(s))
+    return launch_grouped_gemm<64, 64, 64, 4, 2, true, false, false>(
+        (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
+        s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
+  return launch_grouped_gemm<256, 256, 32, 4, 1, true, false, false>(
       (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
       s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
 }

@@ -20,6 +20,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (bf16_t)(u >> 16);
 }
+// two floats to a packed bf16 pair (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2_t));
+}
 __device__ __forceinline__ float load_as_f32(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
 
