@@ -118,10 +118,6 @@ Workspace layout(const moe_shape& s) {
     o = align256(o + bytes);
     return at_;
   };
-  const int64_t G = route_emax((int)E);
-  w.w64 = take((size_t)((E + G - 1) / G) * G * s.d_model * 8);
-  const RoutePlan rp = route_plan(s);
-  w.route_part = take(rp.P > 1 ? (size_t)rp.G * rp.P * E * 64 * 8 : 0);
   w.ids = take((size_t)N * 4);
   w.gates = take((size_t)N * 4);
   w.slot_of = take((size_t)N * 4);
@@ -142,10 +138,8 @@ Workspace layout(const moe_shape& s) {
 namespace {
 
 moe_status do_route(const moe_shape& s, const void* x, const void* w_router, const float* b_router,
-                    int32_t* ids, float* gates, float* logits, void* ws, hipStream_t st) {
-  const Workspace L = layout(s);
-  hipError_t err = launch_route(s, x, w_router, b_router, ids, gates, logits, at<double>(ws, L.w64),
-                                at<double>(ws, L.route_part), st);
+                    int32_t* ids, float* gates, float* logits, hipStream_t st) {
+  hipError_t err = launch_route(s, x, w_router, b_router, ids, gates, logits, st);
   return err == hipSuccess ? MOE_OK : device_error(err, "route");
 }
 
@@ -211,7 +205,7 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   void* y = at<void>(ws, L.y);
 
   MOE_TRY(rec(0));
-  MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, ws, st));
+  MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, st));
   MOE_TRY(rec(1));
   MOE_TRY(do_dispatch(s, ids, gates, counts, offsets, slots, row_token, drop, ws, st));
   MOE_TRY(rec(2));
@@ -289,7 +283,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
   MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
   if (logits) MOE_TRY(check_ptr(logits, 4, "logits"));
   MOE_TRY(check_ws(s, ws, ws_bytes));
-  return do_route(s, x, w_router, b_router, topk_ids, topk_gates, logits, ws, (hipStream_t)stream);
+  return do_route(s, x, w_router, b_router, topk_ids, topk_gates, logits, (hipStream_t)stream);
 }
 
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const float* topk_gates,

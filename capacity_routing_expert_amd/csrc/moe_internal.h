@@ -34,8 +34,6 @@ __device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
 // ---------------------------------------------------------------- workspace layout
 // One workspace buffer serves every call; each sub-buffer starts on a 256-byte boundary.
 struct Workspace {
-  size_t w64;        // router weights widened to fp64    [ceil(E/G) * G, d], G = route_emax(E)
-  size_t route_part; // router partial logits                    [G * P, E, 64] f64
   size_t ids;        // top-k expert ids (layer_forward)          [T*k] int32
   size_t gates;      // top-k gates                               [T*k] f32
   size_t slot_of;    // slot per assignment                       [T*k] int32
@@ -55,20 +53,12 @@ struct Workspace {
 constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
 
 int64_t max_rows(const moe_shape& s);
-int route_emax(int E);  // experts per register group of the router kernel
-// router launch shape: S waves per block, G token groups of 64, P column partitions per group
-struct RoutePlan {
-  int S;
-  int64_t G;
-  int P;
-};
-RoutePlan route_plan(const moe_shape& s);
 Workspace layout(const moe_shape& s);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
 hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
                         const float* b_router, int32_t* ids, float* gates, float* logits,
-                        double* w64, double* part, hipStream_t st);
+                        hipStream_t st);
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,

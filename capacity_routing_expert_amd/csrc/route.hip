@@ -12,75 +12,31 @@
 // the summation order except in the rare case where a probability lies within fp64
 // rounding noise of an fp32 rounding boundary.
 //
-// Mapping (gfx950): the logit GEMM is [T, d] x [d, E] with E <= 256, far too skinny for the
-// matrix cores and bound by streaming x from HBM (or by the fp64 ALUs when E is large).
-// Each lane owns one token; the P blocks of a token group and the S waves of a block split
-// the columns, and each lane keeps up to 16 chunk loads of its row in flight.  The router
-// weights, widened once to fp64, are read with wave-uniform addresses, so they arrive through
-// the scalar cache into SGPRs and every lane does one fp64 FMA per (column, expert) with no
-// cross-lane traffic; partial sums are added in a fixed order, so the logits do not depend on
-// which block finishes first.
+// Mapping (gfx950): the logit GEMM [T, d] x [d, E] (E <= 256) is far too skinny and too
+// precise for the bf16 matrix cores, but it fits the fp64 ones: one kernel reads x and the
+// router weights once, multiplies them on v_mfma_f64_16x16x4f64 and finishes each block's
+// tokens (bias, softmax, top-k) without a second launch or partial sums in memory.
 #include "moe_internal.h"
 
 namespace moe {
 
-// Router weights widened to fp64 and laid out [group][d][EMAX] (experts g*EMAX .. g*EMAX +
-// EMAX-1 of one column contiguous, zero-padded past E), so a column's weights are one aligned
-// run of EMAX doubles: wide unconditional scalar loads.
-template <typename TIn>
-__global__ void k_router_weights_f64(const TIn* __restrict__ w, double* __restrict__ w64,
-                                     int d, int E, int EMAX) {
-  const int G = (E + EMAX - 1) / EMAX;
-  const int64_t n = (int64_t)G * d * EMAX;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t i = tid; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t g = i / ((int64_t)d * EMAX), rem = i % ((int64_t)d * EMAX);
-    const int64_t j = rem / EMAX, e = g * EMAX + rem % EMAX;
-    w64[i] = e < E ? (double)load_as_f32(w + e * d + j) : 0.0;
+namespace {
+
+// 8 bf16 (one 16-byte word) widened exactly to fp64
+__device__ __forceinline__ void widen_bf16x8(uint4 q, double* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = (double)__uint_as_float(w[i] << 16);
+    v[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
 
-template <typename TIn>
-struct VecLoad;
-template <>
-struct VecLoad<bf16_t> {
-  static constexpr int VW = 8;  // columns per 16-byte chunk
-  __device__ __forceinline__ static uint4 raw(const bf16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-  __device__ __forceinline__ static void widen(uint4 q, double* v) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = (double)__uint_as_float(w[i] << 16);
-      v[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-};
-template <>
-struct VecLoad<float> {
-  static constexpr int VW = 4;
-  __device__ __forceinline__ static uint4 raw(const float* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-  __device__ __forceinline__ static void widen(uint4 q, double* v) {
-    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
-    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
-  }
-};
-
-template <int EMAX>
-struct RouteBounds {
-  // waves per block the partial-sum LDS allows (128 KiB / (EMAX * 64 lanes * 8 bytes)), <= 4
-  static constexpr int kMaxS = (128 * 1024) / (EMAX * 64 * 8) < 4 ? (128 * 1024) / (EMAX * 64 * 8) : 4;
-  static constexpr int kThreads = 64 * kMaxS;
-};
-
-constexpr int kRoutePF = 8;  // x chunks (one 128-byte line) a lane has in flight at once
+}  // namespace
 
 // Bias, optional fp32 logits, softmax over all experts in fp64 (rounded once to fp32) and
-// top-k for the 64 tokens whose complete logits sit in lds[e * 64 + i]; every thread of the
-// block calls it (S lanes per token).
+// top-k for the TB tokens whose complete logits sit in lds[e * TB + i]; every thread of the
+// block calls it, S = nthr / TB lanes per token (a power of two, inside one wave).
 template <int TB>
 __device__ void finish_group(double* lds, const float* __restrict__ b_router, int64_t tok0,
                              int64_t T, int E, int k, int S, int nthr, int32_t* __restrict__ ids,
@@ -137,211 +93,185 @@ __device__ void finish_group(double* lds, const float* __restrict__ b_router, in
   }
 }
 
-// Block (g, p): 64 tokens (one per lane) of token group g, column partition p of P, split
-// over the S waves of the block (wave s takes the s-th contiguous run of chunks).  The S
-// wave partials meet in LDS in a fixed order.  With P > 1 the block writes its partial logits
-// to `part`, and the last block of the group to arrive (an integer arrival counter) adds the
-// P partials in partition order and finishes the token group; the result does not depend on
-// which block arrives last.
-template <typename TIn, int EMAX>
-__global__ __launch_bounds__(RouteBounds<EMAX>::kThreads) void k_route(
-    const TIn* __restrict__ x, const double* __restrict__ w64, const float* __restrict__ b_router,
-    int64_t T, int d, int E, int k, int S, int P, double* __restrict__ part,
-    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ logits_out) {
-  extern __shared__ double lds[];  // partials [S][EMAX][64]; then logits/gates [E][64]
-  constexpr int VW = VecLoad<TIn>::VW;
-  constexpr int TB = 64;
-  const int lane = threadIdx.x & 63;
-  // wave-uniform by construction; readfirstlane tells the compiler, so addresses built from
-  // it (the router weights) are scalar
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = blockIdx.x / P, p = blockIdx.x % P;
-  const int64_t tok0 = (int64_t)grp * TB;
-  const int64_t t = tok0 + lane;
-  const bool tok_ok = t < T;
-  const int n_groups = (E + EMAX - 1) / EMAX;  // > 1 only when S == 1 and P == 1 (host)
-  const TIn* xrow = x + (tok_ok ? t : 0) * (int64_t)d;
-  const bool vec = d % VW == 0;
-  const int ncol = vec ? d / VW : d;  // chunks (vector path) or columns
-  const int cb = (int)((int64_t)ncol * p / P), ce = (int)((int64_t)ncol * (p + 1) / P);
+// ---------------------------------------------------------------- matrix-core router
+// The logit GEMM [T, d] x [d, E] on the fp64 matrix cores: v_mfma_f64_16x16x4f64 multiplies a
+// 16 x 4 tile of tokens by a 4 x 16 tile of experts, fp64 products of the widened inputs
+// (exact) accumulated in fp64.  Both operands come from VGPRs, loaded straight from x and the
+// router weights in the operand layout (lane l: token / expert l % 16, 8 consecutive columns of
+// chunk 4 cq + l / 16), so every loaded value feeds 16 products and no weight table is needed.
+// MFMA step s of chunk quad cq pairs column 8 (4 cq + l / 16) + s of both operands: a
+// permutation of the summation order only.  A block of NW waves takes TT = 16 R tokens; wave w
+// takes chunk quads w, w + NW, ...; wave 0 adds the other waves' partial tiles in wave order,
+// so the logits are reproducible, then the block finishes its tokens (bias, softmax, top-k).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-  for (int g = 0; g < n_groups; ++g) {
-    const int e0 = g * EMAX;
-    const int eg = min(EMAX, E - e0);
-    const double* wg = w64 + (int64_t)g * d * EMAX;  // this group's [d][EMAX] weights
-    double acc[EMAX];
+template <typename TIn>
+struct Chunk8;
+template <>
+struct Chunk8<bf16_t> {  // 8 bf16 columns as one 16-byte load (d % 8 == 0 for bf16)
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ m, bool ok, int64_t row, int c,
+                                       int d) {
+    v = ok && c * 8 < d ? *reinterpret_cast<const uint4*>(m + row * d + (int64_t)c * 8)
+                        : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void widen(double* o) const { widen_bf16x8(v, o); }
+};
+template <>
+struct Chunk8<float> {  // 8 fp32 columns, each guarded (any d)
+  float v[8];
+  __device__ __forceinline__ void load(const float* __restrict__ m, bool ok, int64_t row, int c,
+                                       int d) {
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) acc[e] = 0.0;
-
-    if (vec) {
-      // this wave's chunks: a contiguous run of the partition, so each lane reads whole
-      // 128-byte lines of its row; kRoutePF chunk loads in flight at a time
-      const int per = (ce - cb + S - 1) / S;
-      const int wb = cb + wave * per, we = min(ce, wb + per);
-      for (int c0 = wb; c0 < we; c0 += kRoutePF) {
-        uint4 q[kRoutePF];
-#pragma unroll
-        for (int u = 0; u < kRoutePF; ++u) {
-          const int c = c0 + u;
-          q[u] = (tok_ok && c < we) ? VecLoad<TIn>::raw(xrow + (int64_t)c * VW) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kRoutePF; ++u) {
-          const int c = c0 + u;
-          if (c >= we) break;  // wave-uniform
-          double xv[VW];
-          VecLoad<TIn>::widen(q[u], xv);
-#pragma unroll
-          for (int v = 0; v < VW; ++v) {
-            const double* wc = wg + ((int64_t)c * VW + v) * EMAX;
-#pragma unroll
-            for (int e = 0; e < EMAX; ++e) acc[e] = fma(xv[v], wc[e], acc[e]);
-          }
-        }
-      }
-    } else {
-      // generic column loop for widths that are not a multiple of the vector size
-      for (int j = cb + wave; j < ce; j += S) {
-        const double xv = tok_ok ? (double)load_as_f32(xrow + j) : 0.0;
-#pragma unroll
-        for (int e = 0; e < EMAX; ++e) acc[e] = fma(xv, wg[(int64_t)j * EMAX + e], acc[e]);
-      }
-    }
-
-    if (S == 1) {
-#pragma unroll
-      for (int e = 0; e < EMAX; ++e)
-        if (e < eg) lds[(e0 + e) * TB + lane] = acc[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < EMAX; ++e) lds[(wave * EMAX + e) * TB + lane] = acc[e];
+    for (int u = 0; u < 8; ++u) {
+      const int col = c * 8 + u;
+      v[u] = ok && col < d ? m[row * d + col] : 0.0f;
     }
   }
-  __syncthreads();
+  __device__ __forceinline__ void widen(double* o) const {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = v[u];
+  }
+};
 
-  // sum the S wave partials in order; the result lands where partial 0 was (the thread
-  // that writes lds[e][i] is the only one reading partial 0 of (e, i))
-  const int nthr = 64 * S;
-  if (S > 1) {
-    for (int q = threadIdx.x; q < E * TB; q += nthr) {
-      const int e = q / TB, i = q % TB;
-      double sum = 0.0;
-      for (int w = 0; w < S; ++w) sum += lds[(w * EMAX + e) * TB + i];
-      lds[e * TB + i] = sum;
+template <typename TIn, int R, int EBG, int NW>
+__global__ __launch_bounds__(64 * NW) void k_route_mfma(
+    const TIn* __restrict__ x, const TIn* __restrict__ w, const float* __restrict__ b_router,
+    int64_t T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
+    float* __restrict__ logits_out) {
+  constexpr int TT = 16 * R, NT = 64 * NW;
+  constexpr int kPart = R * EBG * 256;  // doubles in one wave's partial tiles
+  extern __shared__ double lds[];       // [NW - 1][kPart] partials, then logits [E][TT]
+  double* logit = lds + (NW - 1) * kPart;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t tok0 = (int64_t)blockIdx.x * TT;
+  const int d8 = (d + 7) / 8, nq = (d8 + 3) / 4;
+  const int EB = (E + 15) / 16;
+
+  for (int b0 = 0; b0 < EB; b0 += EBG) {
+    f64x4_t acc[R][EBG];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int bb = 0; bb < EBG; ++bb) acc[r][bb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+
+    // wave w takes chunk quads w, w + NW, ...; the raw loads of the next quad are issued
+    // before the MFMAs of the current one (quads past the end load zeros)
+    Chunk8<TIn> xr[R], wr[EBG];
+    auto load = [&](int cq) {
+      const int c = cq * 4 + q;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t t = tok0 + 16 * r + i;
+        xr[r].load(x, cq < nq && t < T, t, c, d);
+      }
+#pragma unroll
+      for (int bb = 0; bb < EBG; ++bb) {
+        const int e = (b0 + bb) * 16 + i;
+        wr[bb].load(w, cq < nq && e < E, e, c, d);
+      }
+    };
+    load(wave);
+    for (int cq = wave; cq < nq; cq += NW) {
+      double xa[R][8], wb[EBG][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) xr[r].widen(xa[r]);
+#pragma unroll
+      for (int bb = 0; bb < EBG; ++bb) wr[bb].widen(wb[bb]);
+      load(cq + NW);
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int bb = 0; bb < EBG; ++bb)
+            acc[r][bb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[r][s8], wb[bb][s8], acc[r][bb],
+                                                              0, 0, 0);
+    }
+
+    // lane l, register j of a tile holds token 4 j + l / 16, expert l % 16 of the tile
+    if (wave > 0) {
+      double* mine = lds + (wave - 1) * kPart;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int bb = 0; bb < EBG; ++bb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mine[((r * EBG + bb) * 64 + lane) * 4 + j] = acc[r][bb][j];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int ww = 1; ww < NW; ++ww) {
+        const double* other = lds + (ww - 1) * kPart;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int bb = 0; bb < EBG; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[r][bb][j] += other[((r * EBG + bb) * 64 + lane) * 4 + j];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int bb = 0; bb < EBG; ++bb) {
+          const int e = (b0 + bb) * 16 + i;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (e < E) logit[e * TT + 16 * r + 4 * j + q] = acc[r][bb][j];
+        }
     }
     __syncthreads();
   }
-
-  if (P > 1) {
-    // column partition p of the group: its partial logits go to `part`; k_route_finish adds
-    // the P partials in partition order after this launch
-    double* mine = part + ((int64_t)grp * P + p) * E * TB;
-    for (int q = threadIdx.x; q < E * TB; q += nthr) mine[q] = lds[q];
-    return;
-  }
-  finish_group<TB>(lds, b_router, tok0, T, E, k, S, nthr, ids, gates, logits_out);
+  finish_group<TT>(logit, b_router, tok0, T, E, k, NT / TT, NT, ids, gates, logits_out);
 }
 
-// Token group g of 64: add the P partition partials in order, then bias, softmax, top-k.
-template <int EMAXU>
-__global__ __launch_bounds__(256) void k_route_finish(const double* __restrict__ part,
-                                                      const float* __restrict__ b_router,
-                                                      int64_t T, int E, int k, int P,
-                                                      int32_t* __restrict__ ids,
-                                                      float* __restrict__ gates,
-                                                      float* __restrict__ logits_out) {
-  extern __shared__ double lds[];  // [E][64]
-  constexpr int TB = 64;
-  const int64_t grp = blockIdx.x;
-  const int S = blockDim.x / 64;
-  for (int q = threadIdx.x; q < E * TB; q += blockDim.x) {
-    // partials are loaded 8 at a time (independent loads) and added in partition order
-    double sum = 0.0;
-    for (int p0 = 0; p0 < P; p0 += 8) {
-      double v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = p0 + u < P ? part[(grp * P + p0 + u) * E * TB + q] : 0.0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (p0 + u < P) sum += v[u];
-    }
-    lds[q] = sum;
-  }
-  __syncthreads();
-  finish_group<TB>(lds, b_router, grp * TB, T, E, k, S, (int)blockDim.x, ids, gates, logits_out);
-}
-int route_emax(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
-
-RoutePlan route_plan(const moe_shape& s) {
-  RoutePlan r;
-  const int E = s.n_experts, emax = route_emax(E);
-  const int vw = s.dtype == MOE_BF16 ? 8 : 4;
-  const int ncol = (s.d_model % vw == 0) ? s.d_model / vw : s.d_model;
-  const int max_s = (128 * 1024) / (emax * 64 * 8) < 4 ? (128 * 1024) / (emax * 64 * 8) : 4;
-  r.S = 1;
-  if (E <= emax)
-    while (2 * r.S <= max_s && 2 * r.S <= ncol) r.S *= 2;
-  r.G = (s.T + 63) / 64;
-  // enough waves to keep every SIMD streaming x (small E) or busy with fp64 FMAs (large E);
-  // at least one column chunk per wave
-  const int64_t target = E <= 16 ? 4096 : 1024;
-  r.P = 1;
-  if (E <= emax)
-    while (r.P < 64 && r.G * r.P * r.S < target && (int64_t)2 * r.P * r.S <= ncol) r.P *= 2;
-  return r;
-}
+// dynamic LDS of the largest router block: 7 wave partials of 4 expert tiles + [256][16] logits
+constexpr size_t route_lds_max() { return (size_t)8 * (7 * 4 * 256 + 256 * 16); }
 
 namespace {
 
-template <typename TIn, int EMAX>
-hipError_t route_impl(const moe_shape& s, const TIn* x, const float* b_router, int32_t* ids,
-                      float* gates, float* logits, const double* w64, double* part,
-                      hipStream_t st) {
-  const RoutePlan r = route_plan(s);
-  const size_t lds = (size_t)8 * 64 * (r.S > 1 ? (size_t)r.S * EMAX : (size_t)s.n_experts);
-  static bool attr_set = false;  // allow up to 128 KiB of dynamic LDS, once per instantiation
+template <typename TIn, int EBG>
+hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
+                        int32_t* ids, float* gates, float* logits, hipStream_t st) {
+  constexpr int R = 1, NW = 8, TT = 16 * R;
+  const size_t lds = (size_t)8 * ((NW - 1) * R * EBG * 256 + (size_t)s.n_experts * TT);
+  auto kern = k_route_mfma<TIn, R, EBG, NW>;
+  static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)k_route<TIn, EMAX>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_max());
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_route<TIn, EMAX>), dim3((unsigned)(r.G * r.P)), dim3(64 * r.S), lds, st,
-                     x, w64, b_router, s.T, s.d_model, s.n_experts, s.top_k, r.S, r.P, part, ids,
-                     gates, logits);
-  if (r.P > 1) {
-    const size_t lds2 = (size_t)8 * 64 * s.n_experts;
-    hipLaunchKernelGGL((k_route_finish<EMAX>), dim3((unsigned)r.G), dim3(256), lds2, st, part,
-                       b_router, s.T, s.n_experts, s.top_k, r.P, ids, gates, logits);
-  }
+  const int64_t blocks = (s.T + TT - 1) / TT;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, x, w, b_router, s.T,
+                     s.d_model, s.n_experts, s.top_k, ids, gates, logits);
   return hipGetLastError();
+}
+
+// Tile plan: 16 tokens per block of 8 waves (two waves per SIMD); up to 4 blocks of 16 experts
+// per pass over x, more experts take more passes.
+template <typename TIn>
+hipError_t route_any(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
+                     int32_t* ids, float* gates, float* logits, hipStream_t st) {
+  const int EB = (s.n_experts + 15) / 16;
+  if (EB == 1) return route_launch<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
+  if (EB == 2) return route_launch<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);
+  return route_launch<TIn, 4>(s, x, w, b_router, ids, gates, logits, st);
 }
 
 }  // namespace
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
                         const float* b_router, int32_t* ids, float* gates, float* logits,
-                        double* w64, double* part, hipStream_t st) {
-  const int E = s.n_experts, d = s.d_model, emax = route_emax(E);
-  const int64_t nw = (int64_t)(E + emax - 1) / emax * emax * d;
-  const int cblocks = (int)((nw + 255) / 256 < 1024 ? (nw + 255) / 256 : 1024);
-  if (s.dtype == MOE_BF16) {
-    hipLaunchKernelGGL(k_router_weights_f64<bf16_t>, dim3(cblocks), dim3(256), 0, st,
-                       (const bf16_t*)w_router, w64, d, E, emax);
-    const bf16_t* xp = (const bf16_t*)x;
-    if (E <= 8) return route_impl<bf16_t, 8>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    if (E <= 16) return route_impl<bf16_t, 16>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    if (E <= 32) return route_impl<bf16_t, 32>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    return route_impl<bf16_t, 64>(s, xp, b_router, ids, gates, logits, w64, part, st);
-  } else {
-    hipLaunchKernelGGL(k_router_weights_f64<float>, dim3(cblocks), dim3(256), 0, st,
-                       (const float*)w_router, w64, d, E, emax);
-    const float* xp = (const float*)x;
-    if (E <= 8) return route_impl<float, 8>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    if (E <= 16) return route_impl<float, 16>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    if (E <= 32) return route_impl<float, 32>(s, xp, b_router, ids, gates, logits, w64, part, st);
-    return route_impl<float, 64>(s, xp, b_router, ids, gates, logits, w64, part, st);
-  }
+                        hipStream_t st) {
+  if (s.dtype == MOE_BF16)
+    return route_any<bf16_t>(s, (const bf16_t*)x, (const bf16_t*)w_router, b_router, ids, gates,
+                             logits, st);
+  return route_any<float>(s, (const float*)x, (const float*)w_router, b_router, ids, gates,
+                          logits, st);
 }
 
 }  // namespace moe
