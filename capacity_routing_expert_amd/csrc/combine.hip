@@ -6,56 +6,133 @@
 // no kept choice is copied bit for bit ("Some Tokens Do Not Get In", "Past the edge": it
 // reaches the next layer exactly as it entered), so x + 0 never turns -0.0 into +0.0.
 //
-// HBM-bound stream: one wave per token row, 16-byte loads and stores; the slot numbers and
-// gates of the row are wave-uniform (scalar loads).
+// HBM-bound stream: one wave per token row, 16-byte loads and streaming (nontemporal) stores;
+// the slot numbers and gates of the row are wave-uniform (scalar loads).
 #include "moe_internal.h"
 
 namespace moe {
 
+namespace {
+
+__device__ __forceinline__ void widen8(uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void fma8(float g, uint4 v, float* acc) {
+  float y[8];
+  widen8(v, y);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, y[i], acc[i]);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at `base` (wave-uniform); loads past the range read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int ch) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, ch * 16, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 16-byte streaming store (the output row is not read again by this layer)
+__device__ __forceinline__ void store_nt(uint4 v, uint4* p) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
+}  // namespace
+
+// One wave per token row; each lane takes 16-byte chunks lane, lane + 64, ... in batches of
+// kB.  The x chunks of a batch and the y chunks of the first two kept choices are loaded
+// together, so a row costs one memory round trip per batch (plus one per further kept choice).
 __global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__ x,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_of,
                                                       const bf16_t* __restrict__ y,
                                                       bf16_t* __restrict__ out, int64_t T, int d,
                                                       int k) {
+  constexpr int kB = 4;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the row is wave-uniform; readfirstlane lets the compiler keep it, the slots, the gates and
+  // the buffer resources in scalar registers
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
   const int nch = d / 8;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + t * (int64_t)d);
   uint4* orow = reinterpret_cast<uint4*>(out + t * (int64_t)d);
-  bool any = false;
-  for (int c = 0; c < k; ++c) any |= slot_of[t * k + c] >= 0;
-  if (!any) {
-    for (int ch = lane; ch < nch; ch += 64) orow[ch] = xr[ch];
-    return;
-  }
-  for (int ch = lane; ch < nch; ch += 64) {
-    const uint4 xv = xr[ch];
-    float acc[8];
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = __uint_as_float(xw[i] << 16);
-      acc[2 * i + 1] = __uint_as_float(xw[i] & 0xFFFF0000u);
+  // the first two kept choices (choice order) and the number kept; all wave-uniform
+  int n_kept = 0, s0 = 0, s1 = 0;
+  float g0 = 0.0f, g1 = 0.0f;
+  for (int c = 0; c < k; ++c) {
+    const int sc = slot_of[t * k + c];
+    if (sc < 0) continue;
+    if (n_kept == 0) {
+      s0 = sc;
+      g0 = gates[t * k + c];
+    } else if (n_kept == 1) {
+      s1 = sc;
+      g1 = gates[t * k + c];
     }
-    for (int c = 0; c < k; ++c) {
-      const int s = slot_of[t * k + c];
-      if (s < 0) continue;
-      const float g = gates[t * k + c];
-      const uint4 yv = reinterpret_cast<const uint4*>(y + (int64_t)s * d)[ch];
-      const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+    ++n_kept;
+  }
+  // rows as buffer ranges: chunks past the row, and the rows of absent choices, read as zeros
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const __amdgpu_buffer_rsrc_t xb = row_rsrc(x + t * (int64_t)d, row_bytes);
+  const __amdgpu_buffer_rsrc_t y0 = row_rsrc(y + (int64_t)s0 * d, n_kept >= 1 ? row_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t y1 = row_rsrc(y + (int64_t)s1 * d, n_kept >= 2 ? row_bytes : 0u);
+
+  for (int base = lane; base < nch; base += 64 * kB) {
+    uint4 xv[kB], v0[kB], v1[kB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(g, __uint_as_float(yw[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(g, __uint_as_float(yw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    for (int b = 0; b < kB; ++b) {
+      xv[b] = load16(xb, base + 64 * b);
+      v0[b] = load16(y0, base + 64 * b);
+      v1[b] = load16(y1, base + 64 * b);
+    }
+    if (n_kept == 0) {  // every choice dropped: the row leaves bit for bit
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (base + 64 * b < nch) store_nt(xv[b], orow + base + 64 * b);
+      continue;
+    }
+    float acc[kB][8];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      widen8(xv[b], acc[b]);
+      fma8(g0, v0[b], acc[b]);
+      if (n_kept >= 2) fma8(g1, v1[b], acc[b]);
+    }
+    if (n_kept > 2) {  // further kept choices, in choice order
+      int seen = 0;
+      for (int c = 0; c < k; ++c) {
+        const int sc = slot_of[t * k + c];
+        if (sc < 0 || ++seen <= 2) continue;
+        const float g = gates[t * k + c];
+        const __amdgpu_buffer_rsrc_t yc = row_rsrc(y + (int64_t)sc * d, row_bytes);
+        uint4 vc[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) vc[b] = load16(yc, base + 64 * b);
+#pragma unroll
+        for (int b = 0; b < kB; ++b) fma8(g, vc[b], acc[b]);
       }
     }
-    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
-    orow[ch] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int b = 0; b < kB; ++b) {
+      if (base + 64 * b >= nch) continue;
+      uint4 o;
+      o.x = pack_bf16x2(acc[b][0], acc[b][1]);
+      o.y = pack_bf16x2(acc[b][2], acc[b][3]);
+      o.z = pack_bf16x2(acc[b][4], acc[b][5]);
+      o.w = pack_bf16x2(acc[b][6], acc[b][7]);
+      store_nt(o, orow + base + 64 * b);
+    }
   }
 }
 
