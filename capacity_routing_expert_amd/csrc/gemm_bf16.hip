@@ -90,13 +90,71 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 }  // namespace
 
-// TN x TM tile, NS-deep ring; MINB blocks share a compute unit (1: 256 x 256 tiles with 256
-// accumulators per wave; 2: a second block's main loop covers this one's barriers and epilogue).
-template <int TN, int TM, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER, bool SILU>
-__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
+// Token tiles of height TM per expert, from expert_offsets (lane L owns experts 4L .. 4L+3):
+// te[j] tiles of expert 4L+j, their exclusive prefix `excl` and inclusive `inc` over lanes,
+// and the total MT (wave-uniform).
+template <int TM>
+struct TokenTiles {
+  int te[4], excl, inc, MT;
+  __device__ __forceinline__ TokenTiles(const int32_t* __restrict__ offsets, int E, int lane) {
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ee = lane * 4 + j;
+      const int kept = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+      te[j] = (kept + TM - 1) / TM;
+      local += te[j];
+    }
+    inc = local;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += o;
+    }
+    excl = inc - local;
+    MT = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
+  }
+  // expert and first row of token tile mt (wave-uniform)
+  __device__ __forceinline__ void locate(const int32_t* __restrict__ offsets, int lane, int mt,
+                                         int& e, int& row0, int& rows) const {
+    const uint64_t bal = __ballot(mt >= excl && mt < inc);
+    const int owner = __ffsll((long long)bal) - 1;
+    int esel = 0, tstart = 0, run = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (esel == 0 && mt >= run && mt < run + te[j]) {
+        esel = lane * 4 + j + 1;
+        tstart = run;
+      }
+      run += te[j];
+    }
+    e = __builtin_amdgcn_readfirstlane(__shfl(esel, owner, 64) - 1);
+    tstart = __builtin_amdgcn_readfirstlane(__shfl(tstart, owner, 64));
+    row0 = offsets[e] + (mt - tstart) * TM;
+    rows = min(TM, offsets[e + 1] - row0);
+  }
+};
+
+// Block -> (token tile, weight tile) of a grid of MT x NT tiles: block b runs on XCD b % 8, and
+// the 32 blocks (b / 8) % 32 of round b / 256 on one XCD take one group of kGroupM token tiles x
+// kGroupN weight tiles.  False if the block has no tile.
+__device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) {
+  const int NQ = (NT + kGroupN - 1) / kGroupN;
+  const int NG = ((MT + kGroupM - 1) / kGroupM) * NQ;
+  const int xcd = blockIdx.x & 7, slot = (blockIdx.x >> 3) & 31, round = blockIdx.x >> 8;
+  const int g = round * 8 + xcd;
+  if (g >= NG) return false;
+  mt = (g / NQ) * kGroupM + slot % kGroupM;
+  nt = (g % NQ) * kGroupN + slot / kGroupM;
+  return mt < MT && nt < NT;
+}
+
+// One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
+// n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
+template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, bool SILU>
+__device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
-    const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, int E, int N, int K, int a_rows) {
+    const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
+    int N, int K, int a_rows, int e, int row0, int rows, int n0) {
   constexpr int WN = 2, WM = 2;              // waves along features / slots
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
@@ -111,7 +169,9 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
   constexpr int kStageBytes = (TN + TM) * BK * 2;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(FN >= 1 && FM >= 1 && kWLoads >= 1 && kXLoads >= 1, "tile too small");
-  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
+  static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
+                "whole wave loads per tile");
+  static_assert(NS >= 2 && NS <= 5 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
   // Physical chunk of logical chunk c in row r is c ^ swz(r): the 16 rows read by 16
   // consecutive lanes then fall on distinct 16-byte bank groups (64 banks = 16 groups).
   auto swz = [](int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; };
@@ -121,51 +181,6 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % WN, wm = wave / WN;
   const int r32 = lane & 31, half = lane >> 5;
-
-  // ---- token tiles per expert and their prefix (lane L owns experts 4L .. 4L+3)
-  int te[4], local = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ee = lane * 4 + j;
-    const int kept = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
-    te[j] = (kept + TM - 1) / TM;
-    local += te[j];
-  }
-  int inc = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += o;
-  }
-  const int excl = inc - local;
-  const int MT = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
-  const int NT = (N + TN - 1) / TN;
-  const int NQ = (NT + kGroupN - 1) / kGroupN;
-  const int NG = ((MT + kGroupM - 1) / kGroupM) * NQ;
-
-  // ---- this block's tile
-  const int xcd = blockIdx.x & 7, slot = (blockIdx.x >> 3) & 31, round = blockIdx.x >> 8;
-  const int g = round * 8 + xcd;
-  if (g >= NG) return;
-  const int mt = (g / NQ) * kGroupM + slot % kGroupM;
-  const int nt = (g % NQ) * kGroupN + slot / kGroupM;
-  if (mt >= MT || nt >= NT) return;
-
-  const uint64_t bal = __ballot(mt >= excl && mt < inc);
-  const int owner = __ffsll((long long)bal) - 1;
-  int esel = 0, tstart = 0, run = excl;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (esel == 0 && mt >= run && mt < run + te[j]) {
-      esel = lane * 4 + j + 1;
-      tstart = run;
-    }
-    run += te[j];
-  }
-  const int e = __builtin_amdgcn_readfirstlane(__shfl(esel, owner, 64) - 1);
-  tstart = __builtin_amdgcn_readfirstlane(__shfl(tstart, owner, 64));
-  const int row0 = offsets[e] + (mt - tstart) * TM;
-  const int rows = min(TM, offsets[e + 1] - row0);
-  const int n0 = nt * TN;
   const int wrows = min(TN, N - n0);
 
   // ---- load plan.  A 1 KiB wave load fills kRowsPerLoad rows of kChunks 16-byte chunks: lane i
@@ -365,18 +380,78 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
   }
 }
 
+// The grouped GEMM kernel.  Each block works out the token tiles of every expert from
+// expert_offsets (device memory: the kept-row counts are only known on the device).  With
+// TMB > 0 it can run TMB-high token tiles instead of TMA-high ones; every block makes the same
+// choice from the same offsets: the height whose grid needs the fewest rounds over the `slots`
+// blocks the GPU runs at once, weighted by the tile height (taller tiles use the matrix cores
+// better, so the shorter height must win by 15 %).  The result does not depend on the choice:
+// each output element accumulates the same products in the same K order.
+template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
+          bool SILU>
+__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
+    const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, int E, int N, int K, int a_rows,
+    int slots) {
+  const int lane = threadIdx.x & 63;
+  const int NT = (N + TN - 1) / TN;
+  const TokenTiles<TMA> ta(offsets, E, lane);
+  bool use_b = false;
+  if constexpr (TMB > 0) {
+    const TokenTiles<TMB> tb(offsets, E, lane);
+    const int64_t ra = ((int64_t)ta.MT * NT + slots - 1) / slots;
+    const int64_t rb = ((int64_t)tb.MT * NT + slots - 1) / slots;
+    use_b = rb * TMB * 115 < ra * TMA * 100;
+    if (use_b) {
+      int mt, nt, e, row0, rows;
+      if (!tile_of_block(tb.MT, NT, mt, nt)) return;
+      tb.locate(offsets, lane, mt, e, row0, rows);
+      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, SILU>(A, row_token, W, bias, out, N, K,
+                                                            a_rows, e, row0, rows, nt * TN);
+      return;
+    }
+  }
+  int mt, nt, e, row0, rows;
+  if (!tile_of_block(ta.MT, NT, mt, nt)) return;
+  ta.locate(offsets, lane, mt, e, row0, rows);
+  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, SILU>(A, row_token, W, bias, out, N, K, a_rows,
+                                                        e, row0, rows, nt * TN);
+}
+
 namespace {
 
-template <int TN, int TM, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER, bool SILU>
+constexpr size_t tile_lds(int TN, int TM, int BK, int NS) {
+  const size_t ring = (size_t)NS * (TN + TM) * BK * 2;      // stage ring
+  const size_t tile = (size_t)TM * (TN * 2 + 16);           // epilogue staging tile
+  return ring > tile ? ring : tile;
+}
+
+// compute units of the current device (cached per device)
+int compute_units() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
+          bool SILU>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st) {
   if (rows_ub <= 0) return hipSuccess;
-  constexpr size_t ring = (size_t)NS * (TN + TM) * BK * 2;
-  constexpr size_t tile = (size_t)TM * (TN * 2 + 16);
-  constexpr size_t lds = ring > tile ? ring : tile;
+  constexpr size_t lds_a = tile_lds(TN, TMA, BK, NS);
+  constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS) : 0;
+  constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, INTERLEAVE, GATHER, SILU>;
+  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, SILU>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -384,14 +459,15 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  // upper bound on groups: token tiles <= rows_ub / TM + E
-  const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;
+  // upper bound on groups for the shorter tile height: token tiles <= rows_ub / TM + E
+  constexpr int tm_min = TMB > 0 && TMB < TMA ? TMB : TMA;
+  const int64_t mt_ub = (rows_ub + tm_min - 1) / tm_min + E;
   const int64_t nt = (N + TN - 1) / TN;
   const int64_t nq = (nt + kGroupN - 1) / kGroupN;
   const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
   const int64_t grid = (ng_ub + 7) / 8 * 256;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, A, row_token, offsets, W,
-                     bias, out, E, N, K, a_rows);
+                     bias, out, E, N, K, a_rows, compute_units() * MINB);
   return hipGetLastError();
 }
 
@@ -414,10 +490,10 @@ hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_t
                          hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, st);
   if (skinny(s))
-    return launch_grouped_gemm<64, 64, 64, 4, 2, true, true, true>(
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, true>(
         (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
         s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
-  return launch_grouped_gemm<256, 256, 32, 4, 1, true, true, true>(
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, true>(
       (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
       s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
 }
@@ -426,10 +502,10 @@ hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* off
                            const void* w2, const void* b2, void* y, hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, st);
   if (skinny(s))
-    return launch_grouped_gemm<64, 64, 64, 4, 2, true, false, false>(
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, false>(
         (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
         s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
-  return launch_grouped_gemm<256, 256, 32, 4, 1, true, false, false>(
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, false>(
       (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
       s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
 }
