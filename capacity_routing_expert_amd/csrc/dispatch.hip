@@ -23,6 +23,9 @@
 //                      bucket; blocks take (tile, group of 16 other tiles) work items and add
 //                      their partial counts with integer atomics (exact and order-free);
 //   k_dispatch_emit    slot_of / drop_mask / row_token from the ranks and the capacity.
+// Up to 1024 assignments a single workgroup does all of it instead (k_dispatch_small: one
+// bitonic sort of the (expert, fill order) keys, one per thread), which saves four dependent
+// launches.
 // Integer results only, no order-dependent reductions: the output is deterministic.
 #include "moe_internal.h"
 
@@ -300,12 +303,100 @@ __global__ __launch_bounds__(256) void k_dispatch_emit(const uint64_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- small batches
+// Up to kSmallN assignments: the whole dispatch in one workgroup.  Key of assignment i with
+// expert e: (e << 56) | (~ord(gate) << 24) | i (i < 2^24); ascending order is expert, then the
+// fill order of that expert.  Ids outside [0, E) get (0xFFFFFFFFFF << 24) | i, after every valid
+// key (~ord(gate) < 0xFFFFFFFF for any non-NaN gate).  The keys are unique, so the bitonic sort
+// in LDS has one result, the same order the bucketed multi-kernel path produces; the rank of a
+// key in its expert is its sorted position minus the expert's first position.
+constexpr int kSmallN = 1024;  // one key per thread of a 1024-thread workgroup
+
+__global__ __launch_bounds__(1024) void k_dispatch_small(
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int N, int E, int k,
+    int cap, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token, uint8_t* __restrict__ drop) {
+  __shared__ uint64_t sk[kSmallN];
+  __shared__ int cnt[260], start[260], koff[260];
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < N) P <<= 1;
+  for (int e = tid; e <= E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  uint64_t v = ~0ull;  // this thread's key; padding past N sorts last
+  if (tid < N) {
+    const int e = ids[tid];
+    if (e >= 0 && e < E) {
+      const uint64_t g = sort_key(gates[tid], 0u) >> 32;  // ~ord(gate)
+      v = ((uint64_t)e << 56) | (g << 24) | (uint64_t)tid;
+      atomicAdd(&cnt[e], 1);
+    } else {
+      v = 0xFFFFFFFFFF000000ull | (uint64_t)tid;
+    }
+  }
+  // bitonic sort over threads 0 .. P-1 (threads past P only meet each other): partners closer
+  // than 64 are in the same wave and trade keys by shuffle, farther ones through LDS
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      uint64_t other;
+      if (j >= 64) {
+        sk[tid] = v;
+        __syncthreads();
+        other = sk[tid ^ j];
+        __syncthreads();
+      } else {
+        other = __shfl_xor(v, j, 64);
+      }
+      const bool up = (tid & size) == 0, lower = (tid & j) == 0;
+      v = (lower == up) ? (v < other ? v : other) : (v < other ? other : v);
+    }
+  }
+  sk[tid] = v;
+  __syncthreads();
+  // expert starts in sorted order and kept-slot offsets
+  for (int e = tid; e <= E; e += 1024) {
+    start[e] = e < E ? cnt[e] : 0;
+    koff[e] = e < E ? min(cnt[e], cap) : 0;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    wave_exclusive_scan(start, E + 1, nullptr);
+    wave_exclusive_scan(koff, E + 1, nullptr);
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) {
+    if (e < E) counts[e] = cnt[e];
+    offsets[e] = koff[e];
+  }
+  for (int p = tid; p < N; p += 1024) {
+    const uint64_t key = sk[p];
+    const int i = (int)(key & 0xFFFFFFull);
+    const int e = (int)(key >> 56);
+    const bool valid = (key >> 24) != 0xFFFFFFFFFFull;
+    const int r = p - start[e];
+    if (valid && r < cap) {
+      const int slot = koff[e] + r;
+      slot_of[i] = slot;
+      drop[i] = 0;
+      row_token[slot] = i / k;
+    } else {
+      slot_of[i] = -1;
+      drop[i] = 1;
+    }
+  }
+}
+
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
                            int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st) {
   const int64_t N = s.T * (int64_t)s.top_k;
   const int E = s.n_experts;
+  if (N <= kSmallN) {
+    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), 0, st, ids, gates, (int)N, E,
+                       s.top_k, s.capacity, counts, offsets, slot_of, row_token, drop);
+    return hipGetLastError();
+  }
   const int nb = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
   hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, blk_hist);
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(nb), dim3(256), 0, st, ids, gates, N, E, s.capacity,

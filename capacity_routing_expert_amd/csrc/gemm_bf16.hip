@@ -171,7 +171,7 @@ __device__ __forceinline__ void gemm_tile(
   static_assert(FN >= 1 && FM >= 1 && kWLoads >= 1 && kXLoads >= 1, "tile too small");
   static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
                 "whole wave loads per tile");
-  static_assert(NS >= 2 && NS <= 5 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
+  static_assert(NS >= 2 && NS <= 8 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
   // Physical chunk of logical chunk c in row r is c ^ swz(r): the 16 rows read by 16
   // consecutive lanes then fall on distinct 16-byte bank groups (64 banks = 16 groups).
   auto swz = [](int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; };
