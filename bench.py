@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mid", help="worked_example | mid | fine | decode | collapse")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", default="compact", choices=["compact", "padded"],
+                    help="compact: the expert FFN runs over the kept rows only; padded: over "
+                         "every slot of the fixed per-expert buffers (n_experts x capacity rows)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -128,18 +131,30 @@ def main():
     inp = W.make_inputs(wl)
     d = L.upload(inp, dev)
     shape = L.shape_of(d, wl.top_k, cap)
-    ws = L.workspace(shape, dev)
+    padded = args.layout == "padded"
+    ws = (torch.empty(max(B.workspace_bytes_padded(shape), 256), dtype=torch.uint8, device=dev)
+          if padded else L.workspace(shape, dev))
     out = torch.empty_like(d["x"])
     counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        B.moe_layer_forward(shape, d["x"], d["w_router"], d["b_router"], d["w1"], d["b1"],
-                            d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
+        if padded:
+            B.moe_layer_forward_padded(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                       d["b1"], d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
+        else:
+            B.moe_layer_forward(shape, d["x"], d["w_router"], d["b_router"], d["w1"], d["b1"],
+                                d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
 
     def step_profiled(events):
-        B.moe_layer_forward_profiled(shape, d["x"], d["w_router"], d["b_router"], d["w1"], d["b1"],
-                                     d["w2"], d["b2"], out, events, expert_counts=counts, ws=ws)
+        if padded:
+            B.moe_layer_forward_padded(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                       d["b1"], d["w2"], d["b2"], out, expert_counts=counts,
+                                       ws=ws, events=events)
+        else:
+            B.moe_layer_forward_profiled(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                         d["b1"], d["w2"], d["b2"], out, events,
+                                         expert_counts=counts, ws=ws)
 
     def new_events():
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -182,7 +197,9 @@ def main():
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
     achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
-    traffic = traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2", args.config)
+    # the committed counter summaries are of the compact layout's launches
+    traffic = None if padded else traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2",
+                                                        args.config)
 
     route_bytes = wl.T * dm * inp["x"].itemsize + wl.n_experts * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
     combine_bytes = (2 * wl.T + n_kept) * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
@@ -209,7 +226,8 @@ def main():
         "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
         "config": {"workload": wl.name, "T": wl.T, "d_model": dm, "d_ff": ff,
                    "n_experts": wl.n_experts, "top_k": wl.top_k,
-                   "capacity_factor": wl.capacity_factor, "capacity": cap},
+                   "capacity_factor": wl.capacity_factor, "capacity": cap,
+                   "layout": args.layout},
         "expert_gemm_tflops": 2 * gemm_flop / expert_s / 1e12,
         "expert_gemm_frac_of_bf16_peak": 2 * gemm_flop / expert_s / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
@@ -223,6 +241,10 @@ def main():
         "route_GBps": route_bytes / (stage_ms["route"] / 1e3) / 1e9,
         "combine_GBps": combine_bytes / (stage_ms["combine"] / 1e3) / 1e9,
         "n_kept": n_kept,
+        "expert_rows_computed": wl.n_experts * cap if padded else n_kept,
+        # FLOP rate of what the matrix cores executed (buffer rows included), padded layout
+        "expert_gemm_tflops_executed": 2 * 2.0 * (wl.n_experts * cap if padded else n_kept) * dm * ff
+                                       / expert_s / 1e12,
         "drop_rate": 1.0 - n_kept / (wl.T * wl.top_k),
         "expert_rows": [int(v) for v in np.minimum(c, cap)],
     }

@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_status_string",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_layer_forward_profiled")
+           "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
+           "moe_layer_forward_padded")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,7 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_layer_forward_profiled.argtypes = L.moe_layer_forward.argtypes + [P]
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                     "moe_layer_forward", "moe_layer_forward_profiled"):
+                     "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
+           "moe_layer_forward_padded"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -87,6 +89,10 @@ def capacity(T: int, top_k: int, n_experts: int, capacity_factor: float) -> int:
 
 def workspace_bytes(shape: MoeShape) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def workspace_bytes_padded(shape: MoeShape) -> int:
+    return int(lib().moe_workspace_bytes_padded(ctypes.byref(shape)))
 
 
 def max_kept_rows(shape: MoeShape) -> int:
@@ -201,3 +207,20 @@ def moe_layer_forward_profiled(shape, x, w_router, b_router, w1, b1, w2, b2, out
                          slot_of, drop_mask, expert_counts, ws)
     _check(lib().moe_layer_forward_profiled(*args, _stream(stream), handles),
            "moe_layer_forward_profiled")
+
+
+def moe_layer_forward_padded(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
+                             topk_gates=None, slot_of=None, drop_mask=None, expert_counts=None,
+                             y_rows=None, ws=None, events=None, stream=None):
+    """The padded fixed-buffer layout; `y_rows` [n_experts * capacity, d_model] optional;
+    `events` None or 6 recorded torch.cuda.Event(enable_timing=True)."""
+    dt = _dtype_of(shape)
+    args = _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                         slot_of, drop_mask, expert_counts, ws)
+    handles = None
+    if events is not None:
+        handles = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+    y = _ptr(y_rows, "y_rows", dt) if y_rows is not None and y_rows.numel() else None
+    # the padded call takes y_rows before the workspace
+    _check(lib().moe_layer_forward_padded(*args[:-2], y, args[-2], args[-1], _stream(stream),
+                                          handles), "moe_layer_forward_padded")

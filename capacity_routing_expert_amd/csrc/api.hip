@@ -78,8 +78,8 @@ moe_status check_ptr(const void* p, size_t a, const char* name) {
   return MOE_OK;
 }
 
-moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes) {
-  const size_t need = layout(s).total;
+moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes, bool padded = false) {
+  const size_t need = layout(s, padded).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   if (need && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
@@ -106,12 +106,12 @@ int64_t max_rows(const moe_shape& s) {
   return a < b ? a : b;
 }
 
-Workspace layout(const moe_shape& s) {
+Workspace layout(const moe_shape& s, bool padded) {
   Workspace w;
   const int64_t N = s.T * (int64_t)s.top_k;
   const int64_t E = s.n_experts;
   const int64_t nb = (N + kDispatchChunk - 1) / kDispatchChunk;
-  const int64_t rows = max_rows(s);
+  const int64_t rows = padded ? E * s.capacity : max_rows(s);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -128,7 +128,9 @@ Workspace layout(const moe_shape& s) {
   w.blk_hist = take((size_t)nb * (E + 1) * 4);
   w.keys = take((size_t)N * 8);
   w.rank = take((size_t)N * 4);
-  w.row_token = take((size_t)rows * 4);
+  w.row_token = take((size_t)max_rows(s) * 4);
+  w.row_token_pad = take(padded ? (size_t)rows * 4 : 0);
+  w.offsets_pad = take(padded ? (size_t)(E + 1) * 4 : 0);
   w.h = take((size_t)rows * s.d_ff * elem_bytes(s));
   w.y = take((size_t)rows * s.d_model * elem_bytes(s));
   w.total = o;
@@ -156,7 +158,7 @@ moe_status do_dispatch(const moe_shape& s, const int32_t* ids, const float* gate
 moe_status check_forward_args(const moe_shape* shape, const void* x, const void* w_router,
                               const float* b_router, const void* w1, const void* b1,
                               const void* w2, const void* b2, void* out, void* ws,
-                              size_t ws_bytes) {
+                              size_t ws_bytes, bool padded = false) {
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   MOE_TRY(check_data_ptr(s, x, "x"));
@@ -168,7 +170,10 @@ moe_status check_forward_args(const moe_shape* shape, const void* x, const void*
   MOE_TRY(check_data_ptr(s, b2, "b2"));
   MOE_TRY(check_data_ptr(s, out, "out"));
   if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
-  MOE_TRY(check_ws(s, ws, ws_bytes));
+  if (padded && (int64_t)s.n_experts * s.capacity >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts * capacity = %lld >= 2^31",
+                (long long)((int64_t)s.n_experts * s.capacity));
+  MOE_TRY(check_ws(s, ws, ws_bytes, padded));
   return MOE_OK;
 }
 
@@ -176,7 +181,8 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
                          const float* b_router, const void* w1, const void* b1, const void* w2,
                          const void* b2, void* out, int32_t* topk_ids, float* topk_gates,
                          int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts, void* ws,
-                         size_t ws_bytes, hipStream_t st, moe_event_t const* events) {
+                         size_t ws_bytes, hipStream_t st, moe_event_t const* events,
+                         bool padded = false, void* y_rows = nullptr) {
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   auto rec = [&](int i) -> moe_status {
@@ -188,12 +194,14 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
     for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
     return MOE_OK;
   }
-  MOE_TRY(check_forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, ws, ws_bytes));
+  MOE_TRY(check_forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, ws, ws_bytes,
+                             padded));
+  if (y_rows) MOE_TRY(check_data_ptr(s, y_rows, "y_rows"));
   if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
   if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
   if (slot_of) MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
   if (expert_counts) MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
-  const Workspace L = layout(s);
+  const Workspace L = layout(s, padded);
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
   int32_t* slots = slot_of ? slot_of : at<int32_t>(ws, L.slot_of);
@@ -202,17 +210,27 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* row_token = at<int32_t>(ws, L.row_token);
   void* h = at<void>(ws, L.h);
-  void* y = at<void>(ws, L.y);
+  void* y = y_rows ? y_rows : at<void>(ws, L.y);
+  int64_t rows = max_rows(s);
 
   MOE_TRY(rec(0));
   MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, st));
   MOE_TRY(rec(1));
   MOE_TRY(do_dispatch(s, ids, gates, counts, offsets, slots, row_token, drop, ws, st));
+  if (padded) {  // every expert's buffer is computed whole: rows e * cap .. (e + 1) * cap - 1
+    int32_t* rt_pad = at<int32_t>(ws, L.row_token_pad);
+    int32_t* off_pad = at<int32_t>(ws, L.offsets_pad);
+    hipError_t err = launch_pad_layout(s, ids, offsets, row_token, slots, rt_pad, off_pad, st);
+    if (err != hipSuccess) return device_error(err, "padded layout");
+    row_token = rt_pad;
+    offsets = off_pad;
+    rows = (int64_t)s.n_experts * s.capacity;
+  }
   MOE_TRY(rec(2));
-  hipError_t err = launch_ffn_up(s, x, row_token, offsets, w1, b1, h, st);
+  hipError_t err = launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
   if (err != hipSuccess) return device_error(err, "expert up-projection");
   MOE_TRY(rec(3));
-  err = launch_ffn_down(s, h, offsets, w2, b2, y, st);
+  err = launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
   if (err != hipSuccess) return device_error(err, "expert down-projection");
   MOE_TRY(rec(4));
   err = launch_combine(s, x, gates, slots, y, out, st);
@@ -250,6 +268,12 @@ int32_t moe_capacity(int64_t T, int32_t top_k, int32_t n_experts, double capacit
 size_t moe_workspace_bytes(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
   return layout(*shape).total;
+}
+
+size_t moe_workspace_bytes_padded(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  if ((int64_t)shape->n_experts * shape->capacity >= ((int64_t)1 << 31)) return 0;
+  return layout(*shape, true).total;
 }
 
 int64_t moe_max_kept_rows(const moe_shape* shape) {
@@ -327,9 +351,9 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   const Workspace L = layout(s);
   hipStream_t st = (hipStream_t)stream;
   void* h = at<void>(ws, L.h);
-  hipError_t err = launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, st);
+  hipError_t err = launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, max_rows(s), st);
   if (err != hipSuccess) return device_error(err, "expert up-projection");
-  err = launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, st);
+  err = launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, max_rows(s), st);
   if (err != hipSuccess) return device_error(err, "expert down-projection");
   return MOE_OK;
 }
@@ -374,6 +398,21 @@ moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
   return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
                        slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
                        events);
+}
+
+moe_status moe_layer_forward_padded(const moe_shape* shape, const void* x, const void* w_router,
+                                    const float* b_router, const void* w1, const void* b1,
+                                    const void* w2, const void* b2, void* out, int32_t* topk_ids,
+                                    float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                                    int32_t* expert_counts, void* y_rows, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream,
+                                    moe_event_t const* events) {
+  if (events)
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                       slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
+                       events, true, y_rows);
 }
 
 }  // extern "C"

@@ -386,6 +386,49 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
   }
 }
 
+// ---------------------------------------------------------------- padded fixed buffers
+// "Some Tokens Do Not Get In", "Why there is a buffer": each expert owns a buffer of `cap`
+// slots whether or not it fills them, and the unused slots are computed anyway.  From the
+// compact result: the kept assignment of rank r of expert e moves to slot e * cap + r, buffer
+// row e * cap + r takes the token of that assignment or -1 (a zero row) when r is past the
+// expert's kept count, and the padded offsets are e * cap.  Thread id covers assignment id and
+// buffer row id.
+__global__ __launch_bounds__(256) void k_pad_layout(const int32_t* __restrict__ ids,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ row_token,
+                                                    int64_t N, int E, int cap,
+                                                    int32_t* __restrict__ slot_of,
+                                                    int32_t* __restrict__ row_token_pad,
+                                                    int32_t* __restrict__ offsets_pad) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id < N) {
+    const int sl = slot_of[id];
+    if (sl >= 0) {
+      const int e = ids[id];  // kept => 0 <= e < E
+      slot_of[id] = e * cap + (sl - offsets[e]);
+    }
+  }
+  if (id < (int64_t)E * cap) {
+    const int e = (int)(id / cap), r = (int)(id % cap);
+    const int kept = offsets[e + 1] - offsets[e];
+    row_token_pad[id] = r < kept ? row_token[offsets[e] + r] : -1;
+  }
+  if (id <= E) offsets_pad[id] = (int)id * cap;
+}
+
+hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32_t* offsets,
+                             const int32_t* row_token, int32_t* slot_of, int32_t* row_token_pad,
+                             int32_t* offsets_pad, hipStream_t st) {
+  const int64_t N = s.T * (int64_t)s.top_k;
+  const int64_t rows = (int64_t)s.n_experts * s.capacity;
+  int64_t n = N > rows ? N : rows;
+  if (n < s.n_experts + 1) n = s.n_experts + 1;
+  hipLaunchKernelGGL(k_pad_layout, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids,
+                     offsets, row_token, N, s.n_experts, s.capacity, slot_of, row_token_pad,
+                     offsets_pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,

@@ -32,10 +32,13 @@ __global__ __launch_bounds__(256) void k_ffn_up_f32(const float* __restrict__ x,
   const int s = (int)(id / f), n = (int)(id % f);
   if (s >= offsets[E]) return;
   const int e = expert_of_slot(offsets, E, s);
-  const float* xr = x + (int64_t)row_token[s] * d;
+  const int rt = row_token[s];  // -1: a zero row (padding)
   const float* wr = w1 + ((int64_t)e * f + n) * d;
   float acc = b1[(int64_t)e * f + n];
-  for (int j = 0; j < d; ++j) acc = fmaf(xr[j], wr[j], acc);
+  if (rt >= 0) {
+    const float* xr = x + (int64_t)rt * d;
+    for (int j = 0; j < d; ++j) acc = fmaf(xr[j], wr[j], acc);
+  }
   h[(int64_t)s * f + n] = acc / (1.0f + expf(-acc));
 }
 
@@ -59,8 +62,7 @@ __global__ __launch_bounds__(256) void k_ffn_down_f32(const float* __restrict__ 
 
 hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* row_token,
                              const int32_t* offsets, const void* w1, const void* b1, void* h,
-                             hipStream_t st) {
-  const int64_t rows = max_rows(s);
+                             int64_t rows, hipStream_t st) {
   const int64_t n = rows * s.d_ff;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_ffn_up_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -70,8 +72,8 @@ hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* r
 }
 
 hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t* offsets,
-                               const void* w2, const void* b2, void* y, hipStream_t st) {
-  const int64_t rows = max_rows(s);
+                               const void* w2, const void* b2, void* y, int64_t rows,
+                               hipStream_t st) {
   const int64_t n = rows * s.d_model;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_ffn_down_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,

@@ -198,8 +198,8 @@ __device__ __forceinline__ void gemm_tile(
     for (int j = 0; j < kXLoads; ++j) {
       const int row = (wave * kXLoads + j) * kRowsPerLoad + lrow;
       const int c = pch ^ swz(row);
-      xoff[j] = row < rows && c * 8 < K ? (uint32_t)(row_token[row0 + row] * K + c * 8) * 2u
-                                        : kOutOfRange;
+      const int rt = row < rows ? row_token[row0 + row] : -1;  // -1: a zero row (padding)
+      xoff[j] = rt >= 0 && c * 8 < K ? (uint32_t)(rt * K + c * 8) * 2u : kOutOfRange;
     }
   } else {
     xsrc = make_srd(A + (int64_t)row0 * K, (uint32_t)(rows * K * 2));
@@ -475,39 +475,44 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
 
 hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* row_token,
                              const int32_t* offsets, const void* w1, const void* b1, void* h,
-                             hipStream_t st);
+                             int64_t rows_ub, hipStream_t st);
 hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t* offsets,
-                               const void* w2, const void* b2, void* y, hipStream_t st);
+                               const void* w2, const void* b2, void* y, int64_t rows_ub,
+                               hipStream_t st);
 
 // Few rows per expert (decode-sized batches): the layer is bound by streaming the expert
 // weights, and 256 x 256 tiles would leave most compute units idle (8 experts x d_model / 256
 // tiles for the down-projection).  64 x 64 tiles with 64-deep stages and two blocks per compute
 // unit put every unit to work on its own weight rows with 48 KiB of loads in flight.
-static bool skinny(const moe_shape& s) { return max_rows(s) <= (int64_t)64 * s.n_experts; }
+static bool skinny(const moe_shape& s, int64_t rows_ub) {
+  return rows_ub <= (int64_t)64 * s.n_experts;
+}
 
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const void* w1, const void* b1, void* h,
-                         hipStream_t st) {
-  if (s.dtype != MOE_BF16) return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, st);
-  if (skinny(s))
+                         int64_t rows_ub, hipStream_t st) {
+  if (s.dtype != MOE_BF16)
+    return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, rows_ub, st);
+  if (skinny(s, rows_ub))
     return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, true>(
         (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
-        s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
+        s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
   return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, true>(
       (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
-      s.n_experts, s.d_ff, s.d_model, (int)s.T, max_rows(s), st);
+      s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
 }
 
 hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
-                           const void* w2, const void* b2, void* y, hipStream_t st) {
-  if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, st);
-  if (skinny(s))
+                           const void* w2, const void* b2, void* y, int64_t rows_ub,
+                           hipStream_t st) {
+  if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, rows_ub, st);
+  if (skinny(s, rows_ub))
     return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, false>(
         (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
-        s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
+        s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
   return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, false>(
       (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
-      s.n_experts, s.d_model, s.d_ff, (int)max_rows(s), max_rows(s), st);
+      s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
 }
 
 }  // namespace moe

@@ -45,15 +45,18 @@ struct Workspace {
   size_t keys;       // bucketed sort keys                        [T*k] u64
   size_t rank;       // rank of each bucketed key in its expert   [T*k] int32
   size_t row_token;  // token per slot                            [max_rows] int32
-  size_t h;          // activation between the GEMMs              [max_rows, d_ff]
-  size_t y;          // expert outputs per slot                   [max_rows, d_model]
+  size_t row_token_pad;  // padded layout: token per buffer row  [E * cap] int32 (else 0 B)
+  size_t offsets_pad;    // padded layout: e * cap                   [E+1] int32 (else 0 B)
+  size_t h;          // activation between the GEMMs              [rows, d_ff]
+  size_t y;          // expert outputs per slot                   [rows, d_model]
+                     // rows = max_rows (compact) or E * cap (padded)
   size_t total;
 };
 
 constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
 
 int64_t max_rows(const moe_shape& s);
-Workspace layout(const moe_shape& s);
+Workspace layout(const moe_shape& s, bool padded = false);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
 hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
@@ -65,11 +68,20 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
                            int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st);
 
+// rows_ub: an upper bound on the slot rows of the layout (max_rows(s) compact, E * capacity
+// padded); row_token entries < 0 are zero rows
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const void* w1, const void* b1, void* h,
-                         hipStream_t st);
+                         int64_t rows_ub, hipStream_t st);
 hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
-                           const void* w2, const void* b2, void* y, hipStream_t st);
+                           const void* w2, const void* b2, void* y, int64_t rows_ub,
+                           hipStream_t st);
+
+// compact slots -> padded fixed buffers: slot_of (in place) becomes e * cap + rank, the padded
+// row tokens (-1 for unused rows) and the padded offsets e * cap are written
+hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32_t* offsets,
+                             const int32_t* row_token, int32_t* slot_of, int32_t* row_token_pad,
+                             int32_t* offsets_pad, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape& s, const void* x, const float* gates,
                           const int32_t* slot_of, const void* y, void* out, hipStream_t st);

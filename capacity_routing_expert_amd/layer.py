@@ -62,6 +62,34 @@ def layer_forward(dev: dict, top_k: int, capacity: int, ws: torch.Tensor | None 
     return res
 
 
+def layer_forward_padded(dev: dict, top_k: int, capacity: int, ws: torch.Tensor | None = None,
+                         events=None, want_rows: bool = True) -> dict:
+    """The padded fixed-buffer layout in one call: as layer_forward, plus `y_rows`
+    [n_experts * capacity, d_model] (every buffer row's expert output) when want_rows."""
+    shape = shape_of(dev, top_k, capacity)
+    device = dev["x"].device
+    T, E = shape.T, shape.n_experts
+    if ws is None:
+        ws = torch.empty(max(B.workspace_bytes_padded(shape), 256), dtype=torch.uint8,
+                         device=device)
+    res = {
+        "out": torch.empty_like(dev["x"]),
+        "ids": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "slot_of": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "drop_mask": torch.empty((T, top_k), dtype=torch.uint8, device=device),
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+        "y_rows": torch.empty((E * capacity, shape.d_model), dtype=dev["x"].dtype,
+                              device=device) if want_rows else None,
+    }
+    B.moe_layer_forward_padded(shape, dev["x"], dev["w_router"], dev["b_router"], dev["w1"],
+                               dev["b1"], dev["w2"], dev["b2"], res["out"], topk_ids=res["ids"],
+                               topk_gates=res["gates"], slot_of=res["slot_of"],
+                               drop_mask=res["drop_mask"], expert_counts=res["counts"],
+                               y_rows=res["y_rows"], ws=ws, events=events)
+    return res
+
+
 def route(dev: dict, top_k: int, capacity: int, ws=None, want_logits=False) -> dict:
     shape = shape_of(dev, top_k, capacity)
     device = dev["x"].device

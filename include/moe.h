@@ -167,6 +167,35 @@ moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
                                       int32_t* expert_counts, void* ws, size_t ws_bytes,
                                       moe_stream_t stream, moe_event_t const* events);
 
+/* ---- Padded fixed-buffer layout.  "Some Tokens Do Not Get In", "Why there is a buffer": each
+ * expert gets a buffer of `capacity` slots whether it fills it or not, and the empty slots are
+ * computed anyway.  Same layer and same result as moe_layer_forward; only the layout of the
+ * expert rows differs: expert e owns rows [e * capacity, (e + 1) * capacity), row e * capacity
+ * + r holds its kept assignment of rank r in the fill order, and an unused row is a zero input
+ * row, so its expert output is W2 SiLU(b1) + b2 of that expert.  The expert FFN runs over all
+ * n_experts * capacity rows (the cost of the fixed buffers), against min(T * k, E * capacity)
+ * kept rows at most in the compact layout. */
+
+/* Workspace bytes for moe_layer_forward_padded; 0 for an invalid shape or when
+ * n_experts * capacity >= 2^31. */
+size_t moe_workspace_bytes_padded(const moe_shape* shape);
+
+/* moe_layer_forward in the padded layout.
+ *   slot_of [T, k] out (optional): e * capacity + rank, or -1 if dropped
+ *   y_rows  [n_experts * capacity, d_model] out (optional, dtype): every buffer row's expert
+ *           output, unused rows included; NULL keeps them in the workspace
+ *   events  NULL, or 6 hipEvent_t recorded as in moe_layer_forward_profiled (the padded
+ *           remap belongs to the dispatch stage)
+ * Other arguments, rules and errors as moe_layer_forward; MOE_ERR_UNSUPPORTED when
+ * n_experts * capacity >= 2^31. */
+moe_status moe_layer_forward_padded(const moe_shape* shape, const void* x, const void* w_router,
+                                    const float* b_router, const void* w1, const void* b1,
+                                    const void* w2, const void* b2, void* out, int32_t* topk_ids,
+                                    float* topk_gates, int32_t* slot_of, uint8_t* drop_mask,
+                                    int32_t* expert_counts, void* y_rows, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream,
+                                    moe_event_t const* events);
+
 #ifdef __cplusplus
 }
 #endif

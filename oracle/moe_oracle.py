@@ -49,6 +49,9 @@ __all__ = [
     "expert_ffn_slots",
     "combine",
     "forward",
+    "dispatch_padded",
+    "expert_ffn_padded",
+    "forward_padded",
     "forward_with_routing",
 ]
 
@@ -258,3 +261,67 @@ def forward(x, w_router, b_router, w1, b1, w2, b2, k: int, capacity_factor: floa
     res = forward_with_routing(x, r["ids"], r["gates"], cap, E, w1, b1, w2, b2)
     res.update({"logits": r["logits"], "probs": r["probs"], "gates_all": r["gates_all"]})
     return res
+
+
+def dispatch_padded(ids: np.ndarray, gates: np.ndarray, n_experts: int, cap: int) -> dict:
+    """The fixed per-expert buffers themselves ("Some Tokens Do Not Get In", "Why there is a
+    buffer": every expert gets a buffer of `cap` token slots whether it fills it or not).
+
+    Expert e's buffer is rows e*cap .. e*cap + cap - 1; its r-th kept assignment in the fill
+    order (the ranking of `dispatch`) sits in row e*cap + r; rows past its kept count are
+    empty (token -1).  Returns slot_of [T, k] (buffer row or -1) and row_token [E*cap]."""
+    d = dispatch(ids, gates, n_experts, cap)
+    T, k = ids.shape
+    slot_of = np.full((T, k), -1, dtype=np.int64)
+    row_token = np.full(n_experts * cap, -1, dtype=np.int64)
+    for t in range(T):
+        for c in range(k):
+            s = int(d["slot_of"][t, c])
+            if s < 0:
+                continue
+            e = int(ids[t, c])
+            r = s - int(d["offsets"][e])
+            slot_of[t, c] = e * cap + r
+            row_token[e * cap + r] = t
+    return {"slot_of": slot_of, "row_token": row_token, "counts": d["counts"],
+            "n_kept": d["n_kept"], "compact": d}
+
+
+def expert_ffn_padded(x, row_token, n_experts, cap, w1, b1, w2, b2, rows=None) -> np.ndarray:
+    """Expert output of every buffer row (or of the listed `rows`): FFN_e of the row's token,
+    and of an all-zero input row for an empty slot, which the fixed buffer computes anyway."""
+    row_token = np.asarray(row_token)
+    if rows is None:
+        rows = np.arange(n_experts * cap)
+    rows = np.asarray(rows, dtype=np.int64)
+    d = x.shape[1]
+    out = np.zeros((len(rows), d), dtype=np.float64)
+    if cap == 0 or len(rows) == 0:
+        return out
+    expert_of = rows // cap
+    for e in range(n_experts):
+        sel = np.nonzero(expert_of == e)[0]
+        if len(sel) == 0:
+            continue
+        tok = row_token[rows[sel]]
+        inp = np.zeros((len(sel), d), dtype=np.float64)
+        has = tok >= 0
+        inp[has] = np.asarray(x, dtype=np.float64)[tok[has]]
+        out[sel] = expert_ffn(inp, w1[e], b1[e], w2[e], b2[e])
+    return out
+
+
+def forward_padded(x, w_router, b_router, w1, b1, w2, b2, k: int, capacity_factor: float) -> dict:
+    """Whole layer with the fixed buffers computed whole: route, capacity, fill the buffers,
+    expert FFN of every buffer row, combine from the buffer rows.  The output is the layer's
+    output (empty rows are never combined); Y holds every buffer row."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    cap = capacity(T, k, E, capacity_factor)
+    d = dispatch_padded(r["ids"], r["gates"], E, cap)
+    Y = expert_ffn_padded(x, d["row_token"], E, cap, w1, b1, w2, b2)
+    out, all_dropped = combine(x, r["gates"], d["slot_of"], Y)
+    return {"ids": r["ids"], "gates": r["gates"], "cap": cap, "slot_of": d["slot_of"],
+            "row_token": d["row_token"], "counts": d["counts"], "Y": Y, "out": out,
+            "all_dropped": all_dropped}

@@ -15,7 +15,10 @@ What pins what:
   * brute force: integer-valued router logits summed exactly in Python integers; top-k by
     enumerating all k-subsets; slot ranks by an independent counting definition;
   * invariants: counts sum to T*k, slot map is a bijection, kept gates dominate dropped
-    gates, permutation equivariance, capacity 0 returns the input.
+    gates, permutation equivariance, capacity 0 returns the input;
+  * the padded fixed buffers: the worked example's batches in their buffers with one empty
+    slot, an empty slot's output b2 exactly when b1 = 0 (SiLU(0) = 0), the same layer output
+    as the compact layout.
 """
 from __future__ import annotations
 
@@ -391,11 +394,79 @@ def check_capacity_zero(o):
     assert np.array_equal(res["out"], x) and np.signbit(res["out"][3, 2])
 
 
+# ----------------------------------------------------------------------------- padded buffers
+def check_padded_worked_example(o):
+    """"Why there is a buffer": with the worked example's forced assignment and capacity 2,
+    the four fixed buffers hold the page's kept batches, in fill order (gate descending), and
+    expert 2's buffer has one empty slot; token 4 has no slot."""
+    g = golden()
+    ids = np.array(g["assignment"]["ids"], dtype=np.int32)[:, None]
+    gates = np.array(FORCED_GATES, dtype=np.float32)[:, None]
+    cap = g["capacity"]["value"]
+    d = o.dispatch_padded(ids, gates, 4, cap)
+    rows = [int(t) for t in d["row_token"]]
+    # buffer e holds the page's kept batch e, ordered by the forced gates (descending)
+    want = []
+    for batch in g["kept_batches"]["value"]:
+        b = sorted(batch, key=lambda t: -FORCED_GATES[t])
+        want += b + [-1] * (cap - len(b))
+    assert rows == want
+    assert int(d["slot_of"][g["dropped_token"]["value"], 0]) == -1
+    assert sum(r < 0 for r in rows) == 4 * cap - (8 - 1)
+
+
+def check_padded_empty_rows(o):
+    """An empty slot's input is the zero row: with b1 = 0, SiLU(0) = 0 makes its expert output
+    exactly b2; with b1 != 0 it is torch's FFN of a zero row."""
+    rng = _rng(47)
+    T, d, f, E, k = 12, 4, 6, 3, 1
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d)) * 3
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    res = o.forward_padded(x, w, None, w1, np.zeros_like(b1), w2, b2, k, 2.0)  # cap = 8
+    cap = res["cap"]
+    assert cap == 8
+    empty = np.nonzero(res["row_token"] < 0)[0]
+    assert len(empty) == E * cap - T * k
+    for r in empty:
+        assert np.array_equal(res["Y"][r], b2[r // cap])
+    res = o.forward_padded(x, w, None, w1, b1, w2, b2, k, 2.0)
+    for r in np.nonzero(res["row_token"] < 0)[0]:
+        e = r // cap
+        want = _torch_ffn(np.zeros((1, d)), w1[e], b1[e], w2[e], b2[e])[0]
+        assert np.max(np.abs(res["Y"][r] - want)) < 1e-14
+
+
+def check_padded_same_layer(o):
+    """Computing the empty slots changes nothing the layer returns: same routing, same kept
+    assignments, same output as the compact layout (to float64 rounding of the batched
+    products), and each filled buffer row is torch's FFN of its token."""
+    rng = _rng(53)
+    T, d, f, E, k = 20, 6, 8, 5, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    for C in (0.5, 1.25):
+        a = o.forward(x, w, None, w1, b1, w2, b2, k, C)
+        p = o.forward_padded(x, w, None, w1, b1, w2, b2, k, C)
+        assert np.array_equal(a["slot_of"] >= 0, p["slot_of"] >= 0)
+        assert np.max(np.abs(a["out"] - p["out"])) < 1e-13
+        cap = p["cap"]
+        for r in np.nonzero(p["row_token"] >= 0)[0]:
+            e, t = r // cap, p["row_token"][r]
+            assert np.max(np.abs(p["Y"][r] - _torch_ffn(x[t:t + 1], w1[e], b1[e], w2[e], b2[e])[0])) < 1e-13
+        # the kept assignment of rank r of expert e sits in row e * cap + r
+        for t in range(T):
+            for c in range(k):
+                if a["slot_of"][t, c] >= 0:
+                    e = a["ids"][t, c]
+                    assert p["slot_of"][t, c] == e * cap + a["slot_of"][t, c] - a["offsets"][e]
+
+
 ALL_CHECKS = [
     check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
     check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
     check_worked_example_dispatch, check_dispatch_exhaustive, check_dispatch_invariants,
     check_permutation_equivariance, check_silu_closed_forms, check_expert_ffn_vs_torch,
     check_worked_example_outputs, check_dense_special_case, check_dropless_per_token,
-    check_all_experts, check_capacity_zero,
+    check_all_experts, check_capacity_zero, check_padded_worked_example,
+    check_padded_empty_rows, check_padded_same_layer,
 ]

@@ -360,3 +360,76 @@ def test_short_workspace_is_refused():
     with pytest.raises(B.MoeError) as ei:
         L.layer_forward(dev, 2, 32, ws=ws)
     assert ei.value.status == 3
+
+
+# --------------------------------------------------------------------------- padded fixed buffers
+PADDED_SMALL = [
+    # T, d, f, E, k, C, dtype   (E * cap buffer rows; skinny and large GEMM tiles both covered)
+    (7, 72, 136, 2, 2, 1.0, "bf16"),
+    (65, 264, 328, 8, 2, 1.25, "bf16"),
+    (1000, 136, 72, 8, 3, 1.0, "bf16"),
+    (300, 128, 256, 16, 4, 0.25, "bf16"),
+    (65, 12, 20, 8, 2, 0.75, "f32"),
+    (200, 16, 16, 200, 3, 2.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,C,dt", PADDED_SMALL)
+def test_padded_small_shapes(T, d, f, E, k, C, dt):
+    """moe_layer_forward_padded against the oracle's fixed buffers: every buffer row, the
+    empty ones included (FFN of a zero row), the buffer slots exactly, and the layer output."""
+    inp = W.make_shape_inputs(T, d, f, E, dt, seed=T * 17 + E, router_bias_std=1.0)
+    f64 = lambda a: W.to_float64(a, dt)
+    dev = L.upload(inp, DEV)
+    cap = O.capacity(T, k, E, C)
+    res = L.layer_forward_padded(dev, k, cap)
+    ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
+    full = O.forward(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], f64(inp["w1"]),
+                     f64(inp["b1"]), f64(inp["w2"]), f64(inp["b2"]), k, C)
+    P.compare_route(ids, gates, full)
+    pref = O.dispatch_padded(ids, gates, E, cap)
+    assert np.array_equal(P.to_np(res["slot_of"]), pref["slot_of"])
+    Y = O.expert_ffn_padded(f64(inp["x"]), pref["row_token"], E, cap, f64(inp["w1"]),
+                            f64(inp["b1"]), f64(inp["w2"]), f64(inp["b2"]))
+    if E * cap:
+        assert P.max_abs_rel(P.to_np(res["y_rows"]), Y) <= P.TOL[dt]
+        empty = pref["row_token"] < 0
+        if empty.any():
+            assert P.max_abs_rel(P.to_np(res["y_rows"])[empty], Y[empty]) <= P.TOL[dt]
+    out_ref, all_dropped = O.combine(f64(inp["x"]), gates, pref["slot_of"], Y)
+    assert P.max_abs_rel(P.to_np(res["out"]), out_ref) <= P.TOL[dt]
+    for t in np.nonzero(all_dropped)[0]:
+        assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
+
+
+@pytest.mark.parametrize("key", ["mid", "decode"])
+def test_padded_matches_compact(key):
+    """At full size the padded layout computes E * cap rows but returns the compact layout's
+    output bit for bit (each kept row accumulates the same products in the same K order);
+    its slots are e * cap + rank, and sampled empty rows match the oracle's FFN of a zero row."""
+    inp, ref, cap = case(key)
+    wl = inp["workload"]
+    dev = L.upload(inp, DEV)
+    a = L.layer_forward(dev, wl.top_k, cap)
+    p = L.layer_forward_padded(dev, wl.top_k, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(a["out"].view(torch.int16), p["out"].view(torch.int16))
+    ids = P.to_np(a["ids"])
+    so_a, so_p = P.to_np(a["slot_of"]), P.to_np(p["slot_of"])
+    offs = np.concatenate([[0], np.cumsum(np.minimum(P.to_np(a["counts"]), cap))])
+    kept = so_a >= 0
+    assert np.array_equal(so_p >= 0, kept)
+    assert np.array_equal(so_p[kept], ids[kept] * cap + so_a[kept] - offs[ids[kept]])
+    pref = O.dispatch_padded(ids, P.to_np(a["gates"]), wl.n_experts, cap)
+    empty = np.nonzero(pref["row_token"] < 0)[0]
+    say(f"[{key}] padded: {wl.n_experts * cap} buffer rows, {len(empty)} empty")
+    if len(empty):
+        rows = np.random.default_rng(5).choice(empty, size=min(64, len(empty)), replace=False)
+        dt = inp["dtype"]
+        Y = O.expert_ffn_padded(W.to_float64(inp["x"], dt), pref["row_token"], wl.n_experts, cap,
+                                F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
+                                F64(inp["b2"], dt), rows=rows)
+        got = P.to_np(p["y_rows"][torch.as_tensor(rows, device=DEV)])
+        assert P.max_abs_rel(got, Y) <= P.TOL[dt]
+    del dev, a, p
+    torch.cuda.empty_cache()

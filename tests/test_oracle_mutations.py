@@ -141,7 +141,52 @@ def _combine_plus_zero(x, gates, slot_of, Y):
     return out + 0.0, dropped  # turns -0.0 into +0.0 on the residual path
 
 
+def _ffn_padded_minus_one_index(x, row_token, n_experts, cap, w1, b1, w2, b2, rows=None):
+    # an empty slot's -1 used as an index: the last token's row instead of a zero row
+    if rows is None:
+        rows = np.arange(n_experts * cap)
+    rows = np.asarray(rows)
+    out = np.zeros((len(rows), x.shape[1]))
+    for j, r in enumerate(rows):
+        e = r // cap
+        out[j] = O.expert_ffn(np.asarray(x, np.float64)[[row_token[r]]], w1[e], b1[e], w2[e], b2[e])[0]
+    return out
+
+
+def _dispatch_padded_reversed(ids, gates, n_experts, cap):
+    d = _orig["dispatch_padded"](ids, gates, n_experts, cap)
+    rt = d["row_token"].copy()
+    so = d["slot_of"].copy()
+    for e in range(n_experts):
+        blk = rt[e * cap:(e + 1) * cap]
+        n = int((blk >= 0).sum())
+        rt[e * cap:e * cap + n] = blk[:n][::-1]
+    for t in range(so.shape[0]):
+        for c in range(so.shape[1]):
+            s = so[t, c]
+            if s >= 0:
+                e = s // cap
+                n = int((d["row_token"][e * cap:(e + 1) * cap] >= 0).sum())
+                so[t, c] = e * cap + (n - 1 - (s - e * cap))
+    d.update(row_token=rt, slot_of=so)
+    return d
+
+
+def _dispatch_padded_compact_rows(ids, gates, n_experts, cap):
+    # buffer rows at the compact offsets instead of e * cap
+    d = _orig["dispatch_padded"](ids, gates, n_experts, cap)
+    comp = d["compact"]
+    rt = np.full(n_experts * cap, -1, dtype=np.int64)
+    n = int(comp["n_kept"])
+    rt[:n] = comp["row_token"][:n]
+    d.update(row_token=rt, slot_of=comp["slot_of"].astype(np.int64))
+    return d
+
+
 MUTATIONS = {
+    "padded_empty_slot_uses_last_token": {"expert_ffn_padded": _ffn_padded_minus_one_index},
+    "padded_buffer_order_reversed": {"dispatch_padded": _dispatch_padded_reversed},
+    "padded_rows_at_compact_offsets": {"dispatch_padded": _dispatch_padded_compact_rows},
     "capacity_ceil": {"capacity": _cap_ceil},
     "capacity_without_k": {"capacity": _cap_no_k},
     "capacity_float_arith": {"capacity": _cap_float},
