@@ -84,8 +84,16 @@ def cpu_baseline(inp, wl, cap):
     while not times or (sum(times) < 10.0 and len(times) < 20):
         t0 = time.perf_counter()
         r = O.route(x, wr, inp["b_router"], wl.top_k)
-        res = O.forward_with_routing(x, r["ids"], r["gates"], cap, wl.n_experts, F64(inp["w1"]),
-                                     F64(inp["b1"]), F64(inp["w2"]), F64(inp["b2"]))
+        if wl.expert == "gated":
+            disp = O.dispatch(r["ids"], r["gates"], wl.n_experts, cap)
+            Y = O.expert_ffn_slots_gated(x, disp["row_token"], disp["offsets"], F64(inp["w1"]),
+                                         F64(inp["w2"]))
+            O.combine(x, r["gates"], disp["slot_of"], Y)
+            res = disp
+        else:
+            res = O.forward_with_routing(x, r["ids"], r["gates"], cap, wl.n_experts,
+                                         F64(inp["w1"]), F64(inp["b1"]), F64(inp["w2"]),
+                                         F64(inp["b2"]))
         times.append(time.perf_counter() - t0)
     t = float(np.mean(times))
     # the per-expert float64 weight conversion is inside the timed region: it is part of
@@ -102,7 +110,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mid", help="worked_example | mid | fine | decode | collapse")
+    ap.add_argument("--config", default="mid",
+                    help="worked_example | mid | fine | decode | collapse | gated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", default="compact", choices=["compact", "padded"],
                     help="compact: the expert FFN runs over the kept rows only; padded: over "
@@ -138,8 +147,16 @@ def main():
     counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    gated = wl.expert == "gated"
+    if gated and padded:
+        print("the padded layout is built for the FFN expert only", file=sys.stderr)
+        sys.exit(2)
+
     def step():
-        if padded:
+        if gated:
+            B.moe_layer_forward_gated(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                      d["w2"], out, expert_counts=counts, ws=ws)
+        elif padded:
             B.moe_layer_forward_padded(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
                                        d["b1"], d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
         else:
@@ -147,7 +164,10 @@ def main():
                                 d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
 
     def step_profiled(events):
-        if padded:
+        if gated:
+            B.moe_layer_forward_gated(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                      d["w2"], out, expert_counts=counts, ws=ws, events=events)
+        elif padded:
             B.moe_layer_forward_padded(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
                                        d["b1"], d["w2"], d["b2"], out, expert_counts=counts,
                                        ws=ws, events=events)
@@ -191,11 +211,14 @@ def main():
     c = counts.cpu().numpy()
     n_kept = int(np.minimum(c, cap).sum())
     dm, ff = wl.d_model, wl.d_ff
-    gemm_flop = 2.0 * n_kept * dm * ff  # each of the two expert GEMMs, kept rows only
+    # kept rows only; a gated expert's first GEMM has 2 d_ff outputs (gate and up)
+    gemm2_flop = 2.0 * n_kept * dm * ff
+    gemm1_flop = 2.0 * gemm2_flop if gated else gemm2_flop
     expert_s = (stage_ms["expert_up"] + stage_ms["expert_down"]) / 1e3
     dom = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
+    gemm_flop = gemm1_flop if dom == "expert_up" else gemm2_flop
     achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
     # the committed counter summaries are of the compact layout's launches
     traffic = None if padded else traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2",
@@ -228,12 +251,14 @@ def main():
                    "n_experts": wl.n_experts, "top_k": wl.top_k,
                    "capacity_factor": wl.capacity_factor, "capacity": cap,
                    "layout": args.layout},
-        "expert_gemm_tflops": 2 * gemm_flop / expert_s / 1e12,
-        "expert_gemm_frac_of_bf16_peak": 2 * gemm_flop / expert_s / 1e12 / PEAK_BF16_TFLOPS,
+        "expert_gemm_tflops": (gemm1_flop + gemm2_flop) / expert_s / 1e12,
+        "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
+                                         / PEAK_BF16_TFLOPS,
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "units_per_launch": f"{n_kept} kept rows x 2*{dm}*{ff} FLOP"},
+                     "units_per_launch": f"{n_kept} kept rows x 2*{dm}*{ff}"
+                                         f"{'*2' if gated and dom == 'expert_up' else ''} FLOP"},
         "stages_ms": stage_ms,
         "stage_timing": "HIP events at the stage boundaries over a second run of the same number "
                         "of steps, right after the timed region",
@@ -243,7 +268,8 @@ def main():
         "n_kept": n_kept,
         "expert_rows_computed": wl.n_experts * cap if padded else n_kept,
         # FLOP rate of what the matrix cores executed (buffer rows included), padded layout
-        "expert_gemm_tflops_executed": 2 * 2.0 * (wl.n_experts * cap if padded else n_kept) * dm * ff
+        "expert_gemm_tflops_executed": (3 if gated else 2) * 2.0
+                                       * (wl.n_experts * cap if padded else n_kept) * dm * ff
                                        / expert_s / 1e12,
         "drop_rate": 1.0 - n_kept / (wl.T * wl.top_k),
         "expert_rows": [int(v) for v in np.minimum(c, cap)],

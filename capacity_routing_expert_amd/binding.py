@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_status_string",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
-           "moe_layer_forward_padded")
+           "moe_layer_forward_padded", "moe_layer_forward_gated")
 
 
 class MoeShape(ctypes.Structure):
@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_profiled.argtypes = L.moe_layer_forward.argtypes + [P]
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                      "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
-           "moe_layer_forward_padded"):
+           "moe_layer_forward_padded", "moe_layer_forward_gated"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -224,3 +224,22 @@ def moe_layer_forward_padded(shape, x, w_router, b_router, w1, b1, w2, b2, out, 
     # the padded call takes y_rows before the workspace
     _check(lib().moe_layer_forward_padded(*args[:-2], y, args[-2], args[-1], _stream(stream),
                                           handles), "moe_layer_forward_padded")
+
+
+def moe_layer_forward_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids=None,
+                            topk_gates=None, slot_of=None, drop_mask=None, expert_counts=None,
+                            ws=None, events=None, stream=None):
+    """Gated experts: w13 [E, 2 d_ff, d_model] (gate rows first), w2 [E, d_model, d_ff], no
+    biases; bf16 only.  `events` None or 6 recorded torch.cuda.Event(enable_timing=True)."""
+    dt = _dtype_of(shape)
+    handles = None
+    if events is not None:
+        handles = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+    _check(lib().moe_layer_forward_gated(
+        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
+        _ptr(b_router, "b_router", torch.float32), _ptr(w13, "w13", dt), _ptr(w2, "w2", dt),
+        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
+        _ptr(topk_gates, "topk_gates", torch.float32), _ptr(slot_of, "slot_of", torch.int32),
+        _ptr(drop_mask, "drop_mask", torch.uint8), _ptr(expert_counts, "expert_counts", torch.int32),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), handles),
+        "moe_layer_forward_gated")

@@ -158,16 +158,16 @@ moe_status do_dispatch(const moe_shape& s, const int32_t* ids, const float* gate
 moe_status check_forward_args(const moe_shape* shape, const void* x, const void* w_router,
                               const float* b_router, const void* w1, const void* b1,
                               const void* w2, const void* b2, void* out, void* ws,
-                              size_t ws_bytes, bool padded = false) {
+                              size_t ws_bytes, bool padded = false, bool gated = false) {
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   MOE_TRY(check_data_ptr(s, x, "x"));
   MOE_TRY(check_data_ptr(s, w_router, "w_router"));
   if (b_router) MOE_TRY(check_ptr(b_router, 4, "b_router"));
   MOE_TRY(check_data_ptr(s, w1, "w1"));
-  MOE_TRY(check_data_ptr(s, b1, "b1"));
+  if (!gated) MOE_TRY(check_data_ptr(s, b1, "b1"));  // the gated expert has no biases
   MOE_TRY(check_data_ptr(s, w2, "w2"));
-  MOE_TRY(check_data_ptr(s, b2, "b2"));
+  if (!gated) MOE_TRY(check_data_ptr(s, b2, "b2"));
   MOE_TRY(check_data_ptr(s, out, "out"));
   if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
   if (padded && (int64_t)s.n_experts * s.capacity >= ((int64_t)1 << 31))
@@ -182,7 +182,7 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
                          const void* b2, void* out, int32_t* topk_ids, float* topk_gates,
                          int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts, void* ws,
                          size_t ws_bytes, hipStream_t st, moe_event_t const* events,
-                         bool padded = false, void* y_rows = nullptr) {
+                         bool padded = false, void* y_rows = nullptr, bool gated = false) {
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   auto rec = [&](int i) -> moe_status {
@@ -194,8 +194,13 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
     for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
     return MOE_OK;
   }
+  if (gated) {
+    if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the gated expert is bf16 only");
+    if ((int64_t)4 * s.d_ff * s.d_model >= ((int64_t)1 << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "2 * d_ff * d_model bf16 weights per expert: >= 2 GiB");
+  }
   MOE_TRY(check_forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, ws, ws_bytes,
-                             padded));
+                             padded, gated));
   if (y_rows) MOE_TRY(check_data_ptr(s, y_rows, "y_rows"));
   if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
   if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
@@ -227,10 +232,12 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
     rows = (int64_t)s.n_experts * s.capacity;
   }
   MOE_TRY(rec(2));
-  hipError_t err = launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
+  hipError_t err = gated ? launch_ffn_up_gated(s, x, row_token, offsets, w1, h, rows, st)
+                         : launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
   if (err != hipSuccess) return device_error(err, "expert up-projection");
   MOE_TRY(rec(3));
-  err = launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
+  err = gated ? launch_ffn_down_nobias(s, h, offsets, w2, y, rows, st)
+              : launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
   if (err != hipSuccess) return device_error(err, "expert down-projection");
   MOE_TRY(rec(4));
   err = launch_combine(s, x, gates, slots, y, out, st);
@@ -413,6 +420,20 @@ moe_status moe_layer_forward_padded(const moe_shape* shape, const void* x, const
   return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
                        slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
                        events, true, y_rows);
+}
+
+moe_status moe_layer_forward_gated(const moe_shape* shape, const void* x, const void* w_router,
+                                   const float* b_router, const void* w13, const void* w2,
+                                   void* out, int32_t* topk_ids, float* topk_gates,
+                                   int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts,
+                                   void* ws, size_t ws_bytes, moe_stream_t stream,
+                                   moe_event_t const* events) {
+  if (events)
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  return layer_forward(shape, x, w_router, b_router, w13, nullptr, w2, nullptr, out, topk_ids,
+                       topk_gates, slot_of, drop_mask, expert_counts, ws, ws_bytes,
+                       (hipStream_t)stream, events, false, nullptr, true);
 }
 
 }  // extern "C"

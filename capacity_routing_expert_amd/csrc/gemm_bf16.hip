@@ -53,6 +53,11 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// epilogue activation of a tile
+constexpr int kActNone = 0;   // Y = acc + bias
+constexpr int kActSilu = 1;   // H = SiLU(acc + bias)
+constexpr int kActGated = 2;  // H = SiLU(gate) * up, gate and up rows of one weight tile, no bias
+
 constexpr int kGroupM = 8;               // token tiles per XCD group
 constexpr int kGroupN = 32 / kGroupM;    // weight tiles per XCD group
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset beyond every buffer range used
@@ -150,7 +155,7 @@ __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) 
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, bool SILU>
+template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
@@ -172,6 +177,10 @@ __device__ __forceinline__ void gemm_tile(
   static_assert(TM % (kRowsPerLoad * kWaves) == 0 && TN % (kRowsPerLoad * kWaves) == 0,
                 "whole wave loads per tile");
   static_assert(NS >= 2 && NS <= 8 && (NS - 1) * kLoads < 64, "ring depth (vmcnt holds 63)");
+  constexpr bool GATED = ACT == kActGated;
+  // output features per tile: a gated tile holds a gate row and an up row per output feature
+  constexpr int TNO = GATED ? TN / 2 : TN;
+  static_assert(!GATED || FN % 2 == 0, "gated tiles pair gate block i with up block i + FN/2");
   // Physical chunk of logical chunk c in row r is c ^ swz(r): the 16 rows read by 16
   // consecutive lanes then fall on distinct 16-byte bank groups (64 banks = 16 groups).
   auto swz = [](int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; };
@@ -181,7 +190,7 @@ __device__ __forceinline__ void gemm_tile(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % WN, wm = wave / WN;
   const int r32 = lane & 31, half = lane >> 5;
-  const int wrows = min(TN, N - n0);
+  const int wrows = min(TN, N - n0);  // weight rows of the tile (non-gated)
 
   // ---- load plan.  A 1 KiB wave load fills kRowsPerLoad rows of kChunks 16-byte chunks: lane i
   // writes row i / kChunks, physical chunk p = i % kChunks, which holds logical chunk
@@ -189,7 +198,28 @@ __device__ __forceinline__ void gemm_tile(
   // the logical chunk of a lane can differ from one load of the stage to the next.
   const int lrow = lane / kChunks;
   const int pch = lane % kChunks;
-  const i32x4_t wsrc = make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
+  // Weight rows.  Non-gated: rows n0 .. n0 + TN - 1 of expert e's [N, K] block (rows past N
+  // are out of the resource's range).  Gated: expert e's block is [2N, K], gate rows first;
+  // LDS row rho of wave half wv = rho / (TN / 2) holds gate row n0 + wv TN/4 + m (m < TN/4) or
+  // the up row N + n0 + wv TN/4 + (m - TN/4), so gate block i and up block i + FN/2 of a wave
+  // cover the same output features; features past N are out of range.
+  const i32x4_t wsrc =
+      GATED ? make_srd(W + (int64_t)e * 2 * N * K, (uint32_t)(2 * N * K * 2))
+            : make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
+  uint32_t woff[kWLoads];  // byte offset of the lane's chunk at stage 0, or kOutOfRange
+#pragma unroll
+  for (int j = 0; j < kWLoads; ++j) {
+    const int row = (wave * kWLoads + j) * kRowsPerLoad + lrow;
+    const int c = pch ^ swz(row);
+    if (GATED) {
+      const int wv = row / (TN / 2), m = row % (TN / 2);
+      const int feat = n0 + wv * (TN / 4) + (m % (TN / 4));
+      const int grow = feat + (m >= TN / 4 ? N : 0);
+      woff[j] = feat < N && c * 8 < K ? (uint32_t)(grow * K + c * 8) * 2u : kOutOfRange;
+    } else {
+      woff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
+    }
+  }
   i32x4_t xsrc;
   uint32_t xoff[kXLoads];  // byte offset of the lane's chunk in stage 0, or kOutOfRange
   if (GATHER) {
@@ -223,10 +253,9 @@ __device__ __forceinline__ void gemm_tile(
   do {                                                                                         \
     if ((q) < kWLoads) {                                                                       \
       const int g_ = wave * kWLoads + (q);                                                     \
-      const int row_ = g_ * kRowsPerLoad + lrow;                                               \
-      const int c_ = pch ^ swz(row_);                                                          \
+      const int c_ = pch ^ swz(g_ * kRowsPerLoad + lrow);                                      \
       lds_dma16(wsrc, sb_ + (uint32_t)(g_ * 1024),                                             \
-                k0_ + c_ * 8 < K ? (uint32_t)((row_ * K + c_ * 8) * 2) + kb_ : kOutOfRange);   \
+                (k0_ + c_ * 8 < K && woff[(q)] != kOutOfRange) ? woff[(q)] + kb_ : kOutOfRange); \
     } else {                                                                                   \
       const int j_ = (q) - kWLoads;                                                            \
       const int c_ = pch ^ swz((wave * kXLoads + j_) * kRowsPerLoad + lrow);                   \
@@ -333,18 +362,21 @@ __device__ __forceinline__ void gemm_tile(
 
   // ---- epilogue.  Lane (r32, half) holds, for block (i, j), features
   // 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32.  Bias + activation + bf16 go
-  // into an LDS tile [TM slots][TN features] (row pitch TN * 2 + 16 bytes, so 16 consecutive
-  // rows start on distinct banks); the tile then leaves as coalesced 16-byte stores.
-  constexpr int kPitch = TN * 2 + 16;
+  // into an LDS tile [TM slots][TNO features] (row pitch TNO * 2 + 16 bytes, so 16 consecutive
+  // rows start on distinct banks); the tile then leaves as coalesced 16-byte stores.  A gated
+  // tile pairs gate block i with up block i + FN/2 (same lane layout, same output features).
+  constexpr int kPitch = TNO * 2 + 16;
+  constexpr int FNO = GATED ? FN / 2 : FN;  // output blocks per wave along features
   unsigned char* stile = reinterpret_cast<unsigned char*>(smem);
   __syncthreads();  // every wave is done reading the ring
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
+  for (int i = 0; i < FNO; ++i) {
     uint2 bb[4];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int n = n0 + wn * (TN / WN) + i * 32 + 8 * g4 + 4 * half;
-      bb[g4] = n < N ? *reinterpret_cast<const uint2*>(bias + (int64_t)e * N + n) : make_uint2(0, 0);
+      const int n = n0 + wn * (TNO / WN) + i * 32 + 8 * g4 + 4 * half;
+      bb[g4] = !GATED && bias && n < N ? *reinterpret_cast<const uint2*>(bias + (int64_t)e * N + n)
+                                       : make_uint2(0, 0);
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -352,15 +384,23 @@ __device__ __forceinline__ void gemm_tile(
       const int tl = wm * (TM / WM) + j * 32 + r32;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int fl = wn * (TN / WN) + i * 32 + 8 * g4 + 4 * half;
+        const int fl = wn * (TNO / WN) + i * 32 + 8 * g4 + 4 * half;
         float v[4];
-        v[0] = acc[i][j][4 * g4 + 0] + __uint_as_float(bb[g4].x << 16);
-        v[1] = acc[i][j][4 * g4 + 1] + __uint_as_float(bb[g4].x & 0xFFFF0000u);
-        v[2] = acc[i][j][4 * g4 + 2] + __uint_as_float(bb[g4].y << 16);
-        v[3] = acc[i][j][4 * g4 + 3] + __uint_as_float(bb[g4].y & 0xFFFF0000u);
-        if (SILU) {
+        if (GATED) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = v[u] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u]));
+          for (int u = 0; u < 4; ++u) {
+            const float gt = acc[i][j][4 * g4 + u], up = acc[i + FNO][j][4 * g4 + u];
+            v[u] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+        } else {
+          v[0] = acc[i][j][4 * g4 + 0] + __uint_as_float(bb[g4].x << 16);
+          v[1] = acc[i][j][4 * g4 + 1] + __uint_as_float(bb[g4].x & 0xFFFF0000u);
+          v[2] = acc[i][j][4 * g4 + 2] + __uint_as_float(bb[g4].y << 16);
+          v[3] = acc[i][j][4 * g4 + 3] + __uint_as_float(bb[g4].y & 0xFFFF0000u);
+          if (ACT == kActSilu) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = v[u] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u]));
+          }
         }
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
@@ -370,8 +410,8 @@ __device__ __forceinline__ void gemm_tile(
     }
   }
   __syncthreads();
-  constexpr int kChunksPerRow = TN / 8;
-  const int ncols = min(TN, N - n0);
+  constexpr int kChunksPerRow = TNO / 8;
+  const int ncols = min(TNO, N - n0);
   for (int c = threadIdx.x; c < rows * kChunksPerRow; c += kThreads) {
     const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
     if (ch * 8 < ncols)
@@ -388,14 +428,15 @@ __device__ __forceinline__ void gemm_tile(
 // better, so the shorter height must win by 15 %).  The result does not depend on the choice:
 // each output element accumulates the same products in the same K order.
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          bool SILU>
+          int ACT>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, int E, int N, int K, int a_rows,
     int slots) {
   const int lane = threadIdx.x & 63;
-  const int NT = (N + TN - 1) / TN;
+  constexpr int TNO = ACT == kActGated ? TN / 2 : TN;  // output features per tile
+  const int NT = (N + TNO - 1) / TNO;
   const TokenTiles<TMA> ta(offsets, E, lane);
   bool use_b = false;
   if constexpr (TMB > 0) {
@@ -407,16 +448,16 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       int mt, nt, e, row0, rows;
       if (!tile_of_block(tb.MT, NT, mt, nt)) return;
       tb.locate(offsets, lane, mt, e, row0, rows);
-      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, SILU>(A, row_token, W, bias, out, N, K,
-                                                            a_rows, e, row0, rows, nt * TN);
+      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT>(A, row_token, W, bias, out, N, K,
+                                                           a_rows, e, row0, rows, nt * TNO);
       return;
     }
   }
   int mt, nt, e, row0, rows;
   if (!tile_of_block(ta.MT, NT, mt, nt)) return;
   ta.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, SILU>(A, row_token, W, bias, out, N, K, a_rows,
-                                                        e, row0, rows, nt * TN);
+  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT>(A, row_token, W, bias, out, N, K, a_rows,
+                                                       e, row0, rows, nt * TNO);
 }
 
 namespace {
@@ -442,7 +483,7 @@ int compute_units() {
 }
 
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          bool SILU>
+          int ACT>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st) {
@@ -451,7 +492,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS) : 0;
   constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, SILU>;
+  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -462,7 +503,8 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   // upper bound on groups for the shorter tile height: token tiles <= rows_ub / TM + E
   constexpr int tm_min = TMB > 0 && TMB < TMA ? TMB : TMA;
   const int64_t mt_ub = (rows_ub + tm_min - 1) / tm_min + E;
-  const int64_t nt = (N + TN - 1) / TN;
+  constexpr int TNO = ACT == kActGated ? TN / 2 : TN;
+  const int64_t nt = (N + TNO - 1) / TNO;
   const int64_t nq = (nt + kGroupN - 1) / kGroupN;
   const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
   const int64_t grid = (ng_ub + 7) / 8 * 256;
@@ -494,10 +536,10 @@ hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_t
   if (s.dtype != MOE_BF16)
     return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, rows_ub, st);
   if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, true>(
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActSilu>(
         (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
         s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, true>(
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActSilu>(
       (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
       s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
 }
@@ -507,11 +549,40 @@ hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* off
                            hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, rows_ub, st);
   if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, false>(
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, kActNone>(
         (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
         s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, false>(
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, kActNone>(
       (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
+      s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
+}
+
+// Gated expert (fused-MoE flow diagram, GEMM 1 -> SiLU x mul -> GEMM 2): GEMM 1 over the
+// [2 d_ff, d_model] weights of each expert, gate rows first, with SiLU(gate) * up fused into
+// the epilogue; no biases.  Output H [rows, d_ff].
+hipError_t launch_ffn_up_gated(const moe_shape& s, const void* x, const int32_t* row_token,
+                               const int32_t* offsets, const void* w13, void* h, int64_t rows_ub,
+                               hipStream_t st) {
+  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
+  if (skinny(s, rows_ub))
+    return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, true, kActGated>(
+        (const bf16_t*)x, row_token, offsets, (const bf16_t*)w13, nullptr, (bf16_t*)h,
+        s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActGated>(
+      (const bf16_t*)x, row_token, offsets, (const bf16_t*)w13, nullptr, (bf16_t*)h,
+      s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
+}
+
+// GEMM 2 without bias (gated expert): Y = H W2^T
+hipError_t launch_ffn_down_nobias(const moe_shape& s, const void* h, const int32_t* offsets,
+                                  const void* w2, void* y, int64_t rows_ub, hipStream_t st) {
+  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
+  if (skinny(s, rows_ub))
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, kActNone>(
+        (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, nullptr, (bf16_t*)y,
+        s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, kActNone>(
+      (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, nullptr, (bf16_t*)y,
       s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
 }
 

@@ -77,6 +77,14 @@ hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* off
                            const void* w2, const void* b2, void* y, int64_t rows_ub,
                            hipStream_t st);
 
+// gated expert: H = SiLU(x W_gate^T) * (x W_up^T) with W13 [E, 2 d_ff, d_model] (gate rows
+// first), then Y = H W2^T; no biases; bf16 only
+hipError_t launch_ffn_up_gated(const moe_shape& s, const void* x, const int32_t* row_token,
+                               const int32_t* offsets, const void* w13, void* h, int64_t rows_ub,
+                               hipStream_t st);
+hipError_t launch_ffn_down_nobias(const moe_shape& s, const void* h, const int32_t* offsets,
+                                  const void* w2, void* y, int64_t rows_ub, hipStream_t st);
+
 // compact slots -> padded fixed buffers: slot_of (in place) becomes e * cap + rank, the padded
 // row tokens (-1 for unused rows) and the padded offsets e * cap are written
 hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32_t* offsets,

@@ -27,9 +27,10 @@ def upload(inputs: dict, device="cuda:0") -> dict:
 
 
 def shape_of(dev: dict, top_k: int, capacity: int) -> B.MoeShape:
-    x, w1 = dev["x"], dev["w1"]
+    x, w2 = dev["x"], dev["w2"]
     dtype = B.MOE_BF16 if x.dtype == torch.bfloat16 else B.MOE_F32
-    return B.make_shape(x.shape[0], x.shape[1], w1.shape[1], w1.shape[0], top_k, capacity, dtype)
+    # d_ff is the activation width: W2 [E, d_model, d_ff] for both expert kinds
+    return B.make_shape(x.shape[0], x.shape[1], w2.shape[2], w2.shape[0], top_k, capacity, dtype)
 
 
 def workspace(shape: B.MoeShape, device="cuda:0") -> torch.Tensor:
@@ -87,6 +88,28 @@ def layer_forward_padded(dev: dict, top_k: int, capacity: int, ws: torch.Tensor 
                                topk_gates=res["gates"], slot_of=res["slot_of"],
                                drop_mask=res["drop_mask"], expert_counts=res["counts"],
                                y_rows=res["y_rows"], ws=ws, events=events)
+    return res
+
+
+def layer_forward_gated(dev: dict, top_k: int, capacity: int, ws: torch.Tensor | None = None,
+                        events=None) -> dict:
+    """Whole layer with gated experts (dev["w1"] is W13 [E, 2 d_ff, d_model], no biases)."""
+    shape = shape_of(dev, top_k, capacity)
+    device = dev["x"].device
+    T, E = shape.T, shape.n_experts
+    ws = workspace(shape, device) if ws is None else ws
+    res = {
+        "out": torch.empty_like(dev["x"]),
+        "ids": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "slot_of": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "drop_mask": torch.empty((T, top_k), dtype=torch.uint8, device=device),
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+    }
+    B.moe_layer_forward_gated(shape, dev["x"], dev["w_router"], dev["b_router"], dev["w1"],
+                              dev["w2"], res["out"], topk_ids=res["ids"], topk_gates=res["gates"],
+                              slot_of=res["slot_of"], drop_mask=res["drop_mask"],
+                              expert_counts=res["counts"], ws=ws, events=events)
     return res
 
 

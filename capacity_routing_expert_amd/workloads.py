@@ -30,6 +30,7 @@ class Workload:
     dtype: str         # "f32" or "bf16"
     router_bias: str   # "none" | "normal" | "zipf" | "hot"
     weight_bias_std: float | None  # None -> N(0, 1/sqrt(fan_in)) for biases too
+    expert: str = "ffn"  # "ffn": W2 SiLU(W1 x + b1) + b2; "gated": W2 (SiLU(W_gate x) * W_up x)
 
 
 WORKLOADS = {
@@ -48,6 +49,10 @@ WORKLOADS = {
     # bf16, T 32768, d 4096, d_ff 14336, 8 experts, top-2, C 2.0 (capacity 16384), +2.5 hot expert
     "collapse": Workload("collapse", "collapse_bf16_T32768_d4096_f14336_E8_top2_C2.0", 4,
                          32768, 4096, 14336, 8, 2, 2.0, "bf16", "hot", 0.02),
+    # gated experts with the fused-MoE flow diagram's widths (d_model 2048, GEMM 1 out 2 x 768),
+    # the mid layer's routing: bf16, T 4096, 8 experts, top-2, C 1.25 (capacity 1280), no biases
+    "gated": Workload("gated", "gated_bf16_T4096_d2048_f768_E8_top2_C1.25", 5,
+                      4096, 2048, 768, 8, 2, 1.25, "bf16", "normal", None, "gated"),
 }
 
 
@@ -120,6 +125,16 @@ def make_inputs(wl: Workload | str, seed: int | None = None, T: int | None = Non
         raise ValueError(wl.router_bias)
 
     sdt = np.uint16 if wl.dtype == "bf16" else np.float32
+    if wl.expert == "gated":
+        # per expert: W13[e] [2f, d] (gate rows, then up rows), then W2[e] [d, f]; no biases
+        w1 = np.empty((E, 2 * f, d), dtype=sdt)
+        w2 = np.empty((E, d, f), dtype=sdt)
+        for e in range(E):
+            w1[e] = _store(_normal(rng, (2 * f, d), 1.0 / math.sqrt(d)), wl.dtype)
+            w2[e] = _store(_normal(rng, (d, f), 1.0 / math.sqrt(f)), wl.dtype)
+        return {"x": _store(x, wl.dtype), "w_router": _store(w_router, wl.dtype),
+                "b_router": b_router, "w1": w1, "b1": None, "w2": w2, "b2": None,
+                "dtype": wl.dtype, "T": T, "workload": wl}
     w1 = np.empty((E, f, d), dtype=sdt)
     b1 = np.empty((E, f), dtype=sdt)
     w2 = np.empty((E, d, f), dtype=sdt)
@@ -143,11 +158,12 @@ def make_inputs(wl: Workload | str, seed: int | None = None, T: int | None = Non
 
 def make_shape_inputs(T: int, d: int, f: int, E: int, dtype: str, seed: int,
                       router_bias_std: float = 0.0, bias_std: float = 0.02,
-                      x_values: tuple | None = None) -> dict:
+                      x_values: tuple | None = None, gated: bool = False) -> dict:
     """Inputs of an arbitrary small shape for randomized tests.
 
     With `x_values` given, x and the router weights are drawn from that finite set of
-    values (used to force exact gate ties).
+    values (used to force exact gate ties).  With `gated`, w1 is W13 [E, 2f, d] (gate rows
+    first) and there are no biases.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if x_values is not None:
@@ -160,6 +176,14 @@ def make_shape_inputs(T: int, d: int, f: int, E: int, dtype: str, seed: int,
     b_router = (rng.standard_normal(E).astype(np.float32) * np.float32(router_bias_std)
                 if router_bias_std > 0 else None)
     sdt = np.uint16 if dtype == "bf16" else np.float32
+    if gated:
+        w1 = np.empty((E, 2 * f, d), dtype=sdt)
+        w2 = np.empty((E, d, f), dtype=sdt)
+        for e in range(E):
+            w1[e] = _store(_normal(rng, (2 * f, d), 1.0 / math.sqrt(d)), dtype)
+            w2[e] = _store(_normal(rng, (d, f), 1.0 / math.sqrt(f)), dtype)
+        return {"x": _store(x, dtype), "w_router": _store(w_router, dtype), "b_router": b_router,
+                "w1": w1, "b1": None, "w2": w2, "b2": None, "dtype": dtype, "T": T}
     w1 = np.empty((E, f, d), dtype=sdt)
     b1 = np.empty((E, f), dtype=sdt)
     w2 = np.empty((E, d, f), dtype=sdt)

@@ -196,6 +196,24 @@ moe_status moe_layer_forward_padded(const moe_shape* shape, const void* x, const
                                     size_t ws_bytes, moe_stream_t stream,
                                     moe_event_t const* events);
 
+/* ---- Gated expert.  Fused-MoE flow diagram (moe-vllm flow): GEMM 1 writes two halves per
+ * row, the SiLU x mul box turns them into one, GEMM 2 follows; the diagram shows no biases.
+ * Reading taken: the first half is the gate, the second the up projection, so each expert is
+ *   y = W2 (SiLU(W_gate x) * (W_up x))       (element-wise product, no biases)
+ * with SiLU(gate) * up fused into GEMM 1's epilogue.
+ *   w13 [E, 2 * d_ff, d_model] dtype: rows 0 .. d_ff - 1 of expert e are W_gate, rows d_ff ..
+ *       2 d_ff - 1 are W_up;  w2 [E, d_model, d_ff].
+ * Routing, capacity, dispatch and combine (with the residual) as moe_layer_forward; shape.d_ff
+ * is the width of the product (the activation), the workspace is moe_workspace_bytes(shape);
+ * events NULL or 6 hipEvent_t as in moe_layer_forward_profiled.  bf16 only:
+ * MOE_ERR_UNSUPPORTED for fp32 and when 2 * d_ff * d_model weights per expert reach 2 GiB. */
+moe_status moe_layer_forward_gated(const moe_shape* shape, const void* x, const void* w_router,
+                                   const float* b_router, const void* w13, const void* w2,
+                                   void* out, int32_t* topk_ids, float* topk_gates,
+                                   int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts,
+                                   void* ws, size_t ws_bytes, moe_stream_t stream,
+                                   moe_event_t const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,9 @@ __all__ = [
     "expert_ffn_slots",
     "combine",
     "forward",
+    "expert_ffn_gated",
+    "expert_ffn_slots_gated",
+    "forward_gated",
     "dispatch_padded",
     "expert_ffn_padded",
     "forward_padded",
@@ -325,3 +328,52 @@ def forward_padded(x, w_router, b_router, w1, b1, w2, b2, k: int, capacity_facto
     return {"ids": r["ids"], "gates": r["gates"], "cap": cap, "slot_of": d["slot_of"],
             "row_token": d["row_token"], "counts": d["counts"], "Y": Y, "out": out,
             "all_dropped": all_dropped}
+
+
+def expert_ffn_gated(x_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """Gated expert of the fused-MoE flow diagram (moe-vllm flow): GEMM 1 writes 2f values
+    per row, the SiLU x mul box turns them into f, GEMM 2 follows; no biases are drawn.
+    Reading taken: the first f outputs of GEMM 1 are the gate, the last f the up projection.
+
+        g = W_gate x,  u = W_up x,  a = SiLU(g) * u,  y = W2 a
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    w13 = np.asarray(w13, dtype=np.float64)
+    f = w13.shape[0] // 2
+    g = x_rows @ w13[:f].T
+    u = x_rows @ w13[f:].T
+    a = silu(g) * u
+    return a @ np.asarray(w2, dtype=np.float64).T
+
+
+def expert_ffn_slots_gated(x, row_token, offsets, w13, w2, slots=None) -> np.ndarray:
+    """expert_ffn_slots with the gated expert."""
+    offsets = np.asarray(offsets)
+    E = len(offsets) - 1
+    if slots is None:
+        slots = np.arange(int(offsets[-1]))
+    slots = np.asarray(slots, dtype=np.int64)
+    out = np.zeros((len(slots), x.shape[1]), dtype=np.float64)
+    expert_of = np.searchsorted(offsets, slots, side="right") - 1
+    for e in range(E):
+        sel = np.nonzero(expert_of == e)[0]
+        if len(sel):
+            rows = np.asarray(x, dtype=np.float64)[np.asarray(row_token)[slots[sel]]]
+            out[sel] = expert_ffn_gated(rows, w13[e], w2[e])
+    return out
+
+
+def forward_gated(x, w_router, b_router, w13, w2, k: int, capacity_factor: float) -> dict:
+    """Whole layer with gated experts: route, capacity, dispatch, gated expert FFN, combine."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    cap = capacity(T, k, E, capacity_factor)
+    disp = dispatch(r["ids"], r["gates"], E, cap)
+    Y = expert_ffn_slots_gated(x, disp["row_token"], disp["offsets"], w13, w2)
+    out, all_dropped = combine(x, r["gates"], disp["slot_of"], Y)
+    res = dict(disp)
+    res.update({"ids": r["ids"], "gates": r["gates"], "cap": cap, "Y": Y, "out": out,
+                "all_dropped": all_dropped, "logits": r["logits"], "probs": r["probs"],
+                "gates_all": r["gates_all"]})
+    return res

@@ -16,6 +16,8 @@ What pins what:
     enumerating all k-subsets; slot ranks by an independent counting definition;
   * invariants: counts sum to T*k, slot map is a bijection, kept gates dominate dropped
     gates, permutation equivariance, capacity 0 returns the input;
+  * the gated expert: SiLU(ln 3) = (3/4) ln 3 through a gate and an up row, a zero gate
+    gives zero, torch float64 linear/SiLU for the expert and the layer;
   * the padded fixed buffers: the worked example's batches in their buffers with one empty
     slot, an empty slot's output b2 exactly when b1 = 0 (SiLU(0) = 0), the same layer output
     as the compact layout.
@@ -461,6 +463,55 @@ def check_padded_same_layer(o):
                     assert p["slot_of"][t, c] == e * cap + a["slot_of"][t, c] - a["offsets"][e]
 
 
+# ----------------------------------------------------------------------------- gated expert
+def _torch_gated(x_rows, w13, w2):
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    f = np.asarray(w13).shape[0] // 2
+    g = F.linear(t(x_rows), t(w13)[:f])
+    u = F.linear(t(x_rows), t(w13)[f:])
+    return F.linear(F.silu(g) * u, t(w2)).numpy()
+
+
+def check_gated_closed_forms(o):
+    """SiLU(ln 3) = (3/4) ln 3, so with one input, gate and up rows of 1 and W2 = 1 the
+    expert returns (3/4) (ln 3)^2; a zero gate gives exactly zero (SiLU(0) = 0)."""
+    x = np.array([[math.log(3.0)]])
+    y = o.expert_ffn_gated(x, np.array([[1.0], [1.0]]), np.array([[1.0]]))
+    assert abs(y[0, 0] - 0.75 * math.log(3.0) ** 2) < 1e-15
+    rng = _rng(59)
+    d, f = 5, 3
+    w13 = rng.standard_normal((2 * f, d)); w13[:f] = 0.0
+    y = o.expert_ffn_gated(rng.standard_normal((4, d)), w13, rng.standard_normal((d, f)))
+    assert np.array_equal(y, np.zeros_like(y))
+    # gate and up halves are not interchangeable: a negative gate with a positive up differs
+    x = np.array([[-2.0]])
+    y = o.expert_ffn_gated(x, np.array([[1.0], [-1.0]]), np.array([[1.0]]))  # g = -2, u = 2
+    assert abs(y[0, 0] - (-2.0 / (1.0 + math.exp(2.0))) * 2.0) < 1e-15
+
+
+def check_gated_vs_torch(o):
+    """The gated expert against torch's float64 linear and SiLU, and the whole gated layer
+    against a per-token recomputation with that reference."""
+    rng = _rng(61)
+    T, d, f, E, k = 16, 6, 5, 4, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w13 = rng.standard_normal((E, 2 * f, d)) / math.sqrt(d)
+    w2 = rng.standard_normal((E, d, f)) / math.sqrt(f)
+    for e in range(E):
+        got = o.expert_ffn_gated(x, w13[e], w2[e])
+        assert np.max(np.abs(got - _torch_gated(x, w13[e], w2[e]))) < 1e-13
+    res = o.forward_gated(x, w, None, w13, w2, k, 1.0)
+    for t in range(T):
+        want = x[t].copy()
+        for c in range(k):
+            if res["slot_of"][t, c] >= 0:
+                e = res["ids"][t, c]
+                want = want + float(res["gates"][t, c]) * _torch_gated(x[t:t + 1], w13[e], w2[e])[0]
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+
+
 ALL_CHECKS = [
     check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
     check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
@@ -468,5 +519,6 @@ ALL_CHECKS = [
     check_permutation_equivariance, check_silu_closed_forms, check_expert_ffn_vs_torch,
     check_worked_example_outputs, check_dense_special_case, check_dropless_per_token,
     check_all_experts, check_capacity_zero, check_padded_worked_example,
-    check_padded_empty_rows, check_padded_same_layer,
+    check_padded_empty_rows, check_padded_same_layer, check_gated_closed_forms,
+    check_gated_vs_torch,
 ]

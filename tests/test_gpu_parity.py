@@ -433,3 +433,70 @@ def test_padded_matches_compact(key):
         assert P.max_abs_rel(got, Y) <= P.TOL[dt]
     del dev, a, p
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- gated expert
+GATED_SMALL = [
+    # T, d, f, E, k, C   (bf16; skinny and large GEMM tiles, ragged d_ff and K tails)
+    (7, 72, 136, 2, 2, 1.0),
+    (65, 264, 328, 8, 2, 1.25),
+    (1000, 136, 72, 8, 3, 1.0),
+    (517, 256, 264, 5, 1, 8.0),
+    (300, 128, 200, 16, 4, 0.25),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,C", GATED_SMALL)
+def test_gated_small_shapes(T, d, f, E, k, C):
+    """moe_layer_forward_gated against the oracle's gated layer: routing, slots, every output
+    row, and bit copies for tokens with every choice dropped."""
+    inp = W.make_shape_inputs(T, d, f, E, "bf16", seed=T * 13 + E, router_bias_std=1.0, gated=True)
+    f64 = lambda a: W.to_float64(a, "bf16")
+    dev = L.upload(inp, DEV)
+    cap = O.capacity(T, k, E, C)
+    res = L.layer_forward_gated(dev, k, cap)
+    ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
+    full = O.forward_gated(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], f64(inp["w1"]),
+                           f64(inp["w2"]), k, C)
+    P.compare_route(ids, gates, full)
+    dref = O.dispatch(ids, gates, E, cap)
+    P.compare_dispatch(res, dref)
+    Y = O.expert_ffn_slots_gated(f64(inp["x"]), dref["row_token"], dref["offsets"], f64(inp["w1"]),
+                                 f64(inp["w2"]))
+    out_ref, all_dropped = O.combine(f64(inp["x"]), gates, dref["slot_of"], Y)
+    assert P.max_abs_rel(P.to_np(res["out"]), out_ref) <= P.TOL["bf16"]
+    for t in np.nonzero(all_dropped)[0]:
+        assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
+
+
+def test_gated_config_end_to_end():
+    """The gated workload at full size: routing and dispatch exact, sampled outputs."""
+    inp = W.make_inputs("gated")
+    wl = inp["workload"]
+    cap = O.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
+    dt = inp["dtype"]
+    ref = O.route(W.to_float64(inp["x"], dt), W.to_float64(inp["w_router"], dt), inp["b_router"],
+                  wl.top_k)
+    dev = L.upload(inp, DEV)
+    res = L.layer_forward_gated(dev, wl.top_k, cap)
+    ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
+    P.compare_route(ids, gates, ref)
+    dref = O.dispatch(ids, gates, wl.n_experts, cap)
+    P.compare_dispatch(res, dref)
+    rng = np.random.default_rng(7)
+    kept_any = np.nonzero(np.any(dref["slot_of"] >= 0, axis=1))[0]
+    sample = rng.choice(kept_any, size=min(128, len(kept_any)), replace=False)
+    x64 = W.to_float64(inp["x"][sample], dt)
+    want = x64.copy()
+    w13, w2 = F64(inp["w1"], dt), F64(inp["w2"], dt)
+    for i, t in enumerate(sample):
+        for c in range(wl.top_k):
+            if dref["slot_of"][t, c] >= 0:
+                e = int(ids[t, c])
+                want[i] += float(gates[t, c]) * O.expert_ffn_gated(x64[i:i + 1], w13[e], w2[e])[0]
+    got = P.to_np(res["out"][torch.as_tensor(sample, device=DEV)])
+    err = P.max_abs_rel(got, want)
+    say(f"[gated] sampled out max-abs-rel {err:.3e} over {len(sample)} tokens")
+    assert err <= P.TOL[dt]
+    del dev, res
+    torch.cuda.empty_cache()

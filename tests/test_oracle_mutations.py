@@ -183,7 +183,27 @@ def _dispatch_padded_compact_rows(ids, gates, n_experts, cap):
     return d
 
 
+def _gated_halves_swapped(x_rows, w13, w2):
+    f = np.asarray(w13).shape[0] // 2
+    return _orig["expert_ffn_gated"](x_rows, np.concatenate([w13[f:], w13[:f]]), w2)
+
+
+def _gated_no_up(x_rows, w13, w2):
+    f = np.asarray(w13).shape[0] // 2
+    x_rows = np.asarray(x_rows, np.float64)
+    return O.silu(x_rows @ np.asarray(w13)[:f].T) @ np.asarray(w2).T
+
+
+def _gated_silu_after_mul(x_rows, w13, w2):
+    f = np.asarray(w13).shape[0] // 2
+    x_rows = np.asarray(x_rows, np.float64)
+    return O.silu((x_rows @ np.asarray(w13)[:f].T) * (x_rows @ np.asarray(w13)[f:].T)) @ np.asarray(w2).T
+
+
 MUTATIONS = {
+    "gated_halves_swapped": {"expert_ffn_gated": _gated_halves_swapped},
+    "gated_up_dropped": {"expert_ffn_gated": _gated_no_up},
+    "gated_silu_after_product": {"expert_ffn_gated": _gated_silu_after_mul},
     "padded_empty_slot_uses_last_token": {"expert_ffn_padded": _ffn_padded_minus_one_index},
     "padded_buffer_order_reversed": {"dispatch_padded": _dispatch_padded_reversed},
     "padded_rows_at_compact_offsets": {"dispatch_padded": _dispatch_padded_compact_rows},
