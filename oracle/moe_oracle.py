@@ -21,6 +21,10 @@ what a library primitive (matmul, sort) does internally:
     path and reach the next layer exactly as they entered.
   * "Dynamic Token Routing AI" (freenetmedia.pl), "How it works": a gating network
     scores each token and selects the expert(s).
+  * The fused-MoE flow diagram (monishver11.github.io, moe-vllm flow): the dropless
+    pair-order flow (GEMM 1 reads token row p // top_k and writes pair row p, GEMM 2
+    scales pair row p by its top-k weight, moe_sum adds a token's top_k consecutive
+    rows) and the gated expert (GEMM 1 of width 2 d_ff, then SiLU x mul).
 
 Where the pages leave a step open, the reading taken is stated in the docstring of
 the function that takes it (softmax over all experts, unrenormalised top-k gates,
@@ -56,6 +60,11 @@ __all__ = [
     "expert_ffn_padded",
     "forward_padded",
     "forward_with_routing",
+    "dispatch_pairs",
+    "moe_sum",
+    "forward_dropless_with_routing",
+    "forward_dropless",
+    "forward_dropless_gated",
 ]
 
 
@@ -376,4 +385,92 @@ def forward_gated(x, w_router, b_router, w13, w2, k: int, capacity_factor: float
     res.update({"ids": r["ids"], "gates": r["gates"], "cap": cap, "Y": Y, "out": out,
                 "all_dropped": all_dropped, "logits": r["logits"], "probs": r["probs"],
                 "gates_all": r["gates_all"]})
+    return res
+
+
+# ----------------------------------------------------------------------------- dropless flow
+def dispatch_pairs(ids: np.ndarray, n_experts: int) -> dict:
+    """Group the (token, choice) pairs by expert with no capacity at all.
+
+    Fused-MoE flow diagram (moe-vllm flow), note on the GEMM boxes: both GEMMs walk a list
+    of pair indices sorted by expert, so every block of rows uses one expert's weights.
+    Pair p = t * top_k + c is the c-th choice of token t (the diagram's pair order).
+    Reading taken: within an expert the pairs keep ascending p (a stable sort by expert).
+
+    Returns counts [E], offsets [E+1] (exclusive prefix of the counts), sorted_pairs [T*k]
+    (expert e's pairs at offsets[e] .. offsets[e+1] - 1) and row_token = sorted_pairs // k,
+    the token row GEMM 1 reads for each of them.
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    if np.any((flat < 0) | (flat >= n_experts)):
+        raise ValueError("expert id out of range")
+    groups = [np.nonzero(flat == e)[0] for e in range(n_experts)]  # ascending p
+    counts = np.array([len(g) for g in groups], dtype=np.int32)
+    offsets = np.zeros(n_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_pairs = (np.concatenate(groups) if groups else np.zeros(0, np.int64)).astype(np.int32)
+    return {"counts": counts, "offsets": offsets, "sorted_pairs": sorted_pairs,
+            "row_token": (sorted_pairs // k).astype(np.int32)}
+
+
+def moe_sum(rows: np.ndarray, k: int, residual: np.ndarray | None = None) -> np.ndarray:
+    """moe_sum box of the flow diagram: token t's output is the sum of pair rows
+    t*k .. t*k + k - 1 (pair order back to token order), plus the residual when given."""
+    rows = np.asarray(rows, dtype=np.float64)
+    T = rows.shape[0] // k
+    out = np.zeros((T, rows.shape[1])) if residual is None else np.asarray(residual, np.float64).copy()
+    for t in range(T):
+        for c in range(k):
+            out[t] = out[t] + rows[t * k + c]
+    return out
+
+
+def forward_dropless_with_routing(x, ids, gates, n_experts, expert) -> dict:
+    """Dropless pair-order flow from a given routing; `expert(e, x_rows)` is one expert on a
+    batch of token rows.
+
+    Fused-MoE flow diagram: GEMM 1 reads token row p // top_k and writes pair row p; every
+    step up to GEMM 2 stays in pair order; GEMM 2 writes pair row p multiplied by
+    topk_weights[p]; moe_sum adds the top_k rows of each token.  No pair is ever dropped.
+    Reading taken: the layer's output adds the residual as the worked example's tokens do
+    (x plus the confidence-weighted expert outputs), so with capacity for every pair this is
+    the capacity layer's output; the top-k weights are the unrenormalised gates.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    T, k = ids.shape
+    disp = dispatch_pairs(ids, n_experts)
+    weights = np.asarray(gates, dtype=np.float64).reshape(-1)  # topk_weights[p]
+    rows = np.zeros((T * k, x64.shape[1]))                      # cache3, pair order
+    off = disp["offsets"]
+    for e in range(n_experts):
+        pairs = disp["sorted_pairs"][off[e]:off[e + 1]].astype(np.int64)
+        if len(pairs) == 0:
+            continue
+        y = expert(e, x64[pairs // k])           # GEMM 1 reads row p // top_k ... GEMM 2
+        rows[pairs] = weights[pairs][:, None] * y  # GEMM 2 writes row p, times topk_weights[p]
+    out = moe_sum(rows, k, residual=x64)
+    res = dict(disp)
+    res.update({"ids": ids, "gates": gates, "pair_rows": rows, "out": out})
+    return res
+
+
+def forward_dropless(x, w_router, b_router, w1, b1, w2, b2, k: int) -> dict:
+    """Whole dropless layer with the plain expert (up-projection, SiLU, down-projection)."""
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    res = forward_dropless_with_routing(
+        x, r["ids"], r["gates"], E, lambda e, rows: expert_ffn(rows, w1[e], b1[e], w2[e], b2[e]))
+    res.update({"logits": r["logits"], "probs": r["probs"], "gates_all": r["gates_all"]})
+    return res
+
+
+def forward_dropless_gated(x, w_router, b_router, w13, w2, k: int) -> dict:
+    """Whole dropless layer with the gated expert: the flow diagram end to end."""
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    res = forward_dropless_with_routing(
+        x, r["ids"], r["gates"], E, lambda e, rows: expert_ffn_gated(rows, w13[e], w2[e]))
+    res.update({"logits": r["logits"], "probs": r["probs"], "gates_all": r["gates_all"]})
     return res

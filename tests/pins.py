@@ -20,7 +20,11 @@ What pins what:
     gives zero, torch float64 linear/SiLU for the expert and the layer;
   * the padded fixed buffers: the worked example's batches in their buffers with one empty
     slot, an empty slot's output b2 exactly when b1 = 0 (SiLU(0) = 0), the same layer output
-    as the compact layout.
+    as the compact layout;
+  * the dropless pair-order flow: a hand-sorted pair list, counting-sort invariants
+    (permutation, experts non-decreasing, pairs ascending inside an expert), moe_sum against
+    numpy's reshape-and-sum, each pair row and token output against torch float64 linear/SiLU
+    per token, and the capacity layer's output when the capacity holds every pair.
 """
 from __future__ import annotations
 
@@ -512,6 +516,98 @@ def check_gated_vs_torch(o):
         assert np.max(np.abs(res["out"][t] - want)) < 1e-13
 
 
+# ----------------------------------------------------------------------------- dropless flow
+def check_pairs_hand_example(o):
+    """Three tokens, top-2 over three experts, sorted by hand: pair p = t*2 + c.
+    ids [[1, 0], [0, 2], [2, 1]] -> expert 0 gets pairs 1, 2; expert 1 pairs 0, 5; expert 2
+    pairs 3, 4; GEMM 1 reads token rows p // 2."""
+    d = o.dispatch_pairs(np.array([[1, 0], [0, 2], [2, 1]], dtype=np.int32), 3)
+    assert list(d["counts"]) == [2, 2, 2]
+    assert list(d["offsets"]) == [0, 2, 4, 6]
+    assert list(d["sorted_pairs"]) == [1, 2, 0, 5, 3, 4]
+    assert list(d["row_token"]) == [0, 1, 0, 2, 1, 2]
+    # an expert nobody picked has an empty range
+    d = o.dispatch_pairs(np.array([[3], [0], [3]], dtype=np.int32), 4)
+    assert list(d["offsets"]) == [0, 1, 1, 1, 3] and list(d["sorted_pairs"]) == [1, 0, 2]
+
+
+def check_pairs_invariants(o):
+    """Counting-sort facts on random ids: a permutation of all pairs, experts in
+    non-decreasing order, ascending pairs inside each expert, counts = bincount."""
+    rng = _rng(67)
+    for T, k, E in ((37, 3, 5), (64, 2, 8), (5, 4, 4)):
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        d = o.dispatch_pairs(ids, E)
+        sp = np.asarray(d["sorted_pairs"], dtype=np.int64)
+        assert np.array_equal(np.sort(sp), np.arange(T * k))
+        e_of = ids.reshape(-1)[sp]
+        assert np.all(np.diff(e_of) >= 0)
+        assert np.array_equal(d["counts"], np.bincount(ids.reshape(-1), minlength=E))
+        for e in range(E):
+            seg = sp[d["offsets"][e]:d["offsets"][e + 1]]
+            assert np.all(ids.reshape(-1)[seg] == e) and np.all(np.diff(seg) > 0)
+        assert np.array_equal(d["row_token"], sp // k)
+
+
+def check_moe_sum(o):
+    """moe_sum adds rows t*k .. t*k + k - 1: numpy's reshape to [T, k, d] and sum over k."""
+    rng = _rng(71)
+    T, k, d = 7, 3, 5
+    rows = rng.standard_normal((T * k, d))
+    res = rng.standard_normal((T, d))
+    assert np.max(np.abs(o.moe_sum(rows, k) - rows.reshape(T, k, d).sum(axis=1))) < 1e-14
+    assert np.max(np.abs(o.moe_sum(rows, k, res) - res - rows.reshape(T, k, d).sum(axis=1))) < 1e-14
+
+
+def check_dropless_flow_vs_torch(o):
+    """Each pair row is topk_weight * expert(x[t]) and each token leaves as x[t] plus its k
+    pair rows, against a per-token recomputation with torch's float64 layers (plain and
+    gated experts); skewed router bias so one expert holds most pairs (nothing drops)."""
+    rng = _rng(73)
+    T, d, f, E, k = 14, 6, 7, 4, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    b = np.array([3.0, 0.0, -1.0, 0.5])
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    res = o.forward_dropless(x, w, b, w1, b1, w2, b2, k)
+    assert int(np.max(res["counts"])) > T * k // E  # skewed: a capacity of T*k/E would drop
+    for t in range(T):
+        want = x[t].copy()
+        for c in range(k):
+            e = res["ids"][t, c]
+            y = float(res["gates"][t, c]) * _torch_ffn(x[t:t + 1], w1[e], b1[e], w2[e], b2[e])[0]
+            assert np.max(np.abs(res["pair_rows"][t * k + c] - y)) < 1e-13
+            want = want + y
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+    w13 = rng.standard_normal((E, 2 * f, d)) / math.sqrt(d)
+    w2g = rng.standard_normal((E, d, f)) / math.sqrt(f)
+    res = o.forward_dropless_gated(x, w, b, w13, w2g, k)
+    for t in range(T):
+        want = x[t].copy()
+        for c in range(k):
+            e = res["ids"][t, c]
+            want = want + float(res["gates"][t, c]) * _torch_gated(x[t:t + 1], w13[e], w2g[e])[0]
+        assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+
+
+def check_dropless_is_capacity_without_drops(o):
+    """With a capacity that holds every pair (C = E gives cap = T*k) the capacity layer drops
+    nothing, and the dropless flow returns its output; pair row t*k + c is the gate times the
+    capacity layer's expert output in slot slot_of[t, c]."""
+    rng = _rng(79)
+    T, d, f, E, k = 18, 5, 6, 5, 3
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    a = o.forward(x, w, None, w1, b1, w2, b2, k, float(E))
+    p = o.forward_dropless(x, w, None, w1, b1, w2, b2, k)
+    assert not a["drop_mask"].any()
+    assert np.array_equal(a["ids"], p["ids"]) and np.array_equal(a["counts"], p["counts"])
+    assert np.max(np.abs(a["out"] - p["out"])) < 1e-13
+    for t in range(T):
+        for c in range(k):
+            want = float(a["gates"][t, c]) * a["Y"][a["slot_of"][t, c]]
+            assert np.max(np.abs(p["pair_rows"][t * k + c] - want)) < 1e-13
+
+
 ALL_CHECKS = [
     check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
     check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
@@ -520,5 +616,6 @@ ALL_CHECKS = [
     check_worked_example_outputs, check_dense_special_case, check_dropless_per_token,
     check_all_experts, check_capacity_zero, check_padded_worked_example,
     check_padded_empty_rows, check_padded_same_layer, check_gated_closed_forms,
-    check_gated_vs_torch,
+    check_gated_vs_torch, check_pairs_hand_example, check_pairs_invariants, check_moe_sum,
+    check_dropless_flow_vs_torch, check_dropless_is_capacity_without_drops,
 ]

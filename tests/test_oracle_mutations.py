@@ -200,7 +200,71 @@ def _gated_silu_after_mul(x_rows, w13, w2):
     return O.silu((x_rows @ np.asarray(w13)[:f].T) * (x_rows @ np.asarray(w13)[f:].T)) @ np.asarray(w2).T
 
 
+def _pairs_descending(ids, n_experts):
+    d = _orig["dispatch_pairs"](ids, n_experts)
+    sp = d["sorted_pairs"].copy()
+    for e in range(n_experts):
+        sp[d["offsets"][e]:d["offsets"][e + 1]] = sp[d["offsets"][e]:d["offsets"][e + 1]][::-1]
+    d.update(sorted_pairs=sp, row_token=sp // ids.shape[1])
+    return d
+
+
+def _pairs_row_mod(ids, n_experts):
+    d = _orig["dispatch_pairs"](ids, n_experts)
+    d.update(row_token=d["sorted_pairs"] % ids.shape[1])
+    return d
+
+
+def _moe_sum_token_major(rows, k, residual=None):
+    # rows taken as [k, T] (choice-major) instead of pair order t*k + c
+    rows = np.asarray(rows, np.float64)
+    T = rows.shape[0] // k
+    out = np.zeros((T, rows.shape[1])) if residual is None else np.asarray(residual, np.float64).copy()
+    for t in range(T):
+        for c in range(k):
+            out[t] = out[t] + rows[c * T + t]
+    return out
+
+
+def _moe_sum_no_residual(rows, k, residual=None):
+    return _orig["moe_sum"](rows, k)
+
+
+def _make_dropless(read_row=None, weight=True, weight_by_position=False):
+    def fwd(x, ids, gates, n_experts, expert):
+        x64 = np.asarray(x, np.float64)
+        T, k = ids.shape
+        disp = O.dispatch_pairs(ids, n_experts)
+        wts = np.asarray(gates, np.float64).reshape(-1)
+        rows = np.zeros((T * k, x64.shape[1]))
+        off = disp["offsets"]
+        for e in range(n_experts):
+            pairs = disp["sorted_pairs"][off[e]:off[e + 1]].astype(np.int64)
+            if len(pairs) == 0:
+                continue
+            src = (read_row or (lambda p, k: p // k))(pairs, k)
+            y = expert(e, x64[src])
+            if weight:
+                w = wts[np.arange(off[e], off[e + 1])] if weight_by_position else wts[pairs]
+                y = w[:, None] * y
+            rows[pairs] = y
+        out = O.moe_sum(rows, k, residual=x64)
+        res = dict(disp)
+        res.update({"ids": ids, "gates": gates, "pair_rows": rows, "out": out})
+        return res
+    return fwd
+
+
 MUTATIONS = {
+    "pairs_descending_within_expert": {"dispatch_pairs": _pairs_descending},
+    "pairs_row_token_mod_k": {"dispatch_pairs": _pairs_row_mod},
+    "moe_sum_choice_major_rows": {"moe_sum": _moe_sum_token_major},
+    "moe_sum_drops_residual": {"moe_sum": _moe_sum_no_residual},
+    "dropless_reads_row_p_mod_k": {
+        "forward_dropless_with_routing": _make_dropless(read_row=lambda p, k: p % k)},
+    "dropless_unweighted_rows": {"forward_dropless_with_routing": _make_dropless(weight=False)},
+    "dropless_weight_by_sorted_position": {
+        "forward_dropless_with_routing": _make_dropless(weight_by_position=True)},
     "gated_halves_swapped": {"expert_ffn_gated": _gated_halves_swapped},
     "gated_up_dropped": {"expert_ffn_gated": _gated_no_up},
     "gated_silu_after_product": {"expert_ffn_gated": _gated_silu_after_mul},
