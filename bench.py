@@ -11,7 +11,9 @@ router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), e
                  steps `value` is timed on carry none)
   cpu_baseline   the CPU oracle timed on this host on the same workload (a baseline only)
 Workload: the mid-size layer (T 4096, d_model 2048, d_ff 8192, 8 experts, top-2, capacity
-factor 1.25) unless --config names another.
+factor 1.25) unless --config names another.  --layout dropless times the dropless pair-order
+flow instead (no capacity: pair dispatch, pair-order GEMMs with the top-k weight applied in
+GEMM 2, moe_sum in place of the combine).
 """
 from __future__ import annotations
 
@@ -58,7 +60,7 @@ def traffic_from_profiles(kernel_tag: str, config_key: str):
     return kib * 1024.0
 
 
-def cpu_baseline(inp, wl, cap):
+def cpu_baseline(inp, wl, cap, dropless=False):
     """The oracle on this host: the whole layer on the same workload, repeated for about 10 s."""
     import oracle.moe_oracle as O
     from capacity_routing_expert_amd import workloads as W
@@ -84,7 +86,16 @@ def cpu_baseline(inp, wl, cap):
     while not times or (sum(times) < 10.0 and len(times) < 20):
         t0 = time.perf_counter()
         r = O.route(x, wr, inp["b_router"], wl.top_k)
-        if wl.expert == "gated":
+        if dropless:
+            if wl.expert == "gated":
+                w13, w2 = F64(inp["w1"]), F64(inp["w2"])
+                fn = lambda e, rows: O.expert_ffn_gated(rows, w13[e], w2[e])
+            else:
+                w1, b1, w2, b2 = (F64(inp[n]) for n in ("w1", "b1", "w2", "b2"))
+                fn = lambda e, rows: O.expert_ffn(rows, w1[e], b1[e], w2[e], b2[e])
+            O.forward_dropless_with_routing(x, r["ids"], r["gates"], wl.n_experts, fn)
+            res = {"n_kept": wl.T * wl.top_k}
+        elif wl.expert == "gated":
             disp = O.dispatch(r["ids"], r["gates"], wl.n_experts, cap)
             Y = O.expert_ffn_slots_gated(x, disp["row_token"], disp["offsets"], F64(inp["w1"]),
                                          F64(inp["w2"]))
@@ -113,9 +124,10 @@ def main():
     ap.add_argument("--config", default="mid",
                     help="worked_example | mid | fine | decode | collapse | gated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layout", default="compact", choices=["compact", "padded"],
+    ap.add_argument("--layout", default="compact", choices=["compact", "padded", "dropless"],
                     help="compact: the expert FFN runs over the kept rows only; padded: over "
-                         "every slot of the fixed per-expert buffers (n_experts x capacity rows)")
+                         "every slot of the fixed per-expert buffers (n_experts x capacity rows); "
+                         "dropless: no capacity, every (token, choice) pair in pair order")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -141,8 +153,13 @@ def main():
     d = L.upload(inp, dev)
     shape = L.shape_of(d, wl.top_k, cap)
     padded = args.layout == "padded"
-    ws = (torch.empty(max(B.workspace_bytes_padded(shape), 256), dtype=torch.uint8, device=dev)
-          if padded else L.workspace(shape, dev))
+    dropless = args.layout == "dropless"
+    if padded:
+        ws = torch.empty(max(B.workspace_bytes_padded(shape), 256), dtype=torch.uint8, device=dev)
+    elif dropless:
+        ws = L.workspace_dropless(shape, dev)
+    else:
+        ws = L.workspace(shape, dev)
     out = torch.empty_like(d["x"])
     counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
@@ -152,8 +169,20 @@ def main():
         print("the padded layout is built for the FFN expert only", file=sys.stderr)
         sys.exit(2)
 
-    def step():
+    def step_dropless(events=None):
         if gated:
+            B.moe_layer_forward_dropless_gated(shape, d["x"], d["w_router"], d["b_router"],
+                                               d["w1"], d["w2"], out, expert_counts=counts,
+                                               ws=ws, events=events)
+        else:
+            B.moe_layer_forward_dropless(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                         d["b1"], d["w2"], d["b2"], out, expert_counts=counts,
+                                         ws=ws, events=events)
+
+    def step():
+        if dropless:
+            step_dropless()
+        elif gated:
             B.moe_layer_forward_gated(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
                                       d["w2"], out, expert_counts=counts, ws=ws)
         elif padded:
@@ -164,7 +193,9 @@ def main():
                                 d["w2"], d["b2"], out, expert_counts=counts, ws=ws)
 
     def step_profiled(events):
-        if gated:
+        if dropless:
+            step_dropless(events)
+        elif gated:
             B.moe_layer_forward_gated(shape, d["x"], d["w_router"], d["b_router"], d["w1"],
                                       d["w2"], out, expert_counts=counts, ws=ws, events=events)
         elif padded:
@@ -209,7 +240,7 @@ def main():
                 for j, s in enumerate(STAGES)}
     step_ms = float(np.mean([evs[0].elapsed_time(evs[5]) for evs in evsets]))
     c = counts.cpu().numpy()
-    n_kept = int(np.minimum(c, cap).sum())
+    n_kept = int(c.sum()) if dropless else int(np.minimum(c, cap).sum())
     dm, ff = wl.d_model, wl.d_ff
     # kept rows only; a gated expert's first GEMM has 2 d_ff outputs (gate and up)
     gemm2_flop = 2.0 * n_kept * dm * ff
@@ -218,14 +249,20 @@ def main():
     dom = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
+    if dropless:
+        dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1 in pair order: row p // top_k in, "
+                                   "row p out)",
+                      "expert_down": "k_grouped_gemm (GEMM 2 in pair order: x topk_weights[p])"}[dom]
     gemm_flop = gemm1_flop if dom == "expert_up" else gemm2_flop
     achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
     # the committed counter summaries are of the compact layout's launches
-    traffic = None if padded else traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2",
-                                                        args.config)
+    traffic = None if padded or dropless else traffic_from_profiles(
+        "gemm1" if dom == "expert_up" else "gemm2", args.config)
 
     route_bytes = wl.T * dm * inp["x"].itemsize + wl.n_experts * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
-    combine_bytes = (2 * wl.T + n_kept) * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
+    # combine: x, the kept Y rows, out, gates + slots; moe_sum: x, the T * k pair rows, out, ids
+    combine_bytes = ((2 * wl.T + n_kept) * dm * inp["x"].itemsize
+                     + (4 if dropless else 8) * wl.T * wl.top_k)
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -249,7 +286,7 @@ def main():
         "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
         "config": {"workload": wl.name, "T": wl.T, "d_model": dm, "d_ff": ff,
                    "n_experts": wl.n_experts, "top_k": wl.top_k,
-                   "capacity_factor": wl.capacity_factor, "capacity": cap,
+                   "capacity_factor": wl.capacity_factor, "capacity": None if dropless else cap,
                    "layout": args.layout},
         "expert_gemm_tflops": (gemm1_flop + gemm2_flop) / expert_s / 1e12,
         "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
@@ -267,16 +304,17 @@ def main():
         "combine_GBps": combine_bytes / (stage_ms["combine"] / 1e3) / 1e9,
         "n_kept": n_kept,
         "expert_rows_computed": wl.n_experts * cap if padded else n_kept,
+        "combine_stage": "moe_sum over pair rows" if dropless else "combine (slot gather)",
         # FLOP rate of what the matrix cores executed (buffer rows included), padded layout
         "expert_gemm_tflops_executed": (3 if gated else 2) * 2.0
                                        * (wl.n_experts * cap if padded else n_kept) * dm * ff
                                        / expert_s / 1e12,
         "drop_rate": 1.0 - n_kept / (wl.T * wl.top_k),
-        "expert_rows": [int(v) for v in np.minimum(c, cap)],
+        "expert_rows": [int(v) for v in (c if dropless else np.minimum(c, cap))],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(inp, wl, cap)
+        res["cpu_baseline"] = cpu_baseline(inp, wl, cap, dropless)
     print(json.dumps(res), flush=True)
 
 

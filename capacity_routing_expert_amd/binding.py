@@ -25,7 +25,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_status_string",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
-           "moe_layer_forward_padded", "moe_layer_forward_gated")
+           "moe_layer_forward_padded", "moe_layer_forward_gated", "moe_workspace_bytes_dropless",
+           "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
+           "moe_layer_forward_dropless_gated")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,9 +71,31 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [SP, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_layer_forward_profiled.argtypes = L.moe_layer_forward.argtypes + [P]
+        L.moe_workspace_bytes_padded.argtypes = [SP]
+        L.moe_workspace_bytes_padded.restype = SZ
+        # shape, x, w_router, b_router, w1, b1, w2, b2, out, ids, gates, slot_of, drop, counts,
+        # y_rows, ws, ws_bytes, stream, events
+        L.moe_layer_forward_padded.argtypes = [SP] + [P] * 15 + [SZ, P, P]
+        # shape, x, w_router, b_router, w13, w2, out, ids, gates, slot_of, drop, counts, ws,
+        # ws_bytes, stream, events
+        L.moe_layer_forward_gated.argtypes = [SP] + [P] * 12 + [SZ, P, P]
+        L.moe_workspace_bytes_dropless.argtypes = [SP]
+        L.moe_workspace_bytes_dropless.restype = SZ
+        L.moe_dispatch_pairs.argtypes = [SP, P, P, P, P, P, P, SZ, P]
+        # shape, x, sorted_pairs, row_token, offsets, w1, b1, w2, b2, weights, gated, pair_rows,
+        # ws, ws_bytes, stream
+        L.moe_expert_ffn_pairs.argtypes = [SP] + [P] * 9 + [I32, P, P, SZ, P]
+        L.moe_sum.argtypes = [SP, P, P, P, P, P]
+        # shape, x, w_router, b_router, w1, b1, w2, b2, out, ids, gates, counts, pair_rows, ws,
+        # ws_bytes, stream, events
+        L.moe_layer_forward_dropless.argtypes = [SP] + [P] * 13 + [SZ, P, P]
+        # shape, x, w_router, b_router, w13, w2, out, ids, gates, counts, pair_rows, ws,
+        # ws_bytes, stream, events
+        L.moe_layer_forward_dropless_gated.argtypes = [SP] + [P] * 11 + [SZ, P, P]
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                     "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
-           "moe_layer_forward_padded", "moe_layer_forward_gated"):
+                     "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_padded",
+                     "moe_layer_forward_gated", "moe_dispatch_pairs", "moe_expert_ffn_pairs",
+                     "moe_sum", "moe_layer_forward_dropless", "moe_layer_forward_dropless_gated"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -93,6 +117,10 @@ def workspace_bytes(shape: MoeShape) -> int:
 
 def workspace_bytes_padded(shape: MoeShape) -> int:
     return int(lib().moe_workspace_bytes_padded(ctypes.byref(shape)))
+
+
+def workspace_bytes_dropless(shape: MoeShape) -> int:
+    return int(lib().moe_workspace_bytes_dropless(ctypes.byref(shape)))
 
 
 def max_kept_rows(shape: MoeShape) -> int:
@@ -243,3 +271,73 @@ def moe_layer_forward_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids
         _ptr(drop_mask, "drop_mask", torch.uint8), _ptr(expert_counts, "expert_counts", torch.int32),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), handles),
         "moe_layer_forward_gated")
+
+
+def _events(events):
+    if events is None:
+        return None
+    return (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+
+
+def moe_dispatch_pairs(shape, topk_ids, expert_counts, expert_offsets, sorted_pairs, row_token,
+                       ws, stream=None):
+    _check(lib().moe_dispatch_pairs(ctypes.byref(shape), _ptr(topk_ids, "topk_ids", torch.int32),
+                                    _ptr(expert_counts, "expert_counts", torch.int32),
+                                    _ptr(expert_offsets, "expert_offsets", torch.int32),
+                                    _ptr(sorted_pairs, "sorted_pairs", torch.int32),
+                                    _ptr(row_token, "row_token", torch.int32),
+                                    _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+           "moe_dispatch_pairs")
+
+
+def moe_expert_ffn_pairs(shape, x, sorted_pairs, row_token, expert_offsets, w1, b1, w2, b2,
+                         topk_weights, pair_rows, ws, gated=False, stream=None):
+    """gated: w1 is w13 [E, 2 d_ff, d_model] and b1, b2 are ignored (pass None)."""
+    dt = _dtype_of(shape)
+    _check(lib().moe_expert_ffn_pairs(
+        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(sorted_pairs, "sorted_pairs", torch.int32),
+        _ptr(row_token, "row_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", dt),
+        _ptr(b1, "b1", dt), _ptr(w2, "w2", dt), _ptr(b2, "b2", dt),
+        _ptr(topk_weights, "topk_weights", torch.float32), int(bool(gated)),
+        _ptr(pair_rows, "pair_rows", dt), _ptr(ws, "ws", torch.uint8), ws.numel(),
+        _stream(stream)), "moe_expert_ffn_pairs")
+
+
+def moe_sum(shape, x, topk_ids, pair_rows, out, stream=None):
+    """out[t] = (x[t] +) the sum of pair rows t*k .. t*k + k - 1; x and topk_ids may be None."""
+    dt = _dtype_of(shape)
+    _check(lib().moe_sum(ctypes.byref(shape), _ptr(x, "x", dt),
+                         _ptr(topk_ids, "topk_ids", torch.int32),
+                         _ptr(pair_rows, "pair_rows", dt), _ptr(out, "out", dt),
+                         _stream(stream)), "moe_sum")
+
+
+def moe_layer_forward_dropless(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
+                               topk_gates=None, expert_counts=None, pair_rows=None, ws=None,
+                               events=None, stream=None):
+    """Dropless pair-order layer; `pair_rows` [T * k, d_model] optional; `events` None or 6
+    recorded torch.cuda.Event(enable_timing=True)."""
+    dt = _dtype_of(shape)
+    _check(lib().moe_layer_forward_dropless(
+        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
+        _ptr(b_router, "b_router", torch.float32), _ptr(w1, "w1", dt), _ptr(b1, "b1", dt),
+        _ptr(w2, "w2", dt), _ptr(b2, "b2", dt), _ptr(out, "out", dt),
+        _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_gates, "topk_gates", torch.float32),
+        _ptr(expert_counts, "expert_counts", torch.int32), _ptr(pair_rows, "pair_rows", dt),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), _events(events)),
+        "moe_layer_forward_dropless")
+
+
+def moe_layer_forward_dropless_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids=None,
+                                     topk_gates=None, expert_counts=None, pair_rows=None,
+                                     ws=None, events=None, stream=None):
+    dt = _dtype_of(shape)
+    _check(lib().moe_layer_forward_dropless_gated(
+        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
+        _ptr(b_router, "b_router", torch.float32), _ptr(w13, "w13", dt), _ptr(w2, "w2", dt),
+        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
+        _ptr(topk_gates, "topk_gates", torch.float32),
+        _ptr(expert_counts, "expert_counts", torch.int32), _ptr(pair_rows, "pair_rows", dt),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), _events(events)),
+        "moe_layer_forward_dropless_gated")

@@ -78,8 +78,9 @@ moe_status check_ptr(const void* p, size_t a, const char* name) {
   return MOE_OK;
 }
 
-moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes, bool padded = false) {
-  const size_t need = layout(s, padded).total;
+moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes,
+                    LayoutKind kind = kLayoutCompact) {
+  const size_t need = layout(s, kind).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   if (need && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
@@ -106,12 +107,13 @@ int64_t max_rows(const moe_shape& s) {
   return a < b ? a : b;
 }
 
-Workspace layout(const moe_shape& s, bool padded) {
+Workspace layout(const moe_shape& s, LayoutKind kind) {
   Workspace w;
   const int64_t N = s.T * (int64_t)s.top_k;
   const int64_t E = s.n_experts;
   const int64_t nb = (N + kDispatchChunk - 1) / kDispatchChunk;
-  const int64_t rows = padded ? E * s.capacity : max_rows(s);
+  const bool padded = kind == kLayoutPadded, dropless = kind == kLayoutDropless;
+  const int64_t rows = padded ? E * s.capacity : dropless ? N : max_rows(s);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -120,15 +122,16 @@ Workspace layout(const moe_shape& s, bool padded) {
   };
   w.ids = take((size_t)N * 4);
   w.gates = take((size_t)N * 4);
-  w.slot_of = take((size_t)N * 4);
-  w.drop = take((size_t)N);
+  w.slot_of = take(dropless ? 0 : (size_t)N * 4);
+  w.drop = take(dropless ? 0 : (size_t)N);
   w.counts = take((size_t)E * 4);
   w.offsets = take((size_t)(E + 1) * 4);
-  w.seg_start = take((size_t)(E + 2) * 4);
+  w.seg_start = take(dropless ? 0 : (size_t)(E + 2) * 4);
   w.blk_hist = take((size_t)nb * (E + 1) * 4);
-  w.keys = take((size_t)N * 8);
-  w.rank = take((size_t)N * 4);
-  w.row_token = take((size_t)max_rows(s) * 4);
+  w.keys = take(dropless ? 0 : (size_t)N * 8);
+  w.rank = take(dropless ? 0 : (size_t)N * 4);
+  w.row_token = take((size_t)(dropless ? N : max_rows(s)) * 4);
+  w.pairs = take(dropless ? (size_t)N * 4 : 0);
   w.row_token_pad = take(padded ? (size_t)rows * 4 : 0);
   w.offsets_pad = take(padded ? (size_t)(E + 1) * 4 : 0);
   w.h = take((size_t)rows * s.d_ff * elem_bytes(s));
@@ -173,7 +176,7 @@ moe_status check_forward_args(const moe_shape* shape, const void* x, const void*
   if (padded && (int64_t)s.n_experts * s.capacity >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "n_experts * capacity = %lld >= 2^31",
                 (long long)((int64_t)s.n_experts * s.capacity));
-  MOE_TRY(check_ws(s, ws, ws_bytes, padded));
+  MOE_TRY(check_ws(s, ws, ws_bytes, padded ? kLayoutPadded : kLayoutCompact));
   return MOE_OK;
 }
 
@@ -206,7 +209,7 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
   if (slot_of) MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
   if (expert_counts) MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
-  const Workspace L = layout(s, padded);
+  const Workspace L = layout(s, padded ? kLayoutPadded : kLayoutCompact);
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
   int32_t* slots = slot_of ? slot_of : at<int32_t>(ws, L.slot_of);
@@ -246,6 +249,96 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   return MOE_OK;
 }
 
+// Dropless pair-order flow: checks shared by the layer call and the expert call.
+moe_status check_dropless(const moe_shape& s, bool gated) {
+  if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the dropless flow is bf16 only");
+  // GEMM 2 reads the pair rows of H with 32-bit byte offsets
+  if (s.T * (int64_t)s.top_k * s.d_ff * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * top_k * d_ff bf16 pair activations: >= 2 GiB");
+  if (gated && (int64_t)4 * s.d_ff * s.d_model >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "2 * d_ff * d_model bf16 weights per expert: >= 2 GiB");
+  return MOE_OK;
+}
+
+moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pairs,
+                     const int32_t* row_token, const int32_t* offsets, const void* w1,
+                     const void* b1, const void* w2, const void* b2, const float* weights,
+                     bool gated, void* h, void* pair_rows, hipStream_t st,
+                     moe_event_t const* events) {
+  const int64_t rows = s.T * (int64_t)s.top_k;
+  hipError_t err = launch_ffn_up_pairs(s, x, row_token, sorted_pairs, offsets, w1,
+                                       gated ? nullptr : b1, h, rows, gated, st);
+  if (err != hipSuccess) return device_error(err, "expert up-projection (pair order)");
+  if (events && (err = hipEventRecord((hipEvent_t)events[3], st)) != hipSuccess)
+    return device_error(err, "hipEventRecord");
+  err = launch_ffn_down_pairs(s, h, sorted_pairs, offsets, w2, gated ? nullptr : b2, weights,
+                              pair_rows, rows, st);
+  if (err != hipSuccess) return device_error(err, "expert down-projection (pair order)");
+  return MOE_OK;
+}
+
+moe_status layer_forward_dropless(const moe_shape* shape, const void* x, const void* w_router,
+                                  const float* b_router, const void* w1, const void* b1,
+                                  const void* w2, const void* b2, bool gated, void* out,
+                                  int32_t* topk_ids, float* topk_gates, int32_t* expert_counts,
+                                  void* pair_rows, void* ws, size_t ws_bytes, hipStream_t st,
+                                  moe_event_t const* events) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (events)
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  auto rec = [&](int i) -> moe_status {
+    if (!events) return MOE_OK;
+    hipError_t err = hipEventRecord((hipEvent_t)events[i], st);
+    return err == hipSuccess ? MOE_OK : device_error(err, "hipEventRecord");
+  };
+  if (s.T == 0) {  // empty batch: nothing to check or enqueue
+    for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
+    return MOE_OK;
+  }
+  MOE_TRY(check_dropless(s, gated));
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  MOE_TRY(check_data_ptr(s, w_router, "w_router"));
+  if (b_router) MOE_TRY(check_ptr(b_router, 4, "b_router"));
+  MOE_TRY(check_data_ptr(s, w1, "w1"));
+  MOE_TRY(check_data_ptr(s, w2, "w2"));
+  if (!gated) {
+    MOE_TRY(check_data_ptr(s, b1, "b1"));
+    MOE_TRY(check_data_ptr(s, b2, "b2"));
+  }
+  MOE_TRY(check_data_ptr(s, out, "out"));
+  if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
+  if (pair_rows) MOE_TRY(check_data_ptr(s, pair_rows, "pair_rows"));
+  if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  if (expert_counts) MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
+  MOE_TRY(check_ws(s, ws, ws_bytes, kLayoutDropless));
+  const Workspace L = layout(s, kLayoutDropless);
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
+  int32_t* counts = expert_counts ? expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pairs = at<int32_t>(ws, L.pairs);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  void* y = pair_rows ? pair_rows : at<void>(ws, L.y);
+
+  MOE_TRY(rec(0));
+  MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, st));
+  MOE_TRY(rec(1));
+  hipError_t err = launch_dispatch_pairs(s, ids, counts, offsets, pairs, row_token,
+                                         at<int32_t>(ws, L.blk_hist), st);
+  if (err != hipSuccess) return device_error(err, "pair dispatch");
+  MOE_TRY(rec(2));
+  MOE_TRY(ffn_pairs(s, x, pairs, row_token, offsets, w1, b1, w2, b2, gates, gated,
+                    at<void>(ws, L.h), y, st, events));
+  MOE_TRY(rec(4));
+  err = launch_moe_sum(s, x, ids, y, out, st);
+  if (err != hipSuccess) return device_error(err, "moe_sum");
+  MOE_TRY(rec(5));
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -280,7 +373,12 @@ size_t moe_workspace_bytes(const moe_shape* shape) {
 size_t moe_workspace_bytes_padded(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
   if ((int64_t)shape->n_experts * shape->capacity >= ((int64_t)1 << 31)) return 0;
-  return layout(*shape, true).total;
+  return layout(*shape, kLayoutPadded).total;
+}
+
+size_t moe_workspace_bytes_dropless(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return layout(*shape, kLayoutDropless).total;
 }
 
 int64_t moe_max_kept_rows(const moe_shape* shape) {
@@ -434,6 +532,93 @@ moe_status moe_layer_forward_gated(const moe_shape* shape, const void* x, const 
   return layer_forward(shape, x, w_router, b_router, w13, nullptr, w2, nullptr, out, topk_ids,
                        topk_gates, slot_of, drop_mask, expert_counts, ws, ws_bytes,
                        (hipStream_t)stream, events, false, nullptr, true);
+}
+
+moe_status moe_dispatch_pairs(const moe_shape* shape, const int32_t* topk_ids,
+                              int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_pairs, int32_t* row_token, void* ws,
+                              size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_ptr(sorted_pairs, 4, "sorted_pairs"));
+  MOE_TRY(check_ptr(row_token, 4, "row_token"));
+  MOE_TRY(check_ws(s, ws, ws_bytes, kLayoutDropless));
+  const Workspace L = layout(s, kLayoutDropless);
+  hipError_t err = launch_dispatch_pairs(s, topk_ids, expert_counts, expert_offsets, sorted_pairs,
+                                         row_token, at<int32_t>(ws, L.blk_hist),
+                                         (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(err, "pair dispatch");
+}
+
+moe_status moe_expert_ffn_pairs(const moe_shape* shape, const void* x,
+                                const int32_t* sorted_pairs, const int32_t* row_token,
+                                const int32_t* expert_offsets, const void* w1, const void* b1,
+                                const void* w2, const void* b2, const float* topk_weights,
+                                int32_t gated, void* pair_rows, void* ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  MOE_TRY(check_dropless(s, gated != 0));
+  MOE_TRY(check_data_ptr(s, x, "x"));
+  MOE_TRY(check_ptr(sorted_pairs, 4, "sorted_pairs"));
+  MOE_TRY(check_ptr(row_token, 4, "row_token"));
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_data_ptr(s, w1, "w1"));
+  MOE_TRY(check_data_ptr(s, w2, "w2"));
+  if (!gated) {
+    MOE_TRY(check_data_ptr(s, b1, "b1"));
+    MOE_TRY(check_data_ptr(s, b2, "b2"));
+  }
+  MOE_TRY(check_ptr(topk_weights, 4, "topk_weights"));
+  MOE_TRY(check_data_ptr(s, pair_rows, "pair_rows"));
+  MOE_TRY(check_ws(s, ws, ws_bytes, kLayoutDropless));
+  const Workspace L = layout(s, kLayoutDropless);
+  return ffn_pairs(s, x, sorted_pairs, row_token, expert_offsets, w1, b1, w2, b2, topk_weights,
+                   gated != 0, at<void>(ws, L.h), pair_rows, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_sum(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                   const void* pair_rows, void* out, moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  if (x) MOE_TRY(check_data_ptr(s, x, "x"));
+  if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_TRY(check_data_ptr(s, pair_rows, "pair_rows"));
+  MOE_TRY(check_data_ptr(s, out, "out"));
+  if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
+  if (out == pair_rows) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases pair_rows");
+  hipError_t err = launch_moe_sum(s, x, topk_ids, pair_rows, out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(err, "moe_sum");
+}
+
+moe_status moe_layer_forward_dropless(const moe_shape* shape, const void* x,
+                                      const void* w_router, const float* b_router,
+                                      const void* w1, const void* b1, const void* w2,
+                                      const void* b2, void* out, int32_t* topk_ids,
+                                      float* topk_gates, int32_t* expert_counts, void* pair_rows,
+                                      void* ws, size_t ws_bytes, moe_stream_t stream,
+                                      moe_event_t const* events) {
+  return layer_forward_dropless(shape, x, w_router, b_router, w1, b1, w2, b2, false, out,
+                                topk_ids, topk_gates, expert_counts, pair_rows, ws, ws_bytes,
+                                (hipStream_t)stream, events);
+}
+
+moe_status moe_layer_forward_dropless_gated(const moe_shape* shape, const void* x,
+                                            const void* w_router, const float* b_router,
+                                            const void* w13, const void* w2, void* out,
+                                            int32_t* topk_ids, float* topk_gates,
+                                            int32_t* expert_counts, void* pair_rows, void* ws,
+                                            size_t ws_bytes, moe_stream_t stream,
+                                            moe_event_t const* events) {
+  return layer_forward_dropless(shape, x, w_router, b_router, w13, nullptr, w2, nullptr, true,
+                                out, topk_ids, topk_gates, expert_counts, pair_rows, ws,
+                                ws_bytes, (hipStream_t)stream, events);
 }
 
 }  // extern "C"

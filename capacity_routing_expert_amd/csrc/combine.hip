@@ -164,6 +164,129 @@ __global__ __launch_bounds__(256) void k_combine_f32(const float* __restrict__ x
   }
 }
 
+// ---------------------------------------------------------------- moe_sum
+// moe_sum box of the fused-MoE flow diagram: pair order back to token order.  Token t leaves as
+// the sum of its pair rows t*k .. t*k + k - 1 (GEMM 2 has already multiplied each by its top-k
+// weight), plus the residual x[t] when one is given, summed in choice order in fp32 with one
+// rounding.  With ids given, a pair whose expert id is outside [0, E) has no row and adds
+// nothing; a token left with no row leaves as x[t] bit for bit (zeros without a residual).
+// Same stream shape as the combine: one wave per token, 16-byte loads, streaming stores; the
+// rows of a token are contiguous here, so no slot indirection.
+__global__ __launch_bounds__(256) void k_moe_sum_bf16(const bf16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ ids,
+                                                      const bf16_t* __restrict__ rows,
+                                                      bf16_t* __restrict__ out, int64_t T, int d,
+                                                      int k, int E) {
+  constexpr int kB = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nch = d / 8;
+  uint4* orow = reinterpret_cast<uint4*>(out + t * (int64_t)d);
+  int n = 0, c0 = 0, c1 = 0;  // rows present, first two of them (wave-uniform)
+  for (int c = 0; c < k; ++c) {
+    if (ids && (uint32_t)ids[t * k + c] >= (uint32_t)E) continue;
+    if (n == 0) c0 = c; else if (n == 1) c1 = c;
+    ++n;
+  }
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const bf16_t* prow = rows + t * (int64_t)k * d;
+  const __amdgpu_buffer_rsrc_t xb = row_rsrc(x ? x + t * (int64_t)d : rows, x ? row_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t y0 = row_rsrc(prow + (int64_t)c0 * d, n >= 1 ? row_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t y1 = row_rsrc(prow + (int64_t)c1 * d, n >= 2 ? row_bytes : 0u);
+  for (int base = lane; base < nch; base += 64 * kB) {
+    uint4 xv[kB], v0[kB], v1[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      xv[b] = load16(xb, base + 64 * b);
+      v0[b] = load16(y0, base + 64 * b);
+      v1[b] = load16(y1, base + 64 * b);
+    }
+    if (n == 0) {  // nothing to add: the residual (or zeros) bit for bit
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (base + 64 * b < nch) store_nt(xv[b], orow + base + 64 * b);
+      continue;
+    }
+    float acc[kB][8];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      float y[8];
+      widen8(xv[b], acc[b]);
+      widen8(v0[b], y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[b][i] += y[i];
+      if (n >= 2) {
+        widen8(v1[b], y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[b][i] += y[i];
+      }
+    }
+    if (n > 2) {  // further rows, in choice order
+      int seen = 0;
+      for (int c = 0; c < k; ++c) {
+        if (ids && (uint32_t)ids[t * k + c] >= (uint32_t)E) continue;
+        if (++seen <= 2) continue;
+        const __amdgpu_buffer_rsrc_t yc = row_rsrc(prow + (int64_t)c * d, row_bytes);
+        uint4 vc[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) vc[b] = load16(yc, base + 64 * b);
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          float y[8];
+          widen8(vc[b], y);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[b][i] += y[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      if (base + 64 * b >= nch) continue;
+      uint4 o;
+      o.x = pack_bf16x2(acc[b][0], acc[b][1]);
+      o.y = pack_bf16x2(acc[b][2], acc[b][3]);
+      o.z = pack_bf16x2(acc[b][4], acc[b][5]);
+      o.w = pack_bf16x2(acc[b][6], acc[b][7]);
+      store_nt(o, orow + base + 64 * b);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_moe_sum_f32(const float* __restrict__ x,
+                                                     const int32_t* __restrict__ ids,
+                                                     const float* __restrict__ rows,
+                                                     float* __restrict__ out, int64_t T, int d,
+                                                     int k, int E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float* orow = out + t * (int64_t)d;
+  const float* prow = rows + t * (int64_t)k * d;
+  for (int j = lane; j < d; j += 64) {
+    float acc = x ? x[t * (int64_t)d + j] : 0.0f;
+    for (int c = 0; c < k; ++c) {
+      if (ids && (uint32_t)ids[t * k + c] >= (uint32_t)E) continue;
+      acc += prow[(int64_t)c * d + j];
+    }
+    orow[j] = acc;
+  }
+}
+
+hipError_t launch_moe_sum(const moe_shape& s, const void* x, const int32_t* ids,
+                          const void* rows, void* out, hipStream_t st) {
+  const int64_t grid = (s.T + 3) / 4;
+  if (s.dtype == MOE_BF16)
+    hipLaunchKernelGGL(k_moe_sum_bf16, dim3((unsigned)grid), dim3(256), 0, st, (const bf16_t*)x,
+                       ids, (const bf16_t*)rows, (bf16_t*)out, s.T, s.d_model, s.top_k,
+                       s.n_experts);
+  else
+    hipLaunchKernelGGL(k_moe_sum_f32, dim3((unsigned)grid), dim3(256), 0, st, (const float*)x,
+                       ids, (const float*)rows, (float*)out, s.T, s.d_model, s.top_k,
+                       s.n_experts);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const moe_shape& s, const void* x, const float* gates,
                           const int32_t* slot_of, const void* y, void* out, hipStream_t st) {
   const int64_t grid = (s.T + 3) / 4;

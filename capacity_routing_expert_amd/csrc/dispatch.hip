@@ -429,6 +429,99 @@ hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- dropless pair grouping
+// Fused-MoE flow diagram (moe-vllm flow), note on the GEMM boxes: both GEMMs walk the pairs
+// sorted by expert so that every block uses one expert's weights; nothing is dropped.  Pair
+// p = t * k + c goes to position offsets[e] + #{q < p : ids[q] = e} (a stable counting sort
+// by expert id), with row_token = p / k beside it.  Pairs with ids outside [0, E) land after
+// offsets[E], where no GEMM tile reads.  Same wave-ballot ranking as k_dispatch_scatter; with
+// a single block (N <= kDispatchChunk) the block counts its own chunk, so no histogram kernel
+// runs before it.
+__global__ __launch_bounds__(256) void k_dispatch_pairs(
+    const int32_t* __restrict__ ids, int64_t N, int E, int k, int nb,
+    const int32_t* __restrict__ blk_hist, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ row_token) {
+  __shared__ int s_cnt[260], s_run[260];
+  __shared__ int wcnt[4][260];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kDispatchChunk;
+  for (int e = tid; e <= E; e += 256) {
+    s_cnt[e] = 0;
+    s_run[e] = 0;
+    for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  if (blk_hist) {  // totals and the prefix of the blocks before this one
+    for (int e = tid; e <= E; e += 256) {
+      int tot = 0, pre = 0;
+      for (int b = 0; b < nb; ++b) {
+        const int h = blk_hist[(int64_t)b * (E + 1) + e];
+        if (b < (int)blockIdx.x) pre += h;
+        tot += h;
+      }
+      s_cnt[e] = tot;
+      s_run[e] = pre;
+    }
+  } else {  // the only block: count its own chunk
+    for (int r = 0; r < kDispatchChunk / 256; ++r) {
+      const int64_t i = base + r * 256 + tid;
+      const bool valid = i < N;
+      int e = valid ? ids[i] : 0;
+      if (e < 0 || e >= E) e = E;
+      const uint64_t peers = match_key(e, valid);
+      if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&s_cnt[e], __popcll(peers));
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = s_cnt[e];
+  __syncthreads();
+  if (wave == 0) wave_exclusive_scan(s_cnt, E + 1, nullptr);  // bucket starts; [E] = valid pairs
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += 256) offsets[e] = s_cnt[e];
+  for (int e = tid; e <= E; e += 256) s_run[e] += s_cnt[e];
+  __syncthreads();
+  for (int r = 0; r < kDispatchChunk / 256; ++r) {
+    if (base + r * 256 >= N) break;  // block-uniform
+    const int64_t i = base + r * 256 + tid;
+    const bool valid = i < N;
+    int e = valid ? ids[i] : 0;
+    if (e < 0 || e >= E) e = E;
+    const uint64_t peers = match_key(e, valid);
+    const int wrank = __popcll(peers & lanemask_lt());
+    if (valid && wrank == 0) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = s_run[e] + wrank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      sorted_pairs[pos] = (int32_t)i;
+      row_token[pos] = (int32_t)(i / k);
+    }
+    __syncthreads();
+    for (int ee = tid; ee <= E; ee += 256) {
+      s_run[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
+      wcnt[0][ee] = wcnt[1][ee] = wcnt[2][ee] = wcnt[3][ee] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dispatch_pairs(const moe_shape& s, const int32_t* ids, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pairs, int32_t* row_token,
+                                 int32_t* blk_hist, hipStream_t st) {
+  const int64_t N = s.T * (int64_t)s.top_k;
+  const int E = s.n_experts;
+  const int nb = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
+  if (nb > 1)
+    hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, blk_hist);
+  hipLaunchKernelGGL(k_dispatch_pairs, dim3(nb), dim3(256), 0, st, ids, N, E, s.top_k, nb,
+                     nb > 1 ? (const int32_t*)blk_hist : nullptr, counts, offsets, sorted_pairs,
+                     row_token);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* slot_of,
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,

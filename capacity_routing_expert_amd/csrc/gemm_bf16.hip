@@ -58,6 +58,11 @@ constexpr int kActNone = 0;   // Y = acc + bias
 constexpr int kActSilu = 1;   // H = SiLU(acc + bias)
 constexpr int kActGated = 2;  // H = SiLU(gate) * up, gate and up rows of one weight tile, no bias
 
+// where the rows of a tile go
+constexpr int kOutSlots = 0;        // output row = slot (row0 + r)
+constexpr int kOutPairs = 1;        // output row = out_row[slot] (dropless pair order)
+constexpr int kOutPairsScaled = 2;  // ... and the row times row_scale[out_row[slot]]
+
 constexpr int kGroupM = 8;               // token tiles per XCD group
 constexpr int kGroupN = 32 / kGroupM;    // weight tiles per XCD group
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset beyond every buffer range used
@@ -155,11 +160,12 @@ __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) 
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT>
+template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
-    int N, int K, int a_rows, int e, int row0, int rows, int n0) {
+    const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
+    int a_rows, int e, int row0, int rows, int n0) {
   constexpr int WN = 2, WM = 2;              // waves along features / slots
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
@@ -238,6 +244,17 @@ __device__ __forceinline__ void gemm_tile(
       const int row = (wave * kXLoads + j) * kRowsPerLoad + lrow;
       const int c = pch ^ swz(row);
       xoff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
+    }
+  }
+  // row scales of the slot columns this lane holds in the epilogue (fetched here, ahead of
+  // the K loop, so the dependent index -> scale loads are long done when they are used)
+  float rsc[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    rsc[j] = 1.0f;
+    if (OUT == kOutPairsScaled) {
+      const int tl = wm * (TM / WM) + j * 32 + r32;
+      rsc[j] = tl < rows ? row_scale[out_row[row0 + tl]] : 0.0f;
     }
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
@@ -361,14 +378,19 @@ __device__ __forceinline__ void gemm_tile(
 #undef MOE_MFMA_STEP_ISSUE
 
   // ---- epilogue.  Lane (r32, half) holds, for block (i, j), features
-  // 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32.  Bias + activation + bf16 go
-  // into an LDS tile [TM slots][TNO features] (row pitch TNO * 2 + 16 bytes, so 16 consecutive
-  // rows start on distinct banks); the tile then leaves as coalesced 16-byte stores.  A gated
-  // tile pairs gate block i with up block i + FN/2 (same lane layout, same output features).
+  // 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32.  Bias + activation (+ row
+  // scale) + bf16 go into an LDS tile [TM slots][TNO features] (row pitch TNO * 2 + 16 bytes,
+  // so 16 consecutive rows start on distinct banks); the tile then leaves as coalesced 16-byte
+  // stores, to rows row0 .. or, in pair order, to the rows out_row names (kept in LDS after the
+  // tile).  A gated tile pairs gate block i with up block i + FN/2 (same lane layout, same
+  // output features).
   constexpr int kPitch = TNO * 2 + 16;
   constexpr int FNO = GATED ? FN / 2 : FN;  // output blocks per wave along features
   unsigned char* stile = reinterpret_cast<unsigned char*>(smem);
+  int32_t* srow = reinterpret_cast<int32_t*>(stile + TM * kPitch);
   __syncthreads();  // every wave is done reading the ring
+  if (OUT != kOutSlots)
+    for (int r = threadIdx.x; r < rows; r += kThreads) srow[r] = out_row[row0 + r];
 #pragma unroll
   for (int i = 0; i < FNO; ++i) {
     uint2 bb[4];
@@ -402,6 +424,10 @@ __device__ __forceinline__ void gemm_tile(
             for (int u = 0; u < 4; ++u) v[u] = v[u] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u]));
           }
         }
+        if (OUT == kOutPairsScaled) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] *= rsc[j];
+        }
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
@@ -414,8 +440,9 @@ __device__ __forceinline__ void gemm_tile(
   const int ncols = min(TNO, N - n0);
   for (int c = threadIdx.x; c < rows * kChunksPerRow; c += kThreads) {
     const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
+    const int64_t orow = OUT != kOutSlots ? (int64_t)srow[row] : (int64_t)(row0 + row);
     if (ch * 8 < ncols)
-      *reinterpret_cast<uint4*>(out + (int64_t)(row0 + row) * N + n0 + ch * 8) =
+      *reinterpret_cast<uint4*>(out + orow * N + n0 + ch * 8) =
           *reinterpret_cast<const uint4*>(stile + row * kPitch + ch * 16);
   }
 }
@@ -428,12 +455,12 @@ __device__ __forceinline__ void gemm_tile(
 // better, so the shorter height must win by 15 %).  The result does not depend on the choice:
 // each output element accumulates the same products in the same K order.
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT>
+          int ACT, int OUT>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
-    const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, int E, int N, int K, int a_rows,
-    int slots) {
+    const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, const int32_t* __restrict__ out_row,
+    const float* __restrict__ row_scale, int E, int N, int K, int a_rows, int slots) {
   const int lane = threadIdx.x & 63;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;  // output features per tile
   const int NT = (N + TNO - 1) / TNO;
@@ -448,23 +475,24 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       int mt, nt, e, row0, rows;
       if (!tile_of_block(tb.MT, NT, mt, nt)) return;
       tb.locate(offsets, lane, mt, e, row0, rows);
-      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT>(A, row_token, W, bias, out, N, K,
-                                                           a_rows, e, row0, rows, nt * TNO);
+      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT>(
+          A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
       return;
     }
   }
   int mt, nt, e, row0, rows;
   if (!tile_of_block(ta.MT, NT, mt, nt)) return;
   ta.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT>(A, row_token, W, bias, out, N, K, a_rows,
-                                                       e, row0, rows, nt * TNO);
+  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT>(
+      A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
 }
 
 namespace {
 
-constexpr size_t tile_lds(int TN, int TM, int BK, int NS) {
+constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
   const size_t ring = (size_t)NS * (TN + TM) * BK * 2;      // stage ring
-  const size_t tile = (size_t)TM * (TN * 2 + 16);           // epilogue staging tile
+  const size_t tile = (size_t)TM * (TN * 2 + 16)            // epilogue staging tile
+                      + (out_rows ? (size_t)TM * 4 : 0);    // + the output row of each slot
   return ring > tile ? ring : tile;
 }
 
@@ -483,16 +511,18 @@ int compute_units() {
 }
 
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT>
+          int ACT, int OUT = kOutSlots>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
-                               int K, int a_rows, int64_t rows_ub, hipStream_t st) {
+                               int K, int a_rows, int64_t rows_ub, hipStream_t st,
+                               const int32_t* out_row = nullptr,
+                               const float* row_scale = nullptr) {
   if (rows_ub <= 0) return hipSuccess;
-  constexpr size_t lds_a = tile_lds(TN, TMA, BK, NS);
-  constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS) : 0;
+  constexpr size_t lds_a = tile_lds(TN, TMA, BK, NS, OUT != kOutSlots);
+  constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS, OUT != kOutSlots) : 0;
   constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT>;
+  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -509,7 +539,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
   const int64_t grid = (ng_ub + 7) / 8 * 256;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, A, row_token, offsets, W,
-                     bias, out, E, N, K, a_rows, compute_units() * MINB);
+                     bias, out, out_row, row_scale, E, N, K, a_rows, compute_units() * MINB);
   return hipGetLastError();
 }
 
@@ -584,6 +614,56 @@ hipError_t launch_ffn_down_nobias(const moe_shape& s, const void* h, const int32
   return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, kActNone>(
       (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, nullptr, (bf16_t*)y,
       s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
+}
+
+
+// ---------------------------------------------------------------- dropless pair order
+// Fused-MoE flow diagram (moe-vllm flow): GEMM 1 reads token row p // top_k and writes pair row
+// p; GEMM 2 reads pair row p and writes pair row p times topk_weights[p].  Both walk the pairs
+// grouped by expert (sorted_pairs, expert e's at offsets[e] .. offsets[e+1] - 1), so each tile
+// uses one expert's weights; row_token[i] = sorted_pairs[i] / top_k.  The tiles, the K order and
+// so every product are those of the slot-order GEMMs; only where a row is read and written
+// changes, and GEMM 2 multiplies by the pair's weight before the bf16 rounding.
+hipError_t launch_ffn_up_pairs(const moe_shape& s, const void* x, const int32_t* row_token,
+                               const int32_t* sorted_pairs, const int32_t* offsets,
+                               const void* w1, const void* b1, void* h, int64_t rows_ub,
+                               bool gated, hipStream_t st) {
+  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
+  const bf16_t* xx = (const bf16_t*)x;
+  const bf16_t* w = (const bf16_t*)w1;
+  const bf16_t* b = (const bf16_t*)b1;
+  bf16_t* hh = (bf16_t*)h;
+  const int E = s.n_experts, F = s.d_ff, D = s.d_model, T = (int)s.T;
+  if (gated) {
+    if (skinny(s, rows_ub))
+      return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, true, kActGated, kOutPairs>(
+          xx, row_token, offsets, w, nullptr, hh, E, F, D, T, rows_ub, st, sorted_pairs);
+    return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActGated, kOutPairs>(
+        xx, row_token, offsets, w, nullptr, hh, E, F, D, T, rows_ub, st, sorted_pairs);
+  }
+  if (skinny(s, rows_ub))
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActSilu, kOutPairs>(
+        xx, row_token, offsets, w, b, hh, E, F, D, T, rows_ub, st, sorted_pairs);
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActSilu, kOutPairs>(
+      xx, row_token, offsets, w, b, hh, E, F, D, T, rows_ub, st, sorted_pairs);
+}
+
+// h and y hold T * top_k pair rows; b2 may be NULL (gated expert)
+hipError_t launch_ffn_down_pairs(const moe_shape& s, const void* h, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, const void* w2, const void* b2,
+                                 const float* weights, void* y, int64_t rows_ub, hipStream_t st) {
+  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
+  const bf16_t* hh = (const bf16_t*)h;
+  const bf16_t* w = (const bf16_t*)w2;
+  const bf16_t* b = (const bf16_t*)b2;
+  bf16_t* yy = (bf16_t*)y;
+  const int E = s.n_experts, F = s.d_ff, D = s.d_model;
+  const int P = (int)(s.T * s.top_k);
+  if (skinny(s, rows_ub))
+    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActNone, kOutPairsScaled>(
+        hh, sorted_pairs, offsets, w, b, yy, E, D, F, P, rows_ub, st, sorted_pairs, weights);
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActNone, kOutPairsScaled>(
+      hh, sorted_pairs, offsets, w, b, yy, E, D, F, P, rows_ub, st, sorted_pairs, weights);
 }
 
 }  // namespace moe

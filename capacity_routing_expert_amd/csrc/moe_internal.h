@@ -44,19 +44,22 @@ struct Workspace {
   size_t blk_hist;   // per-block expert histograms               [nb, E+1] int32
   size_t keys;       // bucketed sort keys                        [T*k] u64
   size_t rank;       // rank of each bucketed key in its expert   [T*k] int32
-  size_t row_token;  // token per slot                            [max_rows] int32
+  size_t row_token;  // token per slot (dropless: per sorted pair) [max_rows] int32
+  size_t pairs;      // dropless: pairs sorted by expert          [T*k] int32 (else 0 B)
   size_t row_token_pad;  // padded layout: token per buffer row  [E * cap] int32 (else 0 B)
   size_t offsets_pad;    // padded layout: e * cap                   [E+1] int32 (else 0 B)
   size_t h;          // activation between the GEMMs              [rows, d_ff]
   size_t y;          // expert outputs per slot                   [rows, d_model]
-                     // rows = max_rows (compact) or E * cap (padded)
+                     // rows = max_rows (compact), E * cap (padded) or T * k (dropless, in
+                     // pair order; the slot-dispatch buffers are then 0 B)
   size_t total;
 };
 
 constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
 
 int64_t max_rows(const moe_shape& s);
-Workspace layout(const moe_shape& s, bool padded = false);
+enum LayoutKind { kLayoutCompact = 0, kLayoutPadded = 1, kLayoutDropless = 2 };
+Workspace layout(const moe_shape& s, LayoutKind kind = kLayoutCompact);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)
 hipError_t launch_route(const moe_shape& s, const void* x, const void* w_router,
@@ -93,5 +96,23 @@ hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32
 
 hipError_t launch_combine(const moe_shape& s, const void* x, const float* gates,
                           const int32_t* slot_of, const void* y, void* out, hipStream_t st);
+
+// ---- dropless pair-order flow (bf16 GEMMs; moe_sum also fp32)
+// pairs p = t*k + c grouped by expert, ascending p inside an expert; row_token = pair / k
+hipError_t launch_dispatch_pairs(const moe_shape& s, const int32_t* ids, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pairs, int32_t* row_token,
+                                 int32_t* blk_hist, hipStream_t st);
+// H[pair] = act(x[pair / k] W1^T (+ b1)); gated: W1 is W13 [E, 2 d_ff, d_model], no bias
+hipError_t launch_ffn_up_pairs(const moe_shape& s, const void* x, const int32_t* row_token,
+                               const int32_t* sorted_pairs, const int32_t* offsets,
+                               const void* w1, const void* b1, void* h, int64_t rows_ub,
+                               bool gated, hipStream_t st);
+// Y[pair] = weights[pair] * (H[pair] W2^T (+ b2)); b2 may be NULL
+hipError_t launch_ffn_down_pairs(const moe_shape& s, const void* h, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, const void* w2, const void* b2,
+                                 const float* weights, void* y, int64_t rows_ub, hipStream_t st);
+// out[t] = (x[t] +) sum of pair rows t*k .. t*k + k - 1 whose id is in [0, E) (all if ids NULL)
+hipError_t launch_moe_sum(const moe_shape& s, const void* x, const int32_t* ids,
+                          const void* rows, void* out, hipStream_t st);
 
 }  // namespace moe

@@ -155,3 +155,69 @@ def combine(shape: B.MoeShape, x, gates, slot_of, y_rows) -> torch.Tensor:
     out = torch.empty_like(x)
     B.moe_combine(shape, x, gates, slot_of, y_rows, out)
     return out
+
+
+# ---------------------------------------------------------------- dropless pair-order flow
+def workspace_dropless(shape: B.MoeShape, device="cuda:0") -> torch.Tensor:
+    return torch.empty(max(B.workspace_bytes_dropless(shape), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def layer_forward_dropless(dev: dict, top_k: int, ws: torch.Tensor | None = None, events=None,
+                           gated: bool = False, want_rows: bool = True) -> dict:
+    """Dropless pair-order layer in one call (capacity unused); with `gated`, dev["w1"] is W13.
+    Returns out, ids, gates, counts and, when want_rows, pair_rows [T * k, d_model]."""
+    shape = shape_of(dev, top_k, 0)
+    device = dev["x"].device
+    T, E = shape.T, shape.n_experts
+    ws = workspace_dropless(shape, device) if ws is None else ws
+    res = {
+        "out": torch.empty_like(dev["x"]),
+        "ids": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+        "pair_rows": torch.empty((T * top_k, shape.d_model), dtype=dev["x"].dtype,
+                                 device=device) if want_rows else None,
+    }
+    kw = dict(topk_ids=res["ids"], topk_gates=res["gates"], expert_counts=res["counts"],
+              pair_rows=res["pair_rows"], ws=ws, events=events)
+    if gated:
+        B.moe_layer_forward_dropless_gated(shape, dev["x"], dev["w_router"], dev["b_router"],
+                                           dev["w1"], dev["w2"], res["out"], **kw)
+    else:
+        B.moe_layer_forward_dropless(shape, dev["x"], dev["w_router"], dev["b_router"],
+                                     dev["w1"], dev["b1"], dev["w2"], dev["b2"], res["out"], **kw)
+    return res
+
+
+def dispatch_pairs(shape: B.MoeShape, ids: torch.Tensor, ws=None) -> dict:
+    device = ids.device
+    N, E = shape.T * shape.top_k, shape.n_experts
+    ws = workspace_dropless(shape, device) if ws is None else ws
+    res = {
+        "counts": torch.empty((E,), dtype=torch.int32, device=device),
+        "offsets": torch.empty((E + 1,), dtype=torch.int32, device=device),
+        "sorted_pairs": torch.empty((N,), dtype=torch.int32, device=device),
+        "row_token": torch.empty((N,), dtype=torch.int32, device=device),
+    }
+    B.moe_dispatch_pairs(shape, ids, res["counts"], res["offsets"], res["sorted_pairs"],
+                         res["row_token"], ws)
+    return res
+
+
+def expert_ffn_pairs(shape: B.MoeShape, dev: dict, disp: dict, weights: torch.Tensor, ws=None,
+                     gated: bool = False) -> torch.Tensor:
+    device = dev["x"].device
+    ws = workspace_dropless(shape, device) if ws is None else ws
+    rows = torch.empty((shape.T * shape.top_k, shape.d_model), dtype=dev["x"].dtype,
+                       device=device)
+    B.moe_expert_ffn_pairs(shape, dev["x"], disp["sorted_pairs"], disp["row_token"],
+                           disp["offsets"], dev["w1"], None if gated else dev["b1"], dev["w2"],
+                           None if gated else dev["b2"], weights, rows, ws, gated=gated)
+    return rows
+
+
+def moe_sum(shape: B.MoeShape, x, ids, pair_rows) -> torch.Tensor:
+    out = torch.empty((shape.T, shape.d_model), dtype=pair_rows.dtype, device=pair_rows.device)
+    B.moe_sum(shape, x, ids, pair_rows, out)
+    return out

@@ -214,6 +214,77 @@ moe_status moe_layer_forward_gated(const moe_shape* shape, const void* x, const 
                                    void* ws, size_t ws_bytes, moe_stream_t stream,
                                    moe_event_t const* events);
 
+/* ---- Dropless pair-order flow.  Fused-MoE flow diagram (moe-vllm flow): no capacity and no
+ * combine gather.  Pair p = t * top_k + c is choice c of token t.  GEMM 1 reads token row
+ * p / top_k and writes activation row p; everything up to moe_sum stays in pair order; GEMM 2
+ * writes pair row p multiplied by topk_weights[p] (here the unrenormalised gates); moe_sum adds
+ * the top_k consecutive rows of each token.  Both GEMMs walk the pairs grouped by expert, so
+ * each tile uses one expert's weights.  Reading taken for the output: the residual is added as
+ * in the Worked Example's traces, so with a capacity that holds every pair this is
+ * moe_layer_forward's result.  shape.capacity is ignored.  bf16 only (moe_sum also takes fp32);
+ * MOE_ERR_UNSUPPORTED for fp32 and when the T * top_k * d_ff activation reaches 2 GiB. */
+
+/* Workspace bytes for the dropless calls; 0 for an invalid shape. */
+size_t moe_workspace_bytes_dropless(const moe_shape* shape);
+
+/* Group the pairs by expert (the diagram's sorted ids).  A stable counting sort: expert e's
+ * pairs, in ascending p, at sorted_pairs[offsets[e] .. offsets[e+1] - 1].
+ *   topk_ids       [T, k] int32 in; an id outside [0, E) is not counted and its pair is placed
+ *                  after offsets[E]
+ *   expert_counts  [E] int32 out;  expert_offsets [E+1] int32 out (exclusive prefix of counts)
+ *   sorted_pairs   [T * k] int32 out;  row_token [T * k] int32 out: sorted_pairs[i] / top_k */
+moe_status moe_dispatch_pairs(const moe_shape* shape, const int32_t* topk_ids,
+                              int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_pairs, int32_t* row_token, void* ws,
+                              size_t ws_bytes, moe_stream_t stream);
+
+/* The two expert GEMMs in pair order (diagram boxes GEMM 1, SiLU x mul, GEMM 2):
+ *   pair_rows[p] = topk_weights[p] * (W2[e] act(W1[e] x[p / top_k] + b1[e]) + b2[e])
+ * for every pair p of expert e listed by moe_dispatch_pairs.  gated = 0: act = SiLU, w1
+ * [E, d_ff, d_model], biases b1, b2 required.  gated != 0: w1 is w13 [E, 2 d_ff, d_model] of
+ * moe_layer_forward_gated, act(.) = SiLU(gate) * up, no biases (b1, b2 ignored).
+ *   topk_weights [T, k] fp32 in; pair_rows [T * k, d_model] bf16 out (rows of pairs with an id
+ *   outside [0, E) are not written).  fp32 accumulation on the matrix cores, the activation
+ *   stored as bf16, the weight applied before the bf16 rounding of pair_rows. */
+moe_status moe_expert_ffn_pairs(const moe_shape* shape, const void* x,
+                                const int32_t* sorted_pairs, const int32_t* row_token,
+                                const int32_t* expert_offsets, const void* w1, const void* b1,
+                                const void* w2, const void* b2, const float* topk_weights,
+                                int32_t gated, void* pair_rows, void* ws, size_t ws_bytes,
+                                moe_stream_t stream);
+
+/* moe_sum box: out[t] = x[t] + sum over c of pair_rows[t * k + c], in choice order, fp32
+ * with one rounding to the dtype.
+ *   x [T, d_model] or NULL (no residual: the sum alone)
+ *   topk_ids [T, k] or NULL: when given, pairs whose id is outside [0, E) are skipped
+ *   pair_rows [T * k, d_model];  out [T, d_model], aliasing neither x nor pair_rows
+ * A token with no pair row left leaves as x[t] bit for bit (zeros without x). */
+moe_status moe_sum(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                   const void* pair_rows, void* out, moe_stream_t stream);
+
+/* The whole dropless layer: moe_route, moe_dispatch_pairs, moe_expert_ffn_pairs (gated = 0),
+ * moe_sum with the residual.  topk_ids, topk_gates, expert_counts and pair_rows [T * k,
+ * d_model] are optional outputs (NULL keeps them in the workspace); events NULL or 6
+ * hipEvent_t recorded before routing, after routing, after the pair dispatch, after GEMM 1,
+ * after GEMM 2 and after moe_sum. */
+moe_status moe_layer_forward_dropless(const moe_shape* shape, const void* x,
+                                      const void* w_router, const float* b_router,
+                                      const void* w1, const void* b1, const void* w2,
+                                      const void* b2, void* out, int32_t* topk_ids,
+                                      float* topk_gates, int32_t* expert_counts, void* pair_rows,
+                                      void* ws, size_t ws_bytes, moe_stream_t stream,
+                                      moe_event_t const* events);
+
+/* moe_layer_forward_dropless with the gated expert (w13 as in moe_layer_forward_gated): the
+ * flow diagram end to end. */
+moe_status moe_layer_forward_dropless_gated(const moe_shape* shape, const void* x,
+                                            const void* w_router, const float* b_router,
+                                            const void* w13, const void* w2, void* out,
+                                            int32_t* topk_ids, float* topk_gates,
+                                            int32_t* expert_counts, void* pair_rows, void* ws,
+                                            size_t ws_bytes, moe_stream_t stream,
+                                            moe_event_t const* events);
+
 #ifdef __cplusplus
 }
 #endif
