@@ -21,6 +21,9 @@ what a library primitive (matmul, sort) does internally:
     path and reach the next layer exactly as they entered.
   * "Dynamic Token Routing AI" (freenetmedia.pl), "How it works": a gating network
     scores each token and selects the expert(s).
+  * "Token Routing Optimization in Batch Processing" (subtext diagram): a Token Scheduler
+    that regroups the tokens of several batches, leaving each token's routing unchanged, so
+    that each new batch activates fewer experts with more tokens per active expert.
   * The fused-MoE flow diagram (monishver11.github.io, moe-vllm flow): the dropless
     pair-order flow (GEMM 1 reads token row p // top_k and writes pair row p, GEMM 2
     scales pair row p by its top-k weight, moe_sum adds a token's top_k consecutive
@@ -65,6 +68,9 @@ __all__ = [
     "forward_dropless_with_routing",
     "forward_dropless",
     "forward_dropless_gated",
+    "schedule_batches",
+    "active_experts",
+    "forward_batches",
 ]
 
 
@@ -474,3 +480,65 @@ def forward_dropless_gated(x, w_router, b_router, w13, w2, k: int) -> dict:
         x, r["ids"], r["gates"], E, lambda e, rows: expert_ffn_gated(rows, w13[e], w2[e]))
     res.update({"logits": r["logits"], "probs": r["probs"], "gates_all": r["gates_all"]})
     return res
+
+
+# ----------------------------------------------------------------------------- batch consolidation
+def active_experts(ids: np.ndarray, batches) -> np.ndarray:
+    """Number of distinct experts the tokens of each batch are routed to (the experts a batch
+    "activates" in the Token Routing Optimization diagram)."""
+    ids = np.asarray(ids)
+    return np.array([len({int(e) for t in b for e in ids[t]}) for b in batches], dtype=np.int32)
+
+
+def schedule_batches(ids: np.ndarray, batch_size: int) -> dict:
+    """Token Scheduler of "Token Routing Optimization in Batch Processing" (subtext diagram).
+
+    The diagram keeps token-level routing as it is and changes only which tokens travel
+    together: two batches that each activate every expert with one token per expert become two
+    batches that each activate half the experts with two tokens per expert.  The pages give no
+    algorithm; the reading taken is the plainest one that reproduces the diagram: order the
+    tokens by the set of experts they are routed to (their k ids sorted ascending, compared as
+    tuples), ties by token index, and cut the ordered list into consecutive batches of the
+    original size.  Tokens sharing an expert set then travel together.
+
+    ids [T, k] with T a multiple of batch_size.  Returns order [T] (new position -> token),
+    the new and the original batches (lists of token arrays), and their active-expert counts.
+    """
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    if batch_size < 1 or T % batch_size:
+        raise ValueError("the pool must hold whole batches")
+    keys = [tuple(sorted(int(e) for e in ids[t])) for t in range(T)]
+    order = np.array(sorted(range(T), key=lambda t: (keys[t], t)), dtype=np.int32)
+    M = T // batch_size
+    new = [order[b * batch_size:(b + 1) * batch_size] for b in range(M)]
+    orig = [np.arange(b * batch_size, (b + 1) * batch_size) for b in range(M)]
+    return {"order": order, "batches": new, "orig_batches": orig,
+            "active": active_experts(ids, new), "orig_active": active_experts(ids, orig)}
+
+
+def forward_batches(x, w_router, b_router, w1, b1, w2, b2, k: int, capacity_factor: float,
+                    batch_size: int, consolidate: bool) -> dict:
+    """A pool of batches through the capacity layer, one batch at a time: route every token
+    (routing is per token, so it does not depend on the batch), regroup the batches with
+    schedule_batches when `consolidate`, then run dispatch, expert FFN and combine on each
+    batch with the capacity of a batch of batch_size tokens.  out is in the pool's token
+    order.  With a capacity of at least batch_size nothing can drop, and the output does not
+    depend on the grouping."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    r = route(x, w_router, b_router, k)
+    sched = schedule_batches(r["ids"], batch_size)
+    batches = sched["batches"] if consolidate else sched["orig_batches"]
+    cap = capacity(batch_size, k, E, capacity_factor)
+    x64 = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x64)
+    n_kept = 0
+    for b in batches:
+        res = forward_with_routing(x64[b], r["ids"][b], r["gates"][b], cap, E, w1, b1, w2, b2)
+        out[b] = res["out"]
+        n_kept += res["n_kept"]
+    return {"ids": r["ids"], "gates": r["gates"], "logits": r["logits"], "probs": r["probs"],
+            "gates_all": r["gates_all"], "order": sched["order"], "batches": batches,
+            "active": sched["active"] if consolidate else sched["orig_active"],
+            "cap": cap, "n_kept": n_kept, "out": out}

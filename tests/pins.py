@@ -24,7 +24,12 @@ What pins what:
   * the dropless pair-order flow: a hand-sorted pair list, counting-sort invariants
     (permutation, experts non-decreasing, pairs ascending inside an expert), moe_sum against
     numpy's reshape-and-sum, each pair row and token output against torch float64 linear/SiLU
-    per token, and the capacity layer's output when the capacity holds every pair.
+    per token, and the capacity layer's output when the capacity holds every pair;
+  * the batch scheduler: the Token Routing Optimization diagram's counts
+    (tests/golden/batch_consolidation.json: 4 experts per batch with 1 token each become 2
+    with 2 each) for every legible reading of its second batch, brute-force set counting, the
+    top-1 bound E_used + M - 1, and the layer's output unchanged by the grouping when nothing
+    can drop (per-token torch recomputation), per-batch capacity when it can.
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ from fractions import Fraction
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+GOLDEN_SCHED = os.path.join(os.path.dirname(__file__), "golden", "batch_consolidation.json")
 
 
 def golden():
@@ -608,6 +614,75 @@ def check_dropless_is_capacity_without_drops(o):
             assert np.max(np.abs(p["pair_rows"][t * k + c] - want)) < 1e-13
 
 
+# ----------------------------------------------------------------------------- batch scheduler
+def check_schedule_diagram(o):
+    """The diagram's pool: 8 tokens, top-1 over 4 experts, two batches of 4 in which every
+    expert takes one token.  After scheduling, each batch activates 2 experts with 2 tokens
+    each, for every order of the second batch's experts (the transcription does not fix it)."""
+    with open(GOLDEN_SCHED) as fh:
+        g = json.load(fh)["facts"]
+    B = g["pool"]["batch_size"]
+    for perm in itertools.permutations(range(4)):
+        ids = np.array(g["batch1_experts"]["value"] + list(perm), dtype=np.int32)[:, None]
+        s = o.schedule_batches(ids, B)
+        assert [list(b) for b in s["orig_batches"]] == g["original_batches"]["value"]
+        assert list(s["orig_active"]) == [g["original_active_per_batch"]["value"]] * 2
+        assert B // g["original_active_per_batch"]["value"] == g["original_tokens_per_expert"]["value"]
+        assert list(s["active"]) == [g["optimized_active_per_batch"]["value"]] * 2
+        for b in s["batches"]:
+            _, per = np.unique(ids[b, 0], return_counts=True)
+            assert list(per) == [g["optimized_tokens_per_expert"]["value"]] * 2
+        assert sorted(int(t) for t in s["order"]) == list(range(8))
+
+
+def check_schedule_bruteforce(o):
+    """Random pools (top-1 .. top-3): the order is a permutation, tokens sharing an expert set
+    are contiguous in it, sets appear in ascending tuple order with ascending token index
+    inside, and the active counts are the set sizes counted directly; for top-1 the total
+    active experts is at most (experts used) + (batches) - 1."""
+    rng = _rng(83)
+    for T, B, E, k in ((24, 4, 5, 1), (48, 8, 6, 2), (60, 12, 7, 3), (16, 16, 3, 1), (30, 1, 4, 2)):
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        s = o.schedule_batches(ids, B)
+        order = [int(t) for t in s["order"]]
+        assert sorted(order) == list(range(T))
+        keys = [tuple(sorted(ids[t])) for t in order]
+        for i in range(T - 1):
+            assert keys[i] < keys[i + 1] or (keys[i] == keys[i + 1] and order[i] < order[i + 1])
+        for j, b in enumerate(s["batches"]):
+            assert list(b) == order[j * B:(j + 1) * B]
+            assert s["active"][j] == len(set(ids[b].ravel().tolist()))
+        for j in range(T // B):
+            assert s["orig_active"][j] == len(set(ids[j * B:(j + 1) * B].ravel().tolist()))
+        if k == 1:
+            assert int(s["active"].sum()) <= len(set(ids.ravel().tolist())) + T // B - 1
+
+
+def check_batches_output(o):
+    """Capacity at least the batch size: nothing drops and every token leaves as x plus its
+    gate-weighted experts (torch float64, per token), grouped or not.  A smaller capacity is
+    applied per batch: each batch's output is the capacity layer run on that batch alone."""
+    rng = _rng(89)
+    T, B, d, f, E, k = 24, 6, 5, 7, 4, 2
+    x = rng.standard_normal((T, d)); w = rng.standard_normal((E, d))
+    w1, b1, w2, b2 = _rand_weights(rng, E, d, f)
+    C = float(E) / k  # capacity = B
+    for cons in (False, True):
+        res = o.forward_batches(x, w, None, w1, b1, w2, b2, k, C, B, cons)
+        assert res["cap"] == B and res["n_kept"] == T * k
+        for t in range(T):
+            want = x[t].copy()
+            for c in range(k):
+                e = res["ids"][t, c]
+                want = want + float(res["gates"][t, c]) * _torch_ffn(x[t:t + 1], w1[e], b1[e], w2[e], b2[e])[0]
+            assert np.max(np.abs(res["out"][t] - want)) < 1e-13
+    res = o.forward_batches(x, w, None, w1, b1, w2, b2, k, 0.5, B, True)
+    assert res["cap"] == 1
+    for b in res["batches"]:
+        one = o.forward(x[b], w, None, w1, b1, w2, b2, k, 0.5)
+        assert np.max(np.abs(res["out"][b] - one["out"])) < 1e-13
+
+
 ALL_CHECKS = [
     check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
     check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
@@ -618,4 +693,5 @@ ALL_CHECKS = [
     check_padded_empty_rows, check_padded_same_layer, check_gated_closed_forms,
     check_gated_vs_torch, check_pairs_hand_example, check_pairs_invariants, check_moe_sum,
     check_dropless_flow_vs_torch, check_dropless_is_capacity_without_drops,
+    check_schedule_diagram, check_schedule_bruteforce, check_batches_output,
 ]

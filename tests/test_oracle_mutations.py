@@ -255,7 +255,63 @@ def _make_dropless(read_row=None, weight=True, weight_by_position=False):
     return fwd
 
 
+def _sched_choice_order(ids, batch_size):
+    # keys in choice order instead of as sets: (a, b) and (b, a) are kept apart
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    order = np.array(sorted(range(T), key=lambda t: (tuple(int(e) for e in ids[t]), t)), np.int32)
+    M = T // batch_size
+    new = [order[j * batch_size:(j + 1) * batch_size] for j in range(M)]
+    orig = [np.arange(j * batch_size, (j + 1) * batch_size) for j in range(M)]
+    return {"order": order, "batches": new, "orig_batches": orig,
+            "active": O.active_experts(ids, new), "orig_active": O.active_experts(ids, orig)}
+
+
+def _sched_no_tiebreak(ids, batch_size):
+    # equal expert sets in descending token order
+    d = _orig["schedule_batches"](ids, batch_size)
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    keys = [tuple(sorted(int(e) for e in ids[t])) for t in range(T)]
+    order = np.array(sorted(range(T), key=lambda t: (keys[t], -t)), np.int32)
+    new = [order[j * batch_size:(j + 1) * batch_size] for j in range(T // batch_size)]
+    d.update(order=order, batches=new, active=O.active_experts(ids, new))
+    return d
+
+
+def _sched_round_robin(ids, batch_size):
+    # deal the ordered tokens round-robin over the batches instead of in consecutive runs
+    d = _orig["schedule_batches"](ids, batch_size)
+    M = len(d["batches"])
+    new = [d["order"][j::M] for j in range(M)]
+    d.update(batches=new, active=O.active_experts(ids, new))
+    return d
+
+
+def _active_counts_assignments(ids, batches):
+    return np.array([len([e for t in b for e in np.asarray(ids)[t]]) for b in batches], np.int32)
+
+
+def _batches_pool_capacity(x, w_router, b_router, w1, b1, w2, b2, k, C, batch_size, consolidate):
+    # the capacity of the whole pool applied to every batch
+    res = _orig["forward_batches"](x, w_router, b_router, w1, b1, w2, b2, k, C, batch_size,
+                                   consolidate)
+    T, E = x.shape[0], w_router.shape[0]
+    cap = O.capacity(T, k, E, C)
+    out = np.zeros_like(res["out"])
+    for b in res["batches"]:
+        out[b] = O.forward_with_routing(x[b], res["ids"][b], res["gates"][b], cap, E, w1, b1, w2,
+                                        b2)["out"]
+    res.update(out=out, cap=cap)
+    return res
+
+
 MUTATIONS = {
+    "schedule_keys_in_choice_order": {"schedule_batches": _sched_choice_order},
+    "schedule_ties_descending": {"schedule_batches": _sched_no_tiebreak},
+    "schedule_round_robin_batches": {"schedule_batches": _sched_round_robin},
+    "active_counts_assignments": {"active_experts": _active_counts_assignments},
+    "batches_use_pool_capacity": {"forward_batches": _batches_pool_capacity},
     "pairs_descending_within_expert": {"dispatch_pairs": _pairs_descending},
     "pairs_row_token_mod_k": {"dispatch_pairs": _pairs_row_mod},
     "moe_sum_choice_major_rows": {"moe_sum": _moe_sum_token_major},
