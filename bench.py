@@ -13,7 +13,9 @@ router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), e
 Workload: the mid-size layer (T 4096, d_model 2048, d_ff 8192, 8 experts, top-2, capacity
 factor 1.25) unless --config names another.  --layout dropless times the dropless pair-order
 flow instead (no capacity: pair dispatch, pair-order GEMMs with the top-k weight applied in
-GEMM 2, moe_sum in place of the combine).
+GEMM 2, moe_sum in place of the combine).  --config decode_pool times a pool of decode batches
+run one after another, in the original grouping and regrouped by the Token Scheduler; `value`
+is the consolidated run's tokens/s.
 """
 from __future__ import annotations
 
@@ -116,13 +118,129 @@ def cpu_baseline(inp, wl, cap, dropless=False):
             "n_kept": int(res["n_kept"])}
 
 
+def bench_pool(args, wl, inp):
+    """A pool of batches, one after another: the original grouping against the Token
+    Scheduler's.  Roofline: the pool is bound by streaming the active experts' weights once per
+    batch; achieved = those weight bytes / the batch loop's event-bracketed time (dispatch and
+    combine included)."""
+    import torch
+    from capacity_routing_expert_amd import binding as B
+    from capacity_routing_expert_amd import layer as L
+
+    dev = torch.device("cuda:0")
+    d = L.upload(inp, dev)
+    Bsz = wl.batch_size
+    M = wl.T // Bsz
+    cap = B.capacity(Bsz, wl.top_k, wl.n_experts, wl.capacity_factor)
+    dtype = B.MOE_BF16 if wl.dtype == "bf16" else B.MOE_F32
+    shape = B.make_shape(Bsz, wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, cap, dtype)
+    ws = torch.empty(max(B.workspace_bytes_batches(shape, M), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["x"])
+    bexp = torch.empty((M,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    esz = inp["x"].itemsize
+    w_bytes = (2 * wl.d_model * wl.d_ff + wl.d_ff + wl.d_model) * esz  # one expert's W1 b1 W2 b2
+
+    def run(cons, events=None):
+        B.moe_layer_forward_batches(shape, M, cons, d["x"], d["w_router"], d["b_router"], d["w1"],
+                                    d["b1"], d["w2"], d["b2"], out, batch_experts=bexp, ws=ws,
+                                    events=events)
+
+    result = {}
+    for cons in (False, True):
+        for _ in range(args.warmup):
+            run(cons)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run(cons)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        evsets = []
+        for _ in range(args.steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            for ev in evs:
+                ev.record(stream)
+            evsets.append(evs)
+        torch.cuda.synchronize()
+        for evs in evsets:
+            run(cons, evs)
+        torch.cuda.synchronize()
+        st = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evsets]))
+              for j, name in enumerate(["route", "schedule", "batches", "scatter"])}
+        active = [int(v) for v in bexp.cpu().numpy()]
+        loop_s = st["batches"] / 1e3
+        result[cons] = {"tokens_per_s": wl.T / wall, "ms_per_step": wall * 1e3, "stages_ms": st,
+                        "active_experts": active,
+                        "mean_active_experts": float(np.mean(active)),
+                        "tokens_per_active_expert": float(Bsz * wl.top_k / np.mean(active)),
+                        "weight_GBps": sum(active) * w_bytes / loop_s / 1e9}
+    c, o = result[True], result[False]
+    res = {
+        "metric": METRIC,
+        "value": c["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": c["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
+        "config": {"workload": wl.name, "T": wl.T, "batch_size": Bsz, "n_batches": M,
+                   "d_model": wl.d_model, "d_ff": wl.d_ff, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "capacity_factor": wl.capacity_factor, "capacity": cap,
+                   "layout": "batches, Token Scheduler regrouping"},
+        "roofline": {"kernel": "k_grouped_gemm skinny tiles (active experts' weight stream), "
+                               "batch loop", "bound": "hbm", "achieved": c["weight_GBps"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": c["weight_GBps"] / PEAK_HBM_GBS,
+                     "traffic": None,
+                     "units_per_launch": f"{sum(c['active_experts'])} active (batch, expert) "
+                                         f"pairs x {w_bytes} B of weights"},
+        "consolidated": c,
+        "original": o,
+        "speedup_vs_original": c["tokens_per_s"] / o["tokens_per_s"],
+        "stage_timing": "HIP events: route, schedule + regroup, batch loop, scatter back",
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline_pool(inp, wl)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_pool(inp, wl):
+    """The oracle's pooled layer (route, Token Scheduler, per-batch layer) on this host."""
+    import oracle.moe_oracle as O
+    from capacity_routing_expert_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    dt = inp["dtype"]
+    f = {n: W.to_float64(inp[n], dt) for n in ("x", "w_router", "w1", "b1", "w2", "b2")}
+    times = []
+    while not times or (sum(times) < 10.0 and len(times) < 20):
+        t0 = time.perf_counter()
+        O.forward_batches(f["x"], f["w_router"], inp["b_router"], f["w1"], f["b1"], f["w2"],
+                          f["b2"], wl.top_k, wl.capacity_factor, wl.batch_size, True)
+        times.append(time.perf_counter() - t0)
+    t = float(np.mean(times))
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole consolidated pool ({wl.T} tokens in batches of "
+                      f"{wl.batch_size}), {len(times)} runs, {t:.2f} s each, float64 NumPy/BLAS",
+            "seconds": round(t, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mid",
-                    help="worked_example | mid | fine | decode | collapse | gated")
+                    help="worked_example | mid | fine | decode | collapse | gated | decode_pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", default="compact", choices=["compact", "padded", "dropless"],
                     help="compact: the expert FFN runs over the kept rows only; padded: over "
@@ -150,6 +268,9 @@ def main():
     cap = B.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
     log(f"[bench] generating {wl.name}")
     inp = W.make_inputs(wl)
+    if wl.batch_size:
+        bench_pool(args, wl, inp)
+        return
     d = L.upload(inp, dev)
     shape = L.shape_of(d, wl.top_k, cap)
     padded = args.layout == "padded"

@@ -27,7 +27,8 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_stat
            "moe_layer_forward", "moe_layer_forward_profiled", "moe_workspace_bytes_padded",
            "moe_layer_forward_padded", "moe_layer_forward_gated", "moe_workspace_bytes_dropless",
            "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
-           "moe_layer_forward_dropless_gated")
+           "moe_layer_forward_dropless_gated", "moe_workspace_bytes_batches",
+           "moe_schedule_batches", "moe_layer_forward_batches")
 
 
 class MoeShape(ctypes.Structure):
@@ -92,10 +93,17 @@ def lib() -> ctypes.CDLL:
         # shape, x, w_router, b_router, w13, w2, out, ids, gates, counts, pair_rows, ws,
         # ws_bytes, stream, events
         L.moe_layer_forward_dropless_gated.argtypes = [SP] + [P] * 11 + [SZ, P, P]
+        L.moe_workspace_bytes_batches.argtypes = [SP, I32]
+        L.moe_workspace_bytes_batches.restype = SZ
+        L.moe_schedule_batches.argtypes = [SP, I32, P, P, P, P, P]
+        # shape, n_batches, consolidate, x, w_router, b_router, w1, b1, w2, b2, out, ids, gates,
+        # order, batch_experts, ws, ws_bytes, stream, events
+        L.moe_layer_forward_batches.argtypes = [SP, I32, I32] + [P] * 13 + [SZ, P, P]
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                      "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_padded",
                      "moe_layer_forward_gated", "moe_dispatch_pairs", "moe_expert_ffn_pairs",
-                     "moe_sum", "moe_layer_forward_dropless", "moe_layer_forward_dropless_gated"):
+                     "moe_sum", "moe_layer_forward_dropless", "moe_layer_forward_dropless_gated",
+                     "moe_schedule_batches", "moe_layer_forward_batches"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -273,10 +281,12 @@ def moe_layer_forward_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids
         "moe_layer_forward_gated")
 
 
-def _events(events):
+def _events(events, n=6):
     if events is None:
         return None
-    return (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
+    if len(events) != n:
+        raise ValueError(f"expected {n} events, got {len(events)}")
+    return (ctypes.c_void_p * n)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
 
 
 def moe_dispatch_pairs(shape, topk_ids, expert_counts, expert_offsets, sorted_pairs, row_token,
@@ -341,3 +351,33 @@ def moe_layer_forward_dropless_gated(shape, x, w_router, b_router, w13, w2, out,
         _ptr(expert_counts, "expert_counts", torch.int32), _ptr(pair_rows, "pair_rows", dt),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), _events(events)),
         "moe_layer_forward_dropless_gated")
+
+
+def workspace_bytes_batches(batch_shape: MoeShape, n_batches: int) -> int:
+    return int(lib().moe_workspace_bytes_batches(ctypes.byref(batch_shape), int(n_batches)))
+
+
+def moe_schedule_batches(batch_shape, n_batches, topk_ids, order, batch_experts=None,
+                         orig_batch_experts=None, stream=None):
+    _check(lib().moe_schedule_batches(
+        ctypes.byref(batch_shape), int(n_batches), _ptr(topk_ids, "topk_ids", torch.int32),
+        _ptr(order, "order", torch.int32), _ptr(batch_experts, "batch_experts", torch.int32),
+        _ptr(orig_batch_experts, "orig_batch_experts", torch.int32), _stream(stream)),
+        "moe_schedule_batches")
+
+
+def moe_layer_forward_batches(batch_shape, n_batches, consolidate, x, w_router, b_router, w1, b1,
+                              w2, b2, out, topk_ids=None, topk_gates=None, order=None,
+                              batch_experts=None, ws=None, events=None, stream=None):
+    """A pool of n_batches batches of batch_shape.T tokens, one batch after another, regrouped
+    by the Token Scheduler when `consolidate`; `events` None or 5 recorded
+    torch.cuda.Event(enable_timing=True)."""
+    dt = _dtype_of(batch_shape)
+    _check(lib().moe_layer_forward_batches(
+        ctypes.byref(batch_shape), int(n_batches), int(bool(consolidate)), _ptr(x, "x", dt),
+        _ptr(w_router, "w_router", dt), _ptr(b_router, "b_router", torch.float32),
+        _ptr(w1, "w1", dt), _ptr(b1, "b1", dt), _ptr(w2, "w2", dt), _ptr(b2, "b2", dt),
+        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
+        _ptr(topk_gates, "topk_gates", torch.float32), _ptr(order, "order", torch.int32),
+        _ptr(batch_experts, "batch_experts", torch.int32), _ptr(ws, "ws", torch.uint8),
+        ws.numel(), _stream(stream), _events(events, 5)), "moe_layer_forward_batches")

@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm_bf16.hip", "ffn_f32.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm_bf16.hip", "ffn_f32.hip", "combine.hip",
+           "schedule.hip"]
 ARCH = "gfx950"
 
 

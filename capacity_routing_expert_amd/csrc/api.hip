@@ -339,6 +339,163 @@ moe_status layer_forward_dropless(const moe_shape* shape, const void* x, const v
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- batches of a pool
+// Workspace of moe_layer_forward_batches: one batch's workspace (reused batch after batch, the
+// calls being ordered on one stream), then the pool's buffers.
+struct BatchesLayout {
+  Workspace per;  // offsets relative to the start of the workspace
+  size_t ids, gates, order, x_perm, ids_perm, gates_perm, out_perm, total;
+};
+
+moe_shape pool_shape(const moe_shape& b, int32_t n_batches) {
+  moe_shape p = b;
+  p.T = b.T * (int64_t)n_batches;
+  return p;
+}
+
+BatchesLayout batches_layout(const moe_shape& b, int32_t n_batches) {
+  BatchesLayout w;
+  w.per = layout(b);
+  const int64_t T = b.T * (int64_t)n_batches;
+  const size_t eb = elem_bytes(b), k = (size_t)b.top_k;
+  size_t o = w.per.total;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = align256(o + bytes);
+    return at_;
+  };
+  w.ids = take((size_t)T * k * 4);
+  w.gates = take((size_t)T * k * 4);
+  w.order = take((size_t)T * 4);
+  w.x_perm = take((size_t)T * b.d_model * eb);
+  w.ids_perm = take((size_t)T * k * 4);
+  w.gates_perm = take((size_t)T * k * 4);
+  w.out_perm = take((size_t)T * b.d_model * eb);
+  w.total = o;
+  return w;
+}
+
+// shape and pool checks shared by the scheduling calls; `consolidate` adds the sort's limits
+moe_status check_batches(const moe_shape* batch_shape, int32_t n_batches, bool consolidate) {
+  MOE_TRY(check_shape(batch_shape));
+  const moe_shape& b = *batch_shape;
+  if (n_batches < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "n_batches = %d < 0", n_batches);
+  const moe_shape p = pool_shape(b, n_batches);
+  MOE_TRY(check_shape(&p));  // the pool's T * k and x size limits
+  if (consolidate) {
+    if (p.T > kSchedMaxT)
+      return fail(MOE_ERR_UNSUPPORTED, "a pool of %lld tokens: the scheduler sorts at most %d",
+                  (long long)p.T, kSchedMaxT);
+    if (b.top_k > kSchedMaxK ||
+        b.top_k * schedule_bits_e(b.n_experts) + kSchedIndexBits > 64)
+      return fail(MOE_ERR_UNSUPPORTED, "top_k = %d ids of %d experts do not fit a 64-bit key",
+                  b.top_k, b.n_experts);
+  }
+  return MOE_OK;
+}
+
+moe_status layer_forward_batches(const moe_shape* batch_shape, int32_t n_batches,
+                                 bool consolidate, const void* x, const void* w_router,
+                                 const float* b_router, const void* w1, const void* b1,
+                                 const void* w2, const void* b2, void* out, int32_t* topk_ids,
+                                 float* topk_gates, int32_t* order, int32_t* batch_experts,
+                                 void* ws, size_t ws_bytes, hipStream_t st,
+                                 moe_event_t const* events) {
+  MOE_TRY(check_batches(batch_shape, n_batches, consolidate));
+  const moe_shape& bs = *batch_shape;
+  if (events)
+    for (int i = 0; i < 5; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  auto rec = [&](int i) -> moe_status {
+    if (!events) return MOE_OK;
+    hipError_t err = hipEventRecord((hipEvent_t)events[i], st);
+    return err == hipSuccess ? MOE_OK : device_error(err, "hipEventRecord");
+  };
+  const moe_shape ps = pool_shape(bs, n_batches);
+  if (ps.T == 0) {  // empty pool: nothing to check or enqueue
+    for (int i = 0; i < 5; ++i) MOE_TRY(rec(i));
+    return MOE_OK;
+  }
+  MOE_TRY(check_data_ptr(bs, x, "x"));
+  MOE_TRY(check_data_ptr(bs, w_router, "w_router"));
+  if (b_router) MOE_TRY(check_ptr(b_router, 4, "b_router"));
+  MOE_TRY(check_data_ptr(bs, w1, "w1"));
+  MOE_TRY(check_data_ptr(bs, b1, "b1"));
+  MOE_TRY(check_data_ptr(bs, w2, "w2"));
+  MOE_TRY(check_data_ptr(bs, b2, "b2"));
+  MOE_TRY(check_data_ptr(bs, out, "out"));
+  if (out == x) return fail(MOE_ERR_INVALID_ARGUMENT, "out aliases x");
+  if (topk_ids) MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  if (topk_gates) MOE_TRY(check_ptr(topk_gates, 4, "topk_gates"));
+  if (order) MOE_TRY(check_ptr(order, 4, "order"));
+  if (batch_experts) MOE_TRY(check_ptr(batch_experts, 4, "batch_experts"));
+  const BatchesLayout L = batches_layout(bs, n_batches);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+
+  const int k = bs.top_k, E = bs.n_experts, B = (int)bs.T;
+  const size_t eb = elem_bytes(bs), xrow = (size_t)bs.d_model * eb;
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, L.gates);
+  int32_t* ord = order ? order : at<int32_t>(ws, L.order);
+  const Workspace& W = L.per;
+  hipError_t err;
+
+  MOE_TRY(rec(0));
+  MOE_TRY(do_route(ps, x, w_router, b_router, ids, gates, nullptr, st));  // once for the pool
+  MOE_TRY(rec(1));
+  const char* xb = static_cast<const char*>(x);
+  const int32_t* idsb = ids;
+  const float* gb = gates;
+  char* outb = static_cast<char*>(out);
+  if (consolidate) {
+    if ((err = launch_schedule(ids, (int)ps.T, k, E, ord, st)) != hipSuccess)
+      return device_error(err, "schedule");
+    if ((err = launch_permute_rows(x, ord, at<void>(ws, L.x_perm), ps.T, (int)xrow, false, st)) !=
+            hipSuccess ||
+        (err = launch_permute_rows(ids, ord, at<void>(ws, L.ids_perm), ps.T, k * 4, false, st)) !=
+            hipSuccess ||
+        (err = launch_permute_rows(gates, ord, at<void>(ws, L.gates_perm), ps.T, k * 4, false,
+                                   st)) != hipSuccess)
+      return device_error(err, "batch gather");
+    xb = at<char>(ws, L.x_perm);
+    idsb = at<int32_t>(ws, L.ids_perm);
+    gb = at<float>(ws, L.gates_perm);
+    outb = at<char>(ws, L.out_perm);
+  }
+  if (batch_experts &&
+      (err = launch_batch_experts(idsb, nullptr, B, n_batches, k, E, batch_experts, st)) !=
+          hipSuccess)
+    return device_error(err, "active experts");
+  MOE_TRY(rec(2));
+  for (int32_t b = 0; b < n_batches; ++b) {  // one batch after the other, as a serving loop runs
+    const size_t r0 = (size_t)b * B;
+    const int32_t* ib = idsb + r0 * k;
+    const float* g = gb + r0 * k;
+    MOE_TRY(do_dispatch(bs, ib, g, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
+                        at<int32_t>(ws, W.slot_of), at<int32_t>(ws, W.row_token),
+                        at<uint8_t>(ws, W.drop), ws, st));
+    if ((err = launch_ffn_up(bs, xb + r0 * xrow, at<int32_t>(ws, W.row_token),
+                             at<int32_t>(ws, W.offsets), w1, b1, at<void>(ws, W.h), max_rows(bs),
+                             st)) != hipSuccess)
+      return device_error(err, "expert up-projection");
+    if ((err = launch_ffn_down(bs, at<void>(ws, W.h), at<int32_t>(ws, W.offsets), w2, b2,
+                               at<void>(ws, W.y), max_rows(bs), st)) != hipSuccess)
+      return device_error(err, "expert down-projection");
+    if ((err = launch_combine(bs, xb + r0 * xrow, g, at<int32_t>(ws, W.slot_of),
+                              at<void>(ws, W.y), outb + r0 * xrow, st)) != hipSuccess)
+      return device_error(err, "combine");
+  }
+  MOE_TRY(rec(3));
+  if (consolidate &&
+      (err = launch_permute_rows(outb, ord, out, ps.T, (int)xrow, true, st)) != hipSuccess)
+    return device_error(err, "batch scatter");
+  MOE_TRY(rec(4));
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -619,6 +776,50 @@ moe_status moe_layer_forward_dropless_gated(const moe_shape* shape, const void* 
   return layer_forward_dropless(shape, x, w_router, b_router, w13, nullptr, w2, nullptr, true,
                                 out, topk_ids, topk_gates, expert_counts, pair_rows, ws,
                                 ws_bytes, (hipStream_t)stream, events);
+}
+
+size_t moe_workspace_bytes_batches(const moe_shape* batch_shape, int32_t n_batches) {
+  if (check_batches(batch_shape, n_batches, false) != MOE_OK) return 0;
+  return batches_layout(*batch_shape, n_batches).total;
+}
+
+moe_status moe_schedule_batches(const moe_shape* batch_shape, int32_t n_batches,
+                                const int32_t* topk_ids, int32_t* order,
+                                int32_t* batch_experts, int32_t* orig_batch_experts,
+                                moe_stream_t stream) {
+  MOE_TRY(check_batches(batch_shape, n_batches, true));
+  const moe_shape& bs = *batch_shape;
+  const int64_t T = bs.T * (int64_t)n_batches;
+  if (T == 0) return MOE_OK;  // empty pool: nothing to check or enqueue
+  MOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  MOE_TRY(check_ptr(order, 4, "order"));
+  if (batch_experts) MOE_TRY(check_ptr(batch_experts, 4, "batch_experts"));
+  if (orig_batch_experts) MOE_TRY(check_ptr(orig_batch_experts, 4, "orig_batch_experts"));
+  hipStream_t st = (hipStream_t)stream;
+  const int k = bs.top_k, E = bs.n_experts, B = (int)bs.T;
+  hipError_t err = launch_schedule(topk_ids, (int)T, k, E, order, st);
+  if (err != hipSuccess) return device_error(err, "schedule");
+  if (orig_batch_experts &&
+      (err = launch_batch_experts(topk_ids, nullptr, B, n_batches, k, E, orig_batch_experts,
+                                  st)) != hipSuccess)
+    return device_error(err, "active experts");
+  if (batch_experts &&  // the new batches, read through the order
+      (err = launch_batch_experts(topk_ids, order, B, n_batches, k, E, batch_experts, st)) !=
+          hipSuccess)
+    return device_error(err, "active experts");
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_batches(const moe_shape* batch_shape, int32_t n_batches,
+                                     int32_t consolidate, const void* x, const void* w_router,
+                                     const float* b_router, const void* w1, const void* b1,
+                                     const void* w2, const void* b2, void* out,
+                                     int32_t* topk_ids, float* topk_gates, int32_t* order,
+                                     int32_t* batch_experts, void* ws, size_t ws_bytes,
+                                     moe_stream_t stream, moe_event_t const* events) {
+  return layer_forward_batches(batch_shape, n_batches, consolidate != 0, x, w_router, b_router,
+                               w1, b1, w2, b2, out, topk_ids, topk_gates, order, batch_experts,
+                               ws, ws_bytes, (hipStream_t)stream, events);
 }
 
 }  // extern "C"

@@ -115,4 +115,21 @@ hipError_t launch_ffn_down_pairs(const moe_shape& s, const void* h, const int32_
 hipError_t launch_moe_sum(const moe_shape& s, const void* x, const int32_t* ids,
                           const void* rows, void* out, hipStream_t st);
 
+// ---- batch consolidation
+constexpr int kSchedMaxT = 8192;     // tokens one scheduling workgroup sorts (64 KiB of keys)
+constexpr int kSchedIndexBits = 13;  // token index bits of a sort key
+constexpr int kSchedMaxK = 8;
+int schedule_bits_e(int E);          // bits of an expert id in a sort key (values 0 .. E)
+// order[i] = token at position i: tokens sorted by expert set (ascending ids as a tuple), then
+// by token index; T <= kSchedMaxT, k * schedule_bits_e(E) + kSchedIndexBits <= 64
+hipError_t launch_schedule(const int32_t* ids, int T, int k, int E, int32_t* order,
+                           hipStream_t st);
+// out[b] = distinct experts in [0, E) of the tokens at positions b * B .. b * B + B - 1: token
+// order[i] at position i, or token i when order is NULL (ids [M * B, k])
+hipError_t launch_batch_experts(const int32_t* ids, const int32_t* order, int B, int M, int k,
+                                int E, int32_t* out, hipStream_t st);
+// rows of row_bytes (a multiple of 4): dst[i] = src[idx[i]], or dst[idx[i]] = src[i] (scatter)
+hipError_t launch_permute_rows(const void* src, const int32_t* idx, void* dst, int64_t n,
+                               int row_bytes, bool scatter, hipStream_t st);
+
 }  // namespace moe

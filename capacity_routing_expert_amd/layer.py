@@ -221,3 +221,48 @@ def moe_sum(shape: B.MoeShape, x, ids, pair_rows) -> torch.Tensor:
     out = torch.empty((shape.T, shape.d_model), dtype=pair_rows.dtype, device=pair_rows.device)
     B.moe_sum(shape, x, ids, pair_rows, out)
     return out
+
+
+# ---------------------------------------------------------------- batch consolidation
+def layer_forward_batches(dev: dict, top_k: int, capacity: int, batch_size: int,
+                          consolidate: bool, ws: torch.Tensor | None = None,
+                          events=None) -> dict:
+    """The pool dev["x"] ([n_batches * batch_size, d]) as batches of batch_size tokens, one after
+    another, regrouped by the Token Scheduler when `consolidate`.  Returns out (pool order),
+    ids, gates, order (consolidating only) and the active experts of each batch as run."""
+    x = dev["x"]
+    device = x.device
+    T = x.shape[0]
+    if T % batch_size:
+        raise ValueError("the pool must hold whole batches")
+    M = T // batch_size
+    w2 = dev["w2"]
+    dtype = B.MOE_BF16 if x.dtype == torch.bfloat16 else B.MOE_F32
+    shape = B.make_shape(batch_size, x.shape[1], w2.shape[2], w2.shape[0], top_k, capacity, dtype)
+    if ws is None:
+        ws = torch.empty(max(B.workspace_bytes_batches(shape, M), 256), dtype=torch.uint8,
+                         device=device)
+    res = {
+        "out": torch.empty_like(x),
+        "ids": torch.empty((T, top_k), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "order": torch.empty((T,), dtype=torch.int32, device=device) if consolidate else None,
+        "batch_experts": torch.empty((M,), dtype=torch.int32, device=device),
+    }
+    B.moe_layer_forward_batches(shape, M, consolidate, x, dev["w_router"], dev["b_router"],
+                                dev["w1"], dev["b1"], dev["w2"], dev["b2"], res["out"],
+                                topk_ids=res["ids"], topk_gates=res["gates"], order=res["order"],
+                                batch_experts=res["batch_experts"], ws=ws, events=events)
+    return res
+
+
+def schedule_batches(ids: torch.Tensor, batch_size: int, n_experts: int) -> dict:
+    T, k = ids.shape
+    M = T // batch_size
+    shape = B.make_shape(batch_size, 8, 8, n_experts, k, 0, B.MOE_BF16)
+    res = {"order": torch.empty((T,), dtype=torch.int32, device=ids.device),
+           "batch_experts": torch.empty((M,), dtype=torch.int32, device=ids.device),
+           "orig_batch_experts": torch.empty((M,), dtype=torch.int32, device=ids.device)}
+    B.moe_schedule_batches(shape, M, ids, res["order"], res["batch_experts"],
+                           res["orig_batch_experts"])
+    return res

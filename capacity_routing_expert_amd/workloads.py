@@ -31,6 +31,7 @@ class Workload:
     router_bias: str   # "none" | "normal" | "zipf" | "hot"
     weight_bias_std: float | None  # None -> N(0, 1/sqrt(fan_in)) for biases too
     expert: str = "ffn"  # "ffn": W2 SiLU(W1 x + b1) + b2; "gated": W2 (SiLU(W_gate x) * W_up x)
+    batch_size: int = 0  # > 0: T is a pool of T / batch_size batches run one after another
 
 
 WORKLOADS = {
@@ -53,6 +54,10 @@ WORKLOADS = {
     # the mid layer's routing: bf16, T 4096, 8 experts, top-2, C 1.25 (capacity 1280), no biases
     "gated": Workload("gated", "gated_bf16_T4096_d2048_f768_E8_top2_C1.25", 5,
                       4096, 2048, 768, 8, 2, 1.25, "bf16", "normal", None, "gated"),
+    # a pool of 8 decode batches for the Token Scheduler: each batch is the decode layer's
+    # (64 tokens, d 2048, d_ff 8192, 8 experts, top-2, C 4.0, capacity 64 per batch)
+    "decode_pool": Workload("decode_pool", "decode_pool_bf16_8x64_d2048_f8192_E8_top2_C4.0", 6,
+                            512, 2048, 8192, 8, 2, 4.0, "bf16", "none", 0.02, "ffn", 64),
 }
 
 

@@ -285,6 +285,54 @@ moe_status moe_layer_forward_dropless_gated(const moe_shape* shape, const void* 
                                             size_t ws_bytes, moe_stream_t stream,
                                             moe_event_t const* events);
 
+/* ---- Batch consolidation.  "Token Routing Optimization in Batch Processing" (subtext diagram):
+ * token-level routing stays as it is, and a Token Scheduler regroups the tokens of several
+ * batches so that each new batch activates fewer experts with more tokens per expert (from
+ * every expert active with one token each, to half the experts with two each).  For
+ * decode-sized batches the expert GEMMs stream every active expert's weights once per batch,
+ * so fewer active experts per batch means fewer weight bytes per batch.
+ * Reading taken (the pages give no algorithm): tokens are ordered by their expert set (the k
+ * ids sorted ascending, compared as a tuple), ties by token index, and the ordered pool is cut
+ * into consecutive batches of the original size.
+ * A pool is n_batches batches of batch_shape->T tokens each, stored batch after batch
+ * (pool token i is token i % T of batch i / T). */
+
+/* Workspace bytes for moe_layer_forward_batches; 0 for an invalid shape. */
+size_t moe_workspace_bytes_batches(const moe_shape* batch_shape, int32_t n_batches);
+
+/* The Token Scheduler on a routed pool.
+ *   topk_ids [n_batches * T, k] int32 in (an id outside [0, E) sorts as E and is not counted)
+ *   order    [n_batches * T] int32 out: order[i] = the pool token at position i; new batch b is
+ *            positions b * T .. b * T + T - 1
+ *   batch_experts      [n_batches] int32 out or NULL: distinct experts of each new batch
+ *   orig_batch_experts [n_batches] int32 out or NULL: the same for the original batches
+ * One workgroup sorts the pool: MOE_ERR_UNSUPPORTED for more than 8192 pool tokens, top_k > 8,
+ * or top_k * (bits of E) + 13 > 64.  No workspace. */
+moe_status moe_schedule_batches(const moe_shape* batch_shape, int32_t n_batches,
+                                const int32_t* topk_ids, int32_t* order,
+                                int32_t* batch_experts, int32_t* orig_batch_experts,
+                                moe_stream_t stream);
+
+/* A pool of batches through the capacity layer, one batch after another on the stream, as a
+ * serving loop runs them: the router once over the pool (routing is per token); with
+ * consolidate != 0 the Token Scheduler regroups the pool and the batches run in the new
+ * grouping; each batch then runs dispatch (batch_shape->capacity slots per expert), the expert
+ * FFN and the combine.  out [n_batches * T, d_model] is in the pool's token order either way.
+ * With a capacity of at least T nothing can drop and out does not depend on the grouping.
+ *   topk_ids, topk_gates [n_batches * T, k] optional outputs (pool order)
+ *   order [n_batches * T] optional output, written when consolidating
+ *   batch_experts [n_batches] optional output: distinct experts of each batch as run
+ *   events NULL, or 5 hipEvent_t recorded before routing, after routing, after scheduling and
+ *          regrouping, after the last batch, and after the outputs are back in pool order.
+ * Limits as moe_layer_forward for the pool, and moe_schedule_batches' when consolidating. */
+moe_status moe_layer_forward_batches(const moe_shape* batch_shape, int32_t n_batches,
+                                     int32_t consolidate, const void* x, const void* w_router,
+                                     const float* b_router, const void* w1, const void* b1,
+                                     const void* w2, const void* b2, void* out,
+                                     int32_t* topk_ids, float* topk_gates, int32_t* order,
+                                     int32_t* batch_experts, void* ws, size_t ws_bytes,
+                                     moe_stream_t stream, moe_event_t const* events);
+
 #ifdef __cplusplus
 }
 #endif
