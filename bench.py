@@ -129,11 +129,14 @@ def bench_pool(args, wl, inp):
 
     dev = torch.device("cuda:0")
     d = L.upload(inp, dev)
+    if args.weights == "packed":
+        d = L.pack_weights(d)
     Bsz = wl.batch_size
     M = wl.T // Bsz
     cap = B.capacity(Bsz, wl.top_k, wl.n_experts, wl.capacity_factor)
     dtype = B.MOE_BF16 if wl.dtype == "bf16" else B.MOE_F32
-    shape = B.make_shape(Bsz, wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, cap, dtype)
+    shape = B.make_shape(Bsz, wl.d_model, wl.d_ff, wl.n_experts, wl.top_k, cap, dtype,
+                         d.get("weight_layout", B.MOE_WEIGHTS_ROW_MAJOR))
     ws = torch.empty(max(B.workspace_bytes_batches(shape, M), 256), dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["x"])
     bexp = torch.empty((M,), dtype=torch.int32, device=dev)
@@ -192,7 +195,7 @@ def bench_pool(args, wl, inp):
         "config": {"workload": wl.name, "T": wl.T, "batch_size": Bsz, "n_batches": M,
                    "d_model": wl.d_model, "d_ff": wl.d_ff, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "capacity_factor": wl.capacity_factor, "capacity": cap,
-                   "layout": "batches, Token Scheduler regrouping"},
+                   "layout": "batches, Token Scheduler regrouping", "weights": args.weights},
         "roofline": {"kernel": "k_grouped_gemm skinny tiles (active experts' weight stream), "
                                "batch loop", "bound": "hbm", "achieved": c["weight_GBps"],
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": c["weight_GBps"] / PEAK_HBM_GBS,
@@ -246,6 +249,10 @@ def main():
                     help="compact: the expert FFN runs over the kept rows only; padded: over "
                          "every slot of the fixed per-expert buffers (n_experts x capacity rows); "
                          "dropless: no capacity, every (token, choice) pair in pair order")
+    ap.add_argument("--weights", default="packed", choices=["packed", "rowmajor"],
+                    help="expert weight storage: packed by moe_pack_weights once before timing "
+                         "(K-block-major, the expert GEMMs' read order), or row-major [E, rows, "
+                         "cols]; the results are bit-identical")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -272,6 +279,8 @@ def main():
         bench_pool(args, wl, inp)
         return
     d = L.upload(inp, dev)
+    if args.weights == "packed":  # a one-time preparation of the weights, outside the timing
+        d = L.pack_weights(d)
     shape = L.shape_of(d, wl.top_k, cap)
     padded = args.layout == "padded"
     dropless = args.layout == "dropless"
@@ -408,7 +417,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d_model": dm, "d_ff": ff,
                    "n_experts": wl.n_experts, "top_k": wl.top_k,
                    "capacity_factor": wl.capacity_factor, "capacity": None if dropless else cap,
-                   "layout": args.layout},
+                   "layout": args.layout, "weights": args.weights},
         "expert_gemm_tflops": (gemm1_flop + gemm2_flop) / expert_s / 1e12,
         "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
                                          / PEAK_BF16_TFLOPS,

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_DEVICE"}
 
@@ -28,13 +29,15 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_stat
            "moe_layer_forward_padded", "moe_layer_forward_gated", "moe_workspace_bytes_dropless",
            "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
            "moe_layer_forward_dropless_gated", "moe_workspace_bytes_batches",
-           "moe_schedule_batches", "moe_layer_forward_batches")
+           "moe_schedule_batches", "moe_layer_forward_batches", "moe_packed_weights_bytes",
+           "moe_pack_weights")
 
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -93,6 +96,10 @@ def lib() -> ctypes.CDLL:
         # shape, x, w_router, b_router, w13, w2, out, ids, gates, counts, pair_rows, ws,
         # ws_bytes, stream, events
         L.moe_layer_forward_dropless_gated.argtypes = [SP] + [P] * 11 + [SZ, P, P]
+        L.moe_packed_weights_bytes.argtypes = [SP, I32, I32]
+        L.moe_packed_weights_bytes.restype = SZ
+        L.moe_pack_weights.argtypes = [SP, P, I32, I32, P, P]
+        L.moe_pack_weights.restype = I32
         L.moe_workspace_bytes_batches.argtypes = [SP, I32]
         L.moe_workspace_bytes_batches.restype = SZ
         L.moe_schedule_batches.argtypes = [SP, I32, P, P, P, P, P]
@@ -110,9 +117,9 @@ def lib() -> ctypes.CDLL:
 
 
 def make_shape(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, capacity: int,
-               dtype: int) -> MoeShape:
+               dtype: int, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR) -> MoeShape:
     return MoeShape(int(T), int(d_model), int(d_ff), int(n_experts), int(top_k), int(capacity),
-                    int(dtype))
+                    int(dtype), int(weight_layout))
 
 
 def capacity(T: int, top_k: int, n_experts: int, capacity_factor: float) -> int:
@@ -381,3 +388,17 @@ def moe_layer_forward_batches(batch_shape, n_batches, consolidate, x, w_router, 
         _ptr(topk_gates, "topk_gates", torch.float32), _ptr(order, "order", torch.int32),
         _ptr(batch_experts, "batch_experts", torch.int32), _ptr(ws, "ws", torch.uint8),
         ws.numel(), _stream(stream), _events(events, 5)), "moe_layer_forward_batches")
+
+
+def packed_weights_bytes(shape: MoeShape, rows: int, cols: int) -> int:
+    return int(lib().moe_packed_weights_bytes(ctypes.byref(shape), int(rows), int(cols)))
+
+
+def moe_pack_weights(shape, w, w_packed, stream=None):
+    """w [E, rows, cols] bf16 -> w_packed (at least moe_packed_weights_bytes bytes)."""
+    E, rows, cols = w.shape
+    if w_packed.numel() * w_packed.element_size() < packed_weights_bytes(shape, rows, cols):
+        raise ValueError("w_packed is too small")
+    _check(lib().moe_pack_weights(ctypes.byref(shape), _ptr(w, "w", torch.bfloat16), int(rows),
+                                  int(cols), _ptr(w_packed, "w_packed"), _stream(stream)),
+           "moe_pack_weights")

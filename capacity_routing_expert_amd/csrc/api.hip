@@ -49,6 +49,10 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_UNSUPPORTED, "T * top_k = %lld >= 2^31", (long long)(s->T * s->top_k));
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "dtype %d unknown", s->dtype);
+  if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "weight_layout %d unknown", s->weight_layout);
+  if (s->weight_layout == MOE_WEIGHTS_PACKED && s->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
   if (s->dtype == MOE_BF16 && (s->d_model % 8 != 0 || s->d_ff % 8 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model (%d) and d_ff (%d) multiples of 8",
                 s->d_model, s->d_ff);
@@ -541,6 +545,31 @@ size_t moe_workspace_bytes_dropless(const moe_shape* shape) {
 int64_t moe_max_kept_rows(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return -1;
   return max_rows(*shape);
+}
+
+size_t moe_packed_weights_bytes(const moe_shape* shape, int32_t rows, int32_t cols) {
+  if (check_shape(shape) != MOE_OK || rows < 1 || cols < 1) return 0;
+  return (size_t)packed_weight_elems(shape->n_experts, rows, cols) * 2;
+}
+
+moe_status moe_pack_weights(const moe_shape* shape, const void* w, int32_t rows, int32_t cols,
+                            void* w_packed, moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
+  if (rows < 1 || cols < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "rows = %d, cols = %d must be >= 1", rows, cols);
+  if (cols % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "cols = %d is not a multiple of 8", cols);
+  MOE_TRY(check_ptr(w, 16, "w"));
+  MOE_TRY(check_ptr(w_packed, 16, "w_packed"));
+  const size_t in_bytes = (size_t)s.n_experts * rows * cols * 2;
+  const size_t out_bytes = (size_t)packed_weight_elems(s.n_experts, rows, cols) * 2;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(w_packed);
+  if (a < b + out_bytes && b < a + in_bytes)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_packed overlaps w");
+  hipError_t err = launch_pack_weights(w, w_packed, s.n_experts, rows, cols, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(err, "pack weights");
 }
 
 const char* moe_status_string(int32_t status) {

@@ -58,6 +58,12 @@ constexpr int kActNone = 0;   // Y = acc + bias
 constexpr int kActSilu = 1;   // H = SiLU(acc + bias)
 constexpr int kActGated = 2;  // H = SiLU(gate) * up, gate and up rows of one weight tile, no bias
 
+// Packed expert weights (MOE_WEIGHTS_PACKED): expert e's [rows, K] matrix is stored as
+// [ceil(K / 32)][rows][32], so the 32-K slice of 256 consecutive rows that one stage of a large
+// tile reads is one contiguous 16 KiB run (a row-major stage reads 256 runs of 64 bytes, 4-16
+// KiB apart).  A 64-K stage of a decode tile reads two such blocks.
+constexpr int kPackK = 32;
+
 // where the rows of a tile go
 constexpr int kOutSlots = 0;        // output row = slot (row0 + r)
 constexpr int kOutPairs = 1;        // output row = out_row[slot] (dropless pair order)
@@ -160,7 +166,7 @@ __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) 
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT>
+template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT, bool WP>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
@@ -209,9 +215,17 @@ __device__ __forceinline__ void gemm_tile(
   // LDS row rho of wave half wv = rho / (TN / 2) holds gate row n0 + wv TN/4 + m (m < TN/4) or
   // the up row N + n0 + wv TN/4 + (m - TN/4), so gate block i and up block i + FN/2 of a wave
   // cover the same output features; features past N are out of range.
+  static_assert(BK % kPackK == 0, "a stage reads whole packed blocks");
+  const int NW = GATED ? 2 * N : N;                 // weight rows per expert
+  const int KBW = (K + kPackK - 1) / kPackK;        // packed blocks per expert
   const i32x4_t wsrc =
-      GATED ? make_srd(W + (int64_t)e * 2 * N * K, (uint32_t)(2 * N * K * 2))
-            : make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
+      WP ? make_srd(W + (int64_t)e * KBW * NW * kPackK, (uint32_t)KBW * (uint32_t)NW * (kPackK * 2u))
+      : GATED ? make_srd(W + (int64_t)e * 2 * N * K, (uint32_t)(2 * N * K * 2))
+              : make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
+  // byte offset of K column kc of weight row r (expert-relative) in the packed layout
+  auto packed_off = [&](int r, int kc) {
+    return (uint32_t)(((kc / kPackK) * NW + r) * kPackK + kc % kPackK) * 2u;
+  };
   uint32_t woff[kWLoads];  // byte offset of the lane's chunk at stage 0, or kOutOfRange
 #pragma unroll
   for (int j = 0; j < kWLoads; ++j) {
@@ -221,7 +235,10 @@ __device__ __forceinline__ void gemm_tile(
       const int wv = row / (TN / 2), m = row % (TN / 2);
       const int feat = n0 + wv * (TN / 4) + (m % (TN / 4));
       const int grow = feat + (m >= TN / 4 ? N : 0);
-      woff[j] = feat < N && c * 8 < K ? (uint32_t)(grow * K + c * 8) * 2u : kOutOfRange;
+      woff[j] = feat < N && c * 8 < K ? (WP ? packed_off(grow, c * 8) : (uint32_t)(grow * K + c * 8) * 2u)
+                                      : kOutOfRange;
+    } else if (WP) {
+      woff[j] = n0 + row < N && c * 8 < K ? packed_off(n0 + row, c * 8) : kOutOfRange;
     } else {
       woff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
     }
@@ -265,6 +282,7 @@ __device__ __forceinline__ void gemm_tile(
 #define MOE_STAGE_BASE(S)                                                                      \
   const int k0_ = (S) * BK;                                                                    \
   const uint32_t kb_ = (uint32_t)k0_ * 2u;                                                     \
+  const uint32_t kw_ = WP ? (uint32_t)(k0_ / kPackK) * (uint32_t)NW * (kPackK * 2u) : kb_;     \
   const uint32_t sb_ = lds0 + (uint32_t)(((S) % NS) * kStageBytes)
 #define MOE_ISSUE_LOAD(q)                                                                      \
   do {                                                                                         \
@@ -272,7 +290,7 @@ __device__ __forceinline__ void gemm_tile(
       const int g_ = wave * kWLoads + (q);                                                     \
       const int c_ = pch ^ swz(g_ * kRowsPerLoad + lrow);                                      \
       lds_dma16(wsrc, sb_ + (uint32_t)(g_ * 1024),                                             \
-                (k0_ + c_ * 8 < K && woff[(q)] != kOutOfRange) ? woff[(q)] + kb_ : kOutOfRange); \
+                (k0_ + c_ * 8 < K && woff[(q)] != kOutOfRange) ? woff[(q)] + kw_ : kOutOfRange); \
     } else {                                                                                   \
       const int j_ = (q) - kWLoads;                                                            \
       const int c_ = pch ^ swz((wave * kXLoads + j_) * kRowsPerLoad + lrow);                   \
@@ -455,7 +473,7 @@ __device__ __forceinline__ void gemm_tile(
 // better, so the shorter height must win by 15 %).  The result does not depend on the choice:
 // each output element accumulates the same products in the same K order.
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT>
+          int ACT, int OUT, bool WP>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       int mt, nt, e, row0, rows;
       if (!tile_of_block(tb.MT, NT, mt, nt)) return;
       tb.locate(offsets, lane, mt, e, row0, rows);
-      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT>(
+      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP>(
           A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
       return;
     }
@@ -483,8 +501,45 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
   int mt, nt, e, row0, rows;
   if (!tile_of_block(ta.MT, NT, mt, nt)) return;
   ta.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT>(
+  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP>(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
+}
+
+// ---------------------------------------------------------------- weight packing
+// [E, rows, cols] row-major -> [E, ceil(cols / 32), rows, 32], K columns past cols zero.  One
+// thread per 16-byte chunk of the packed array (cols is a multiple of 8 in bf16).
+__global__ __launch_bounds__(256) void k_pack_weights(const bf16_t* __restrict__ w,
+                                                      bf16_t* __restrict__ wp, int64_t E, int rows,
+                                                      int cols) {
+  const int kb_n = (cols + kPackK - 1) / kPackK;
+  const int64_t chunks = E * kb_n * (int64_t)rows * (kPackK / 8);
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int q = (int)(c % (kPackK / 8));
+    const int64_t r_all = c / (kPackK / 8);  // (e, kb, row)
+    const int row = (int)(r_all % rows);
+    const int64_t ekb = r_all / rows;
+    const int kb = (int)(ekb % kb_n);
+    const int64_t e = ekb / kb_n;
+    const int col = kb * kPackK + q * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col < cols) v = *reinterpret_cast<const uint4*>(w + (e * rows + row) * (int64_t)cols + col);
+    *reinterpret_cast<uint4*>(wp + c * 8) = v;
+  }
+}
+
+int64_t packed_weight_elems(int64_t E, int rows, int cols) {
+  return E * ((cols + kPackK - 1) / kPackK) * (int64_t)rows * kPackK;
+}
+
+hipError_t launch_pack_weights(const void* w, void* wp, int64_t E, int rows, int cols,
+                               hipStream_t st) {
+  const int64_t chunks = packed_weight_elems(E, rows, cols) / 8;
+  if (chunks <= 0) return hipSuccess;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, st, (const bf16_t*)w, (bf16_t*)wp, E, rows, cols);
+  return hipGetLastError();
 }
 
 namespace {
@@ -511,7 +566,7 @@ int compute_units() {
 }
 
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT = kOutSlots>
+          int ACT, int OUT, bool WP>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st,
@@ -522,7 +577,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS, OUT != kOutSlots) : 0;
   constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT>;
+  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT, WP>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -560,31 +615,64 @@ static bool skinny(const moe_shape& s, int64_t rows_ub) {
   return rows_ub <= (int64_t)64 * s.n_experts;
 }
 
+namespace {
+
+// The tile configurations: large batches, and decode-sized ones (skinny); the gated expert's
+// tiles hold a gate row and an up row per output feature.
+template <int ACT, int OUT, bool GATHER, bool WP>
+hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
+                    const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N, int K,
+                    int a_rows, int64_t rows_ub, hipStream_t st, const int32_t* out_row,
+                    const float* row_scale) {
+  if constexpr (ACT == kActGated) {
+    if (small)
+      return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, GATHER, ACT, OUT, WP>(
+          A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  } else {
+    if (small)
+      return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, GATHER, ACT, OUT, WP>(
+          A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  }
+  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, GATHER, ACT, OUT, WP>(
+      A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+}
+
+// the weight layout of the shape picks the kernel
+template <int ACT, int OUT, bool GATHER>
+hipError_t gemm(const moe_shape& s, const void* A, const int32_t* row_token,
+                const int32_t* offsets, const void* W, const void* bias, void* out, int N, int K,
+                int a_rows, int64_t rows_ub, hipStream_t st, const int32_t* out_row = nullptr,
+                const float* row_scale = nullptr) {
+  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
+  const bool small = skinny(s, rows_ub);
+  auto a = (const bf16_t*)A;
+  auto w = (const bf16_t*)W;
+  auto b = (const bf16_t*)bias;
+  auto o = (bf16_t*)out;
+  if (s.weight_layout == MOE_WEIGHTS_PACKED)
+    return run_gemm<ACT, OUT, GATHER, true>(small, a, row_token, offsets, w, b, o, s.n_experts, N,
+                                            K, a_rows, rows_ub, st, out_row, row_scale);
+  return run_gemm<ACT, OUT, GATHER, false>(small, a, row_token, offsets, w, b, o, s.n_experts, N,
+                                           K, a_rows, rows_ub, st, out_row, row_scale);
+}
+
+}  // namespace
+
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, const void* w1, const void* b1, void* h,
                          int64_t rows_ub, hipStream_t st) {
   if (s.dtype != MOE_BF16)
     return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, rows_ub, st);
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActSilu>(
-        (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
-        s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActSilu>(
-      (const bf16_t*)x, row_token, offsets, (const bf16_t*)w1, (const bf16_t*)b1, (bf16_t*)h,
-      s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
+  return gemm<kActSilu, kOutSlots, true>(s, x, row_token, offsets, w1, b1, h, s.d_ff, s.d_model,
+                                         (int)s.T, rows_ub, st);
 }
 
 hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
                            const void* w2, const void* b2, void* y, int64_t rows_ub,
                            hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, rows_ub, st);
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, kActNone>(
-        (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
-        s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, kActNone>(
-      (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, (const bf16_t*)b2, (bf16_t*)y,
-      s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
+  return gemm<kActNone, kOutSlots, false>(s, h, nullptr, offsets, w2, b2, y, s.d_model, s.d_ff,
+                                          (int)rows_ub, rows_ub, st);
 }
 
 // Gated expert (fused-MoE flow diagram, GEMM 1 -> SiLU x mul -> GEMM 2): GEMM 1 over the
@@ -593,29 +681,16 @@ hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* off
 hipError_t launch_ffn_up_gated(const moe_shape& s, const void* x, const int32_t* row_token,
                                const int32_t* offsets, const void* w13, void* h, int64_t rows_ub,
                                hipStream_t st) {
-  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, true, kActGated>(
-        (const bf16_t*)x, row_token, offsets, (const bf16_t*)w13, nullptr, (bf16_t*)h,
-        s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActGated>(
-      (const bf16_t*)x, row_token, offsets, (const bf16_t*)w13, nullptr, (bf16_t*)h,
-      s.n_experts, s.d_ff, s.d_model, (int)s.T, rows_ub, st);
+  return gemm<kActGated, kOutSlots, true>(s, x, row_token, offsets, w13, nullptr, h, s.d_ff,
+                                          s.d_model, (int)s.T, rows_ub, st);
 }
 
 // GEMM 2 without bias (gated expert): Y = H W2^T
 hipError_t launch_ffn_down_nobias(const moe_shape& s, const void* h, const int32_t* offsets,
                                   const void* w2, void* y, int64_t rows_ub, hipStream_t st) {
-  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, false, kActNone>(
-        (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, nullptr, (bf16_t*)y,
-        s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, false, kActNone>(
-      (const bf16_t*)h, nullptr, offsets, (const bf16_t*)w2, nullptr, (bf16_t*)y,
-      s.n_experts, s.d_model, s.d_ff, (int)rows_ub, rows_ub, st);
+  return gemm<kActNone, kOutSlots, false>(s, h, nullptr, offsets, w2, nullptr, y, s.d_model,
+                                          s.d_ff, (int)rows_ub, rows_ub, st);
 }
-
 
 // ---------------------------------------------------------------- dropless pair order
 // Fused-MoE flow diagram (moe-vllm flow): GEMM 1 reads token row p // top_k and writes pair row
@@ -628,42 +703,20 @@ hipError_t launch_ffn_up_pairs(const moe_shape& s, const void* x, const int32_t*
                                const int32_t* sorted_pairs, const int32_t* offsets,
                                const void* w1, const void* b1, void* h, int64_t rows_ub,
                                bool gated, hipStream_t st) {
-  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
-  const bf16_t* xx = (const bf16_t*)x;
-  const bf16_t* w = (const bf16_t*)w1;
-  const bf16_t* b = (const bf16_t*)b1;
-  bf16_t* hh = (bf16_t*)h;
-  const int E = s.n_experts, F = s.d_ff, D = s.d_model, T = (int)s.T;
-  if (gated) {
-    if (skinny(s, rows_ub))
-      return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, true, kActGated, kOutPairs>(
-          xx, row_token, offsets, w, nullptr, hh, E, F, D, T, rows_ub, st, sorted_pairs);
-    return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActGated, kOutPairs>(
-        xx, row_token, offsets, w, nullptr, hh, E, F, D, T, rows_ub, st, sorted_pairs);
-  }
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActSilu, kOutPairs>(
-        xx, row_token, offsets, w, b, hh, E, F, D, T, rows_ub, st, sorted_pairs);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActSilu, kOutPairs>(
-      xx, row_token, offsets, w, b, hh, E, F, D, T, rows_ub, st, sorted_pairs);
+  if (gated)
+    return gemm<kActGated, kOutPairs, true>(s, x, row_token, offsets, w1, nullptr, h, s.d_ff,
+                                            s.d_model, (int)s.T, rows_ub, st, sorted_pairs);
+  return gemm<kActSilu, kOutPairs, true>(s, x, row_token, offsets, w1, b1, h, s.d_ff, s.d_model,
+                                         (int)s.T, rows_ub, st, sorted_pairs);
 }
 
 // h and y hold T * top_k pair rows; b2 may be NULL (gated expert)
 hipError_t launch_ffn_down_pairs(const moe_shape& s, const void* h, const int32_t* sorted_pairs,
                                  const int32_t* offsets, const void* w2, const void* b2,
                                  const float* weights, void* y, int64_t rows_ub, hipStream_t st) {
-  if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
-  const bf16_t* hh = (const bf16_t*)h;
-  const bf16_t* w = (const bf16_t*)w2;
-  const bf16_t* b = (const bf16_t*)b2;
-  bf16_t* yy = (bf16_t*)y;
-  const int E = s.n_experts, F = s.d_ff, D = s.d_model;
-  const int P = (int)(s.T * s.top_k);
-  if (skinny(s, rows_ub))
-    return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, true, kActNone, kOutPairsScaled>(
-        hh, sorted_pairs, offsets, w, b, yy, E, D, F, P, rows_ub, st, sorted_pairs, weights);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, true, kActNone, kOutPairsScaled>(
-      hh, sorted_pairs, offsets, w, b, yy, E, D, F, P, rows_ub, st, sorted_pairs, weights);
+  return gemm<kActNone, kOutPairsScaled, true>(s, h, sorted_pairs, offsets, w2, b2, y, s.d_model,
+                                               s.d_ff, (int)(s.T * s.top_k), rows_ub, st,
+                                               sorted_pairs, weights);
 }
 
 }  // namespace moe

@@ -115,6 +115,11 @@ hipError_t launch_ffn_down_pairs(const moe_shape& s, const void* h, const int32_
 hipError_t launch_moe_sum(const moe_shape& s, const void* x, const int32_t* ids,
                           const void* rows, void* out, hipStream_t st);
 
+// ---- packed expert weights: [E, rows, cols] -> [E, ceil(cols / 32), rows, 32]
+int64_t packed_weight_elems(int64_t E, int rows, int cols);
+hipError_t launch_pack_weights(const void* w, void* wp, int64_t E, int rows, int cols,
+                               hipStream_t st);
+
 // ---- batch consolidation
 constexpr int kSchedMaxT = 8192;     // tokens one scheduling workgroup sorts (64 KiB of keys)
 constexpr int kSchedIndexBits = 13;  // token index bits of a sort key

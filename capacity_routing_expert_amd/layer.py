@@ -29,8 +29,27 @@ def upload(inputs: dict, device="cuda:0") -> dict:
 def shape_of(dev: dict, top_k: int, capacity: int) -> B.MoeShape:
     x, w2 = dev["x"], dev["w2"]
     dtype = B.MOE_BF16 if x.dtype == torch.bfloat16 else B.MOE_F32
-    # d_ff is the activation width: W2 [E, d_model, d_ff] for both expert kinds
-    return B.make_shape(x.shape[0], x.shape[1], w2.shape[2], w2.shape[0], top_k, capacity, dtype)
+    # d_ff is the activation width: W2 [E, d_model, d_ff] for both expert kinds (a dict from
+    # pack_weights states it, its packed w2 being padded)
+    return B.make_shape(x.shape[0], x.shape[1], dev.get("d_ff", w2.shape[2]), w2.shape[0], top_k,
+                        capacity, dtype, dev.get("weight_layout", B.MOE_WEIGHTS_ROW_MAJOR))
+
+
+def pack_weights(dev: dict) -> dict:
+    """A copy of the device dict with w1 and w2 packed by moe_pack_weights (a one-time
+    preparation of the weights).  Each packed array sits in a tensor of shape
+    [E, rows, cols rounded up to 32]; the dict records the layout and d_ff."""
+    out = dict(dev)
+    shape = shape_of(dev, 1, 0)
+    for name in ("w1", "w2"):
+        w = dev[name]
+        E, rows, cols = w.shape
+        wp = torch.empty((E, rows, (cols + 31) // 32 * 32), dtype=w.dtype, device=w.device)
+        B.moe_pack_weights(shape, w, wp)
+        out[name] = wp
+    out["weight_layout"] = B.MOE_WEIGHTS_PACKED
+    out["d_ff"] = dev["w2"].shape[2]
+    return out
 
 
 def workspace(shape: B.MoeShape, device="cuda:0") -> torch.Tensor:
@@ -238,7 +257,8 @@ def layer_forward_batches(dev: dict, top_k: int, capacity: int, batch_size: int,
     M = T // batch_size
     w2 = dev["w2"]
     dtype = B.MOE_BF16 if x.dtype == torch.bfloat16 else B.MOE_F32
-    shape = B.make_shape(batch_size, x.shape[1], w2.shape[2], w2.shape[0], top_k, capacity, dtype)
+    shape = B.make_shape(batch_size, x.shape[1], dev.get("d_ff", w2.shape[2]), w2.shape[0], top_k,
+                         capacity, dtype, dev.get("weight_layout", B.MOE_WEIGHTS_ROW_MAJOR))
     if ws is None:
         ws = torch.empty(max(B.workspace_bytes_batches(shape, M), 256), dtype=torch.uint8,
                          device=device)

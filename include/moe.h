@@ -34,6 +34,8 @@
  *     choice 0 the largest gate.  Biases have the weight dtype; the router bias is fp32.
  *   - Limits: 1 <= top_k <= n_experts <= 256; capacity >= 0; T * top_k < 2^31;
  *     bf16 needs d_model and d_ff multiples of 8 and x smaller than 2 GiB.
+ *   - shape->weight_layout says how w1 (w13) and w2 are stored (row-major as above, or packed
+ *     by moe_pack_weights); every call that reads them honours it.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -58,6 +60,14 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage of the expert weight matrices W1 (or W13) and W2.
+ *   MOE_WEIGHTS_ROW_MAJOR: [E, rows, cols] as in the layouts below.
+ *   MOE_WEIGHTS_PACKED:    [E, ceil(cols / 32), rows, 32], made once by moe_pack_weights: the
+ *                          32-column slices of consecutive rows that the expert GEMMs read
+ *                          together are contiguous.  bf16 only; results are bit-identical to
+ *                          the row-major layout's (same products, same summation order). */
+typedef enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_PACKED = 1 } moe_weight_layout;
+
 /* Problem shape.  `capacity` is the per-expert slot count, normally moe_capacity(...). */
 typedef struct {
   int64_t T;         /* tokens */
@@ -67,6 +77,7 @@ typedef struct {
   int32_t top_k;     /* k */
   int32_t capacity;  /* slots per expert */
   int32_t dtype;     /* moe_dtype of x, weights, biases, y_rows, out */
+  int32_t weight_layout; /* moe_weight_layout of w1 / w13 and w2 */
 } moe_shape;
 
 /* floor(C * T * k / E), evaluated exactly on the binary value of C (no rounding of the
@@ -81,6 +92,19 @@ size_t moe_workspace_bytes(const moe_shape* shape);
 /* Upper bound on the number of kept rows: min(T * k, E * capacity).  y_rows needs this
  * many rows.  -1 for an invalid shape. */
 int64_t moe_max_kept_rows(const moe_shape* shape);
+
+/* Bytes of one packed weight array: E experts of rows x cols, cols rounded up to 32.  0 for an
+ * invalid shape. */
+size_t moe_packed_weights_bytes(const moe_shape* shape, int32_t rows, int32_t cols);
+
+/* Pack an expert weight array for MOE_WEIGHTS_PACKED (a one-time preparation of the weights).
+ *   w        [E, rows, cols] bf16 row-major in (E = shape->n_experts); W1: rows = d_ff, cols =
+ *            d_model; W13 of the gated expert: rows = 2 d_ff; W2: rows = d_model, cols = d_ff
+ *   w_packed [moe_packed_weights_bytes] out: element (e, r, c) at ((e * ceil(cols / 32) + c / 32)
+ *            * rows + r) * 32 + c % 32; columns past cols are zero
+ * bf16 only (shape->dtype); cols a multiple of 8; w_packed must not overlap w. */
+moe_status moe_pack_weights(const moe_shape* shape, const void* w, int32_t rows, int32_t cols,
+                            void* w_packed, moe_stream_t stream);
 
 const char* moe_status_string(int32_t status);
 /* Reason for the last non-OK status returned on the calling thread ("" if none). */
