@@ -115,7 +115,8 @@ Workspace layout(const moe_shape& s, LayoutKind kind) {
   Workspace w;
   const int64_t N = s.T * (int64_t)s.top_k;
   const int64_t E = s.n_experts;
-  const int64_t nb = (N + kDispatchChunk - 1) / kDispatchChunk;
+  const int64_t nb_a = dispatch_blocks(N), nb_p = dispatch_blocks(N, true);
+  const int64_t nb = nb_a > nb_p ? nb_a : nb_p;
   const bool padded = kind == kLayoutPadded, dropless = kind == kLayoutDropless;
   const int64_t rows = padded ? E * s.capacity : dropless ? N : max_rows(s);
   size_t o = 0;

@@ -10,7 +10,7 @@
 // any correct sort gives the same slots.
 //
 // Kernels (N = T*k assignments):
-//   k_dispatch_hist    per block of kDispatchChunk assignments, an expert histogram built
+//   k_dispatch_hist    per block of `chunk` assignments, an expert histogram built
 //                      from wavefront ballots (lanes with equal expert id are matched
 //                      with 9 ballots; one leader per group adds to an LDS counter);
 //   k_dispatch_scatter every block sums the histograms of the blocks before it (bucket
@@ -85,12 +85,13 @@ __device__ void wave_exclusive_scan(int* a, int n, int* total_out) {
 }  // namespace
 
 __global__ __launch_bounds__(256) void k_dispatch_hist(const int32_t* __restrict__ ids, int64_t N,
-                                                       int E, int32_t* __restrict__ blk_hist) {
+                                                       int E, int chunk,
+                                                       int32_t* __restrict__ blk_hist) {
   __shared__ int cnt[260];
   for (int i = threadIdx.x; i <= E; i += 256) cnt[i] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kDispatchChunk;
-  for (int r = 0; r < kDispatchChunk / 256; ++r) {
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  for (int r = 0; r < chunk / 256; ++r) {
     const int64_t i = base + r * 256 + threadIdx.x;
     const bool valid = i < N;
     int e = valid ? ids[i] : 0;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void k_dispatch_hist(const int32_t* __restrict
 
 __global__ __launch_bounds__(256) void k_dispatch_scatter(
     const int32_t* __restrict__ ids, const float* __restrict__ gates, int64_t N, int E, int cap,
-    int nb, const int32_t* __restrict__ blk_hist, uint64_t* __restrict__ keys,
+    int nb, int chunk, const int32_t* __restrict__ blk_hist, uint64_t* __restrict__ keys,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ seg_start,
     int32_t* __restrict__ rank, int32_t* __restrict__ slot_of, uint8_t* __restrict__ drop) {
   __shared__ int s_cnt[260], s_run[260], s_kept[260];
@@ -139,8 +140,9 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
   for (int e = tid; e <= E; e += 256) s_run[e] += s_cnt[e];
   __syncthreads();
 
-  const int64_t base = (int64_t)blockIdx.x * kDispatchChunk;
-  for (int r = 0; r < kDispatchChunk / 256; ++r) {
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  for (int r = 0; r < chunk / 256; ++r) {
+    if (base + r * 256 >= N) break;  // block-uniform
     const int64_t i = base + r * 256 + tid;
     const bool valid = i < N;
     int e = valid ? ids[i] : 0;
@@ -435,17 +437,17 @@ hipError_t launch_pad_layout(const moe_shape& s, const int32_t* ids, const int32
 // p = t * k + c goes to position offsets[e] + #{q < p : ids[q] = e} (a stable counting sort
 // by expert id), with row_token = p / k beside it.  Pairs with ids outside [0, E) land after
 // offsets[E], where no GEMM tile reads.  Same wave-ballot ranking as k_dispatch_scatter; with
-// a single block (N <= kDispatchChunk) the block counts its own chunk, so no histogram kernel
-// runs before it.
+// a single block (N <= chunk) the block counts its own chunk, so no histogram kernel runs
+// before it.
 __global__ __launch_bounds__(256) void k_dispatch_pairs(
-    const int32_t* __restrict__ ids, int64_t N, int E, int k, int nb,
+    const int32_t* __restrict__ ids, int64_t N, int E, int k, int nb, int chunk,
     const int32_t* __restrict__ blk_hist, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ row_token) {
   __shared__ int s_cnt[260], s_run[260];
   __shared__ int wcnt[4][260];
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * kDispatchChunk;
+  const int64_t base = (int64_t)blockIdx.x * chunk;
   for (int e = tid; e <= E; e += 256) {
     s_cnt[e] = 0;
     s_run[e] = 0;
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
       s_run[e] = pre;
     }
   } else {  // the only block: count its own chunk
-    for (int r = 0; r < kDispatchChunk / 256; ++r) {
+    for (int r = 0; r < chunk / 256; ++r) {
       const int64_t i = base + r * 256 + tid;
       const bool valid = i < N;
       int e = valid ? ids[i] : 0;
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
     for (int e = tid; e <= E; e += 256) offsets[e] = s_cnt[e];
   for (int e = tid; e <= E; e += 256) s_run[e] += s_cnt[e];
   __syncthreads();
-  for (int r = 0; r < kDispatchChunk / 256; ++r) {
+  for (int r = 0; r < chunk / 256; ++r) {
     if (base + r * 256 >= N) break;  // block-uniform
     const int64_t i = base + r * 256 + tid;
     const bool valid = i < N;
@@ -508,15 +510,31 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
   }
 }
 
+int dispatch_chunk(int64_t n, bool pairs) {
+  if (pairs && n <= kDispatchChunk) return kDispatchChunk;  // one block, no histogram launch
+  // about 32 blocks: every block sums the histograms of the blocks before it, so many more
+  // blocks cost more in those sums than their extra parallelism saves
+  int64_t c = (n / 32 + 255) / 256 * 256;
+  if (c < 256) c = 256;
+  if (c > kDispatchChunk) c = kDispatchChunk;
+  return (int)c;
+}
+
+int64_t dispatch_blocks(int64_t n, bool pairs) {
+  const int c = dispatch_chunk(n, pairs);
+  return (n + c - 1) / c;
+}
+
 hipError_t launch_dispatch_pairs(const moe_shape& s, const int32_t* ids, int32_t* counts,
                                  int32_t* offsets, int32_t* sorted_pairs, int32_t* row_token,
                                  int32_t* blk_hist, hipStream_t st) {
   const int64_t N = s.T * (int64_t)s.top_k;
   const int E = s.n_experts;
-  const int nb = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
+  const int chunk = dispatch_chunk(N, true);
+  const int nb = (int)dispatch_blocks(N, true);
   if (nb > 1)
-    hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, blk_hist);
-  hipLaunchKernelGGL(k_dispatch_pairs, dim3(nb), dim3(256), 0, st, ids, N, E, s.top_k, nb,
+    hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, chunk, blk_hist);
+  hipLaunchKernelGGL(k_dispatch_pairs, dim3(nb), dim3(256), 0, st, ids, N, E, s.top_k, nb, chunk,
                      nb > 1 ? (const int32_t*)blk_hist : nullptr, counts, offsets, sorted_pairs,
                      row_token);
   return hipGetLastError();
@@ -533,10 +551,11 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
                        s.top_k, s.capacity, counts, offsets, slot_of, row_token, drop);
     return hipGetLastError();
   }
-  const int nb = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
-  hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, blk_hist);
+  const int chunk = dispatch_chunk(N);
+  const int nb = (int)dispatch_blocks(N);
+  hipLaunchKernelGGL(k_dispatch_hist, dim3(nb), dim3(256), 0, st, ids, N, E, chunk, blk_hist);
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(nb), dim3(256), 0, st, ids, gates, N, E, s.capacity,
-                     nb, blk_hist, keys, counts, offsets, seg_start, rank, slot_of, drop);
+                     nb, chunk, blk_hist, keys, counts, offsets, seg_start, rank, slot_of, drop);
   const int tiles_ub = (int)((N + kTile - 1) / kTile) + E;  // >= sum over experts of tiles
   hipLaunchKernelGGL(k_dispatch_tilesort, dim3(tiles_ub), dim3(kTile), 0, st, keys, counts,
                      seg_start, E);

@@ -55,7 +55,12 @@ struct Workspace {
   size_t total;
 };
 
-constexpr int kDispatchChunk = 2048;  // assignments per block in the count/scatter kernels
+constexpr int kDispatchChunk = 2048;  // most assignments per block in the count/scatter kernels
+// Assignments per block of the count/scatter kernels for n assignments: a multiple of 256 near
+// n / 32, from 256 up to kDispatchChunk.  pairs: the pair dispatch, which runs as one block up
+// to kDispatchChunk assignments.
+int dispatch_chunk(int64_t n, bool pairs = false);
+int64_t dispatch_blocks(int64_t n, bool pairs = false);
 
 int64_t max_rows(const moe_shape& s);
 enum LayoutKind { kLayoutCompact = 0, kLayoutPadded = 1, kLayoutDropless = 2 };
