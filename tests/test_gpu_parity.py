@@ -500,3 +500,42 @@ def test_gated_config_end_to_end():
     assert err <= P.TOL[dt]
     del dev, res
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- graph capture
+@pytest.mark.parametrize("key", ["mid", "decode"])
+def test_layer_forward_in_a_captured_graph(key):
+    """The layer enqueues no host synchronisation, allocation or memset, so a HIP graph can
+    capture it: every replay (with eager work and synchronisations between replays) returns
+    the eager call's bits."""
+    inp, ref, cap = case(key)
+    wl = inp["workload"]
+    dev = L.upload(inp, DEV)
+    shape = L.shape_of(dev, wl.top_k, cap)
+    ws = L.workspace(shape, DEV)
+    out = torch.empty_like(dev["x"])
+    ids = torch.empty((wl.T, wl.top_k), dtype=torch.int32, device=DEV)
+    eager = L.layer_forward(dev, wl.top_k, cap)
+    s = torch.cuda.Stream()
+    args = (shape, dev["x"], dev["w_router"], dev["b_router"], dev["w1"], dev["b1"], dev["w2"],
+            dev["b2"], out)
+    with torch.cuda.stream(s):
+        B.moe_layer_forward(*args, topk_ids=ids, ws=ws, stream=s)  # warm on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.moe_layer_forward(*args, topk_ids=ids, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        ids.fill_(-7)
+        ws.fill_(0xA5)  # stale workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager["out"].view(torch.int16)), f"replay {r}"
+        assert torch.equal(ids, eager["ids"]), f"replay {r} ids"
+        L.layer_forward(dev, wl.top_k, cap)  # eager work between replays
+        torch.cuda.synchronize()
+    del g, dev, ws, out
+    torch.cuda.empty_cache()
