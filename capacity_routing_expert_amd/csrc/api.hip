@@ -53,6 +53,12 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "weight_layout %d unknown", s->weight_layout);
   if (s->weight_layout == MOE_WEIGHTS_PACKED && s->dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
+  // a packed expert matrix (up to 2 d_ff x d_model for the gated W13) is addressed with 32-bit
+  // byte offsets as a whole
+  if (s->weight_layout == MOE_WEIGHTS_PACKED &&
+      (int64_t)2 * ((s->d_ff + 31) / 32 * 32) * ((s->d_model + 31) / 32 * 32) * 2 >= ((int64_t)1 << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "packed expert weights of %d x %d: 4 GiB or more per expert",
+                s->d_ff, s->d_model);
   if (s->dtype == MOE_BF16 && (s->d_model % 8 != 0 || s->d_ff % 8 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model (%d) and d_ff (%d) multiples of 8",
                 s->d_model, s->d_ff);

@@ -83,3 +83,27 @@ def test_pointer_errors_before_any_launch(lib):
     assert "workspace" in B.last_error()
     assert lib.moe_combine(ctypes.byref(s), p, p, p, p, p, None) == 1  # out aliases x
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_weight_layout_checks_on_the_host(lib):
+    """The packed weight layout is checked before anything runs: unknown layout values, fp32,
+    and experts too large for 32-bit offsets are refused; the packed size rounds columns up to
+    whole 32-column blocks."""
+    ok = B.make_shape(64, 2048, 8192, 8, 2, 32, B.MOE_BF16, B.MOE_WEIGHTS_PACKED)
+    assert B.workspace_bytes(ok) > 0
+    assert B.packed_weights_bytes(ok, 8192, 2048) == 8 * 8192 * 2048 * 2
+    assert B.packed_weights_bytes(ok, 136, 72) == 8 * 3 * 136 * 32 * 2  # 72 -> 3 blocks of 32
+    assert B.workspace_bytes(B.make_shape(64, 2048, 8192, 8, 2, 32, B.MOE_BF16, 2)) == 0
+    assert "weight_layout" in B.last_error()
+    assert B.workspace_bytes(B.make_shape(8, 8, 8, 4, 1, 2, B.MOE_F32, B.MOE_WEIGHTS_PACKED)) == 0
+    assert "bf16" in B.last_error()
+    assert B.workspace_bytes(B.make_shape(8, 32768, 32768, 4, 1, 0, B.MOE_BF16,
+                                          B.MOE_WEIGHTS_PACKED)) == 0
+    assert "4 GiB" in B.last_error()
+    # packing refuses fp32 and ragged columns before launching anything
+    f32 = B.make_shape(8, 8, 8, 2, 1, 0, B.MOE_F32)
+    assert lib.moe_pack_weights(ctypes.byref(f32), ctypes.c_void_p(16), 8, 8, ctypes.c_void_p(4096),
+                                None) == 2
+    bf = B.make_shape(8, 8, 8, 2, 1, 0, B.MOE_BF16)
+    assert lib.moe_pack_weights(ctypes.byref(bf), ctypes.c_void_p(16), 8, 12, ctypes.c_void_p(4096),
+                                None) == 2
