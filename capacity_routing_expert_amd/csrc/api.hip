@@ -62,10 +62,10 @@ moe_status check_shape(const moe_shape* s) {
   if (s->dtype == MOE_BF16 && (s->d_model % 8 != 0 || s->d_ff % 8 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d_model (%d) and d_ff (%d) multiples of 8",
                 s->d_model, s->d_ff);
-  // the expert GEMMs address x and the weight / activation tiles with 32-bit byte offsets
-  if (s->dtype == MOE_BF16 && s->T * (int64_t)s->d_model * 2 >= ((int64_t)1 << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "bf16 x of %lld bytes: must be below 2 GiB",
-                (long long)(s->T * (int64_t)s->d_model * 2));
+  // the router and the expert GEMMs address x with 32-bit byte offsets
+  const int64_t x_bytes = s->T * (int64_t)s->d_model * (s->dtype == MOE_BF16 ? 2 : 4);
+  if (x_bytes >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "x of %lld bytes: must be below 2 GiB", (long long)x_bytes);
   if (s->dtype == MOE_BF16 && (int64_t)256 * (s->d_model > s->d_ff ? s->d_model : s->d_ff) * 2 >=
                                   ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "d_model / d_ff too large for 32-bit tile offsets");

@@ -28,6 +28,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2_t));
 }
+// Buffer resource over `bytes` bytes at `base` (wave-uniform): a load at a byte offset at or past
+// `bytes` (kBufferOOR, for one) reads zeros, so guarded loads need no branch.
+constexpr uint32_t kBufferOOR = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ float load_as_f32(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
 

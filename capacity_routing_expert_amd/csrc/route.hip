@@ -107,25 +107,27 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 template <typename TIn>
 struct Chunk8;
+// The loads go through buffer resources over the whole matrix: a guarded-off chunk reads zeros
+// from an out-of-range offset instead of sitting in a branch, so the compiler can count the
+// loads in flight and wait only for the ones it needs (a predicated load made it wait for all).
 template <>
 struct Chunk8<bf16_t> {  // 8 bf16 columns as one 16-byte load (d % 8 == 0 for bf16)
   uint4 v;
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ m, bool ok, int64_t row, int c,
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t m, bool ok, int64_t row, int c,
                                        int d) {
-    v = ok && c * 8 < d ? *reinterpret_cast<const uint4*>(m + row * d + (int64_t)c * 8)
-                        : make_uint4(0, 0, 0, 0);
+    v = buffer_load16(m, ok && c * 8 < d ? (uint32_t)((row * d + (int64_t)c * 8) * 2) : kBufferOOR);
   }
   __device__ __forceinline__ void widen(double* o) const { widen_bf16x8(v, o); }
 };
 template <>
 struct Chunk8<float> {  // 8 fp32 columns, each guarded (any d)
   float v[8];
-  __device__ __forceinline__ void load(const float* __restrict__ m, bool ok, int64_t row, int c,
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t m, bool ok, int64_t row, int c,
                                        int d) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int col = c * 8 + u;
-      v[u] = ok && col < d ? m[row * d + col] : 0.0f;
+      v[u] = buffer_load_f32(m, ok && col < d ? (uint32_t)((row * d + col) * 4) : kBufferOOR);
     }
   }
   __device__ __forceinline__ void widen(double* o) const {
@@ -134,7 +136,7 @@ struct Chunk8<float> {  // 8 fp32 columns, each guarded (any d)
   }
 };
 
-template <typename TIn, int R, int EBG, int NW>
+template <typename TIn, int R, int EBG, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void k_route_mfma(
     const TIn* __restrict__ x, const TIn* __restrict__ w, const float* __restrict__ b_router,
     int64_t T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
@@ -149,6 +151,9 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma(
   const int64_t tok0 = (int64_t)blockIdx.x * TT;
   const int d8 = (d + 7) / 8, nq = (d8 + 3) / 4;
   const int EB = (E + 15) / 16;
+  // x and the router weights (< 2 GiB each, host-checked)
+  const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x, (uint32_t)(T * d * (int64_t)sizeof(TIn)));
+  const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(w, (uint32_t)((int64_t)E * d * sizeof(TIn)));
 
   for (int b0 = 0; b0 < EB; b0 += EBG) {
     f64x4_t acc[R][EBG];
@@ -157,38 +162,43 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma(
 #pragma unroll
       for (int bb = 0; bb < EBG; ++bb) acc[r][bb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
-    // wave w takes chunk quads w, w + NW, ...; the raw loads of the next quad are issued
-    // before the MFMAs of the current one (quads past the end load zeros)
-    Chunk8<TIn> xr[R], wr[EBG];
-    auto load = [&](int cq) {
+    // wave w takes chunk quads w, w + NW, ... in that order, with PF quads in flight: the raw
+    // loads of quad cq + PF NW are issued as soon as quad cq is widened (quads past the end
+    // load zeros, whose exact zero products leave the sums as they are)
+    Chunk8<TIn> xr[PF][R], wr[PF][EBG];
+    auto load = [&](int p, int cq) {
       const int c = cq * 4 + q;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int64_t t = tok0 + 16 * r + i;
-        xr[r].load(x, cq < nq && t < T, t, c, d);
+        xr[p][r].load(xs, cq < nq && t < T, t, c, d);
       }
 #pragma unroll
       for (int bb = 0; bb < EBG; ++bb) {
         const int e = (b0 + bb) * 16 + i;
-        wr[bb].load(w, cq < nq && e < E, e, c, d);
+        wr[p][bb].load(ws, cq < nq && e < E, e, c, d);
       }
     };
-    load(wave);
-    for (int cq = wave; cq < nq; cq += NW) {
-      double xa[R][8], wb[EBG][8];
 #pragma unroll
-      for (int r = 0; r < R; ++r) xr[r].widen(xa[r]);
+    for (int p = 0; p < PF; ++p) load(p, wave + p * NW);
+    for (int cq0 = wave; cq0 < nq; cq0 += PF * NW) {
 #pragma unroll
-      for (int bb = 0; bb < EBG; ++bb) wr[bb].widen(wb[bb]);
-      load(cq + NW);
+      for (int p = 0; p < PF; ++p) {
+        double xa[R][8], wb[EBG][8];
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8)
+        for (int r = 0; r < R; ++r) xr[p][r].widen(xa[r]);
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int bb = 0; bb < EBG; ++bb) wr[p][bb].widen(wb[bb]);
+        load(p, cq0 + (p + PF) * NW);
 #pragma unroll
-          for (int bb = 0; bb < EBG; ++bb)
-            acc[r][bb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[r][s8], wb[bb][s8], acc[r][bb],
-                                                              0, 0, 0);
+        for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int bb = 0; bb < EBG; ++bb)
+              acc[r][bb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[r][s8], wb[bb][s8],
+                                                                acc[r][bb], 0, 0, 0);
+      }
     }
 
     // lane l, register j of a tile holds token 4 j + l / 16, expert l % 16 of the tile
@@ -236,8 +246,11 @@ template <typename TIn, int EBG>
 hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                         int32_t* ids, float* gates, float* logits, hipStream_t st) {
   constexpr int R = 1, NW = 8, TT = 16 * R;
+  // chunk quads in flight per wave besides the one being multiplied: with branch-free loads one
+  // is enough (4 and 8 measured no faster, and 8 slower on the large layers)
+  constexpr int PF = 1;
   const size_t lds = (size_t)8 * ((NW - 1) * R * EBG * 256 + (size_t)s.n_experts * TT);
-  auto kern = k_route_mfma<TIn, R, EBG, NW>;
+  auto kern = k_route_mfma<TIn, R, EBG, NW, PF>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,

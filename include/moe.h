@@ -33,7 +33,7 @@
  *     b2 [E, d_model]; x and out [T, d_model]; per-assignment arrays [T, top_k], with
  *     choice 0 the largest gate.  Biases have the weight dtype; the router bias is fp32.
  *   - Limits: 1 <= top_k <= n_experts <= 256; capacity >= 0; T * top_k < 2^31;
- *     bf16 needs d_model and d_ff multiples of 8 and x smaller than 2 GiB.
+ *     bf16 needs d_model and d_ff multiples of 8; x must be smaller than 2 GiB.
  *   - shape->weight_layout says how w1 (w13) and w2 are stored (row-major as above, or packed
  *     by moe_pack_weights); every call that reads them honours it.
  */
