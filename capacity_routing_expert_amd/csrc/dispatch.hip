@@ -215,22 +215,33 @@ __global__ __launch_bounds__(kTile) void k_dispatch_tilesort(uint64_t* __restric
   const int m = min(kTile, n - a * kTile);
   const int64_t base = (int64_t)seg_start[e] + (int64_t)a * kTile;
   const int t = threadIdx.x;
-  sk[t] = t < m ? keys[base + t] : ~0ull;
-  __syncthreads();
+  uint64_t v = t < m ? keys[base + t] : ~0ull;  // padding sorts last
+  // bitonic network, one key per thread: partners closer than 64 are in the same wave and trade
+  // keys by shuffle, farther ones through LDS
   for (int size = 2; size <= kTile; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int partner = t ^ stride;
-      const uint64_t mine = sk[t], other = sk[partner];
-      const bool up = (t & size) == 0;
-      const bool lower = t < partner;
+      uint64_t other;
+      if (stride >= 64) {
+        sk[t] = v;
+        __syncthreads();
+        other = sk[t ^ stride];
+        __syncthreads();
+      } else {
+        other = __shfl_xor(v, stride, 64);
+      }
+      const bool up = (t & size) == 0, lower = (t & stride) == 0;
       // keep the smaller key at the lower index of an ascending pair, the larger otherwise
-      const uint64_t keep = (lower == up) ? (mine < other ? mine : other) : (mine < other ? other : mine);
-      __syncthreads();
-      sk[t] = keep;
-      __syncthreads();
+      v = (lower == up) ? (v < other ? v : other) : (v < other ? other : v);
     }
   }
-  if (t < m) keys[base + t] = sk[t];
+  if (t < m) keys[base + t] = v;
+}
+
+// 8 bytes at byte offset `off` of a buffer resource (zeros past its range)
+__device__ __forceinline__ uint64_t buffer_load_u64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return ((uint64_t)v[1] << 32) | v[0];
 }
 
 __global__ __launch_bounds__(kTile) void k_dispatch_rank(const uint64_t* __restrict__ keys,
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kTile) void k_dispatch_rank(const uint64_t* __restr
                                                          const int32_t* __restrict__ seg_start,
                                                          int E, int32_t* __restrict__ rank) {
   __shared__ int s_pre[260];
-  __shared__ uint64_t sk[kTile];
+  __shared__ uint64_t sk[kTilesPerItem * kTile];  // the item's group of sorted tiles
   // work items of expert e: (own tile a, group g of kTilesPerItem tiles)
   expert_prefix(counts, E, s_pre, [](int n) {
     const int nt = tiles_of(n);
@@ -256,20 +267,33 @@ __global__ __launch_bounds__(kTile) void k_dispatch_rank(const uint64_t* __restr
     const int own_pos = a * kTile + t;
     const uint64_t mine = own_pos < n ? keys[seg + own_pos] : ~0ull;
     int cnt = 0;
-    const int b_end = min(nt, (g + 1) * kTilesPerItem);
-    for (int b = g * kTilesPerItem; b < b_end; ++b) {
+    const int b0 = g * kTilesPerItem, b_end = min(nt, b0 + kTilesPerItem);
+    // all tiles of the group in one round trip: branch-free loads (a tile's resource covers
+    // only its keys; past them, and past the group, reads zeros the searches never reach)
+    uint64_t kv[kTilesPerItem];
+#pragma unroll
+    for (int bb = 0; bb < kTilesPerItem; ++bb) {
+      const int b = b0 + bb;
+      const int mb = b < b_end ? min(kTile, n - b * kTile) : 0;
+      const __amdgpu_buffer_rsrc_t tile =
+          buffer_rsrc(keys + seg + (int64_t)(b < b_end ? b : b0) * kTile, (uint32_t)mb * 8u);
+      kv[bb] = buffer_load_u64(tile, (uint32_t)t * 8u);
+    }
+    __syncthreads();  // the previous item's searches are done with sk
+#pragma unroll
+    for (int bb = 0; bb < kTilesPerItem; ++bb) sk[bb * kTile + t] = kv[bb];
+    __syncthreads();
+    for (int b = b0; b < b_end; ++b) {
       if (b == a) {
         cnt += t;  // sorted own tile: t keys are smaller
         continue;
       }
       const int mb = min(kTile, n - b * kTile);
-      __syncthreads();
-      sk[t] = t < mb ? keys[seg + (int64_t)b * kTile + t] : ~0ull;
-      __syncthreads();
-      int lo = 0, hi = mb;  // first index with sk[idx] >= mine
+      const uint64_t* st = sk + (b - b0) * kTile;
+      int lo = 0, hi = mb;  // first index with st[idx] >= mine
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (sk[mid] < mine) lo = mid + 1; else hi = mid;
+        if (st[mid] < mine) lo = mid + 1; else hi = mid;
       }
       cnt += lo;
     }
