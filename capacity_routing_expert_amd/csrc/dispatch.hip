@@ -82,6 +82,42 @@ __device__ void wave_exclusive_scan(int* a, int n, int* total_out) {
   if (total_out) *total_out = __shfl(inc, 63, 64);
 }
 
+constexpr int kMaxRounds = kDispatchChunk / 256;  // 256-assignment rounds per block chunk
+
+// Expert ids of rounds 0 .. rounds-1 of the chunk at `base`, one per thread and round, all
+// loads issued before the first is used; ids past N read as 0 (the callers test i < N).
+__device__ __forceinline__ void load_chunk_ids(const int32_t* __restrict__ ids, int64_t N,
+                                               int64_t base, int rounds,
+                                               int (&ev)[kMaxRounds]) {
+  const int64_t n = N - base < (int64_t)rounds * 256 ? N - base : (int64_t)rounds * 256;
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(ids + base, (uint32_t)(n * 4));
+#pragma unroll
+  for (int q = 0; q < kMaxRounds; ++q)
+    ev[q] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        r, q < rounds ? (uint32_t)((q * 256 + (int)threadIdx.x) * 4) : kBufferOOR, 0, 0);
+}
+
+// Sum over blocks b < nb of blk_hist[b][e] (total) and over b < before (prefix), with the
+// loads issued eight at a time (blocks past nb read as 0).
+__device__ __forceinline__ void hist_sums(const int32_t* __restrict__ blk_hist, int nb, int E,
+                                          int e, int before, int& tot, int& pre) {
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(blk_hist, (uint32_t)(nb * (E + 1) * 4));
+  tot = 0;
+  pre = 0;
+  for (int b0 = 0; b0 < nb; b0 += 8) {
+    int h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      h[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+          r, (uint32_t)(((b0 + j) * (E + 1) + e) * 4), 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (b0 + j < before) pre += h[j];
+      tot += h[j];
+    }
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void k_dispatch_hist(const int32_t* __restrict__ ids, int64_t N,
@@ -91,10 +127,15 @@ __global__ __launch_bounds__(256) void k_dispatch_hist(const int32_t* __restrict
   for (int i = threadIdx.x; i <= E; i += 256) cnt[i] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * chunk;
-  for (int r = 0; r < chunk / 256; ++r) {
+  const int rounds = chunk / 256;
+  int ev[kMaxRounds];
+  load_chunk_ids(ids, N, base, rounds, ev);
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    if (r >= rounds) break;  // uniform
     const int64_t i = base + r * 256 + threadIdx.x;
     const bool valid = i < N;
-    int e = valid ? ids[i] : 0;
+    int e = valid ? ev[r] : 0;
     if (e < 0 || e >= E) e = E;  // out-of-range ids go to an overflow bucket
     const uint64_t peers = match_key(e, valid);
     if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&cnt[e], __popcll(peers));
@@ -111,13 +152,21 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
   __shared__ int s_cnt[260], s_run[260], s_kept[260];
   __shared__ int wcnt[4][260];
   const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  const int rounds = chunk / 256;
+  int ev[kMaxRounds];
+  float gv[kMaxRounds];
+  load_chunk_ids(ids, N, base, rounds, ev);
+  {
+    const int64_t n = N - base < (int64_t)chunk ? N - base : (int64_t)chunk;
+    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(gates + base, (uint32_t)(n * 4));
+#pragma unroll
+    for (int q = 0; q < kMaxRounds; ++q)
+      gv[q] = buffer_load_f32(gr, q < rounds ? (uint32_t)((q * 256 + tid) * 4) : kBufferOOR);
+  }
   for (int e = tid; e <= E; e += 256) {
-    int tot = 0, pre = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int h = blk_hist[(int64_t)b * (E + 1) + e];
-      if (b < (int)blockIdx.x) pre += h;
-      tot += h;
-    }
+    int tot, pre;
+    hist_sums(blk_hist, nb, E, e, (int)blockIdx.x, tot, pre);
     s_cnt[e] = tot;
     s_run[e] = pre;
     s_kept[e] = e < E ? min(tot, cap) : 0;
@@ -140,12 +189,12 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
   for (int e = tid; e <= E; e += 256) s_run[e] += s_cnt[e];
   __syncthreads();
 
-  const int64_t base = (int64_t)blockIdx.x * chunk;
-  for (int r = 0; r < chunk / 256; ++r) {
-    if (base + r * 256 >= N) break;  // block-uniform
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    if (r >= rounds || base + r * 256 >= N) break;  // block-uniform
     const int64_t i = base + r * 256 + tid;
     const bool valid = i < N;
-    int e = valid ? ids[i] : 0;
+    int e = valid ? ev[r] : 0;
     if (e < 0 || e >= E) e = E;
     const uint64_t peers = match_key(e, valid);
     const int wrank = __popcll(peers & lanemask_lt());
@@ -156,7 +205,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
       for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
       rank[pos] = 0;
       if (e < E) {
-        keys[pos] = sort_key(gates[i], (uint32_t)i);
+        keys[pos] = sort_key(gv[r], (uint32_t)i);
       } else {
         keys[pos] = ~0ull;
         slot_of[i] = -1;
@@ -472,6 +521,9 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
   __shared__ int wcnt[4][260];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t base = (int64_t)blockIdx.x * chunk;
+  const int rounds = chunk / 256;
+  int ev[kMaxRounds];
+  load_chunk_ids(ids, N, base, rounds, ev);
   for (int e = tid; e <= E; e += 256) {
     s_cnt[e] = 0;
     s_run[e] = 0;
@@ -480,20 +532,18 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
   __syncthreads();
   if (blk_hist) {  // totals and the prefix of the blocks before this one
     for (int e = tid; e <= E; e += 256) {
-      int tot = 0, pre = 0;
-      for (int b = 0; b < nb; ++b) {
-        const int h = blk_hist[(int64_t)b * (E + 1) + e];
-        if (b < (int)blockIdx.x) pre += h;
-        tot += h;
-      }
+      int tot, pre;
+      hist_sums(blk_hist, nb, E, e, (int)blockIdx.x, tot, pre);
       s_cnt[e] = tot;
       s_run[e] = pre;
     }
   } else {  // the only block: count its own chunk
-    for (int r = 0; r < chunk / 256; ++r) {
+#pragma unroll
+    for (int r = 0; r < kMaxRounds; ++r) {
+      if (r >= rounds) break;  // uniform
       const int64_t i = base + r * 256 + tid;
       const bool valid = i < N;
-      int e = valid ? ids[i] : 0;
+      int e = valid ? ev[r] : 0;
       if (e < 0 || e >= E) e = E;
       const uint64_t peers = match_key(e, valid);
       if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&s_cnt[e], __popcll(peers));
@@ -509,11 +559,12 @@ __global__ __launch_bounds__(256) void k_dispatch_pairs(
     for (int e = tid; e <= E; e += 256) offsets[e] = s_cnt[e];
   for (int e = tid; e <= E; e += 256) s_run[e] += s_cnt[e];
   __syncthreads();
-  for (int r = 0; r < chunk / 256; ++r) {
-    if (base + r * 256 >= N) break;  // block-uniform
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    if (r >= rounds || base + r * 256 >= N) break;  // block-uniform
     const int64_t i = base + r * 256 + tid;
     const bool valid = i < N;
-    int e = valid ? ids[i] : 0;
+    int e = valid ? ev[r] : 0;
     if (e < 0 || e >= E) e = E;
     const uint64_t peers = match_key(e, valid);
     const int wrank = __popcll(peers & lanemask_lt());
