@@ -12,8 +12,8 @@
 // for every kept slot s of expert e.  Both operands are K-contiguous ("NT" GEMM), the layout
 // v_mfma_f32_32x32x16_bf16 wants: each lane feeds 8 consecutive K values of one row.
 //
-// Block tile: TN output features x TM slots, 4 waves of (TN/2) x (TM/2), each made of 32x32
-// MFMA blocks with fp32 accumulators in AGPRs.  The weights are the MFMA "A" operand, the
+// Block tile: TN output features x TM slots, 4 waves of (TN/2) x (TM/2) (or of (TN/4) x 32 for
+// 32-slot tiles), each made of 32x32 MFMA blocks with fp32 accumulators in AGPRs.  The weights are the MFMA "A" operand, the
 // token rows the "B" operand.
 //
 // K pipeline: stages of BK = 32 K (64-byte rows) in a ring of NS = 4 stage buffers in LDS
@@ -172,7 +172,8 @@ __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
     const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
     int a_rows, int e, int row0, int rows, int n0) {
-  constexpr int WN = 2, WM = 2;              // waves along features / slots
+  // waves along slots / features: 2 x 2, or 1 x 4 for 32-slot tiles
+  constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
   constexpr int KS = BK / 16;                // 16-K MFMA steps per stage
@@ -609,8 +610,12 @@ hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t*
 
 // Few rows per expert (decode-sized batches): the layer is bound by streaming the expert
 // weights, and 256 x 256 tiles would leave most compute units idle (8 experts x d_model / 256
-// tiles for the down-projection).  64 x 64 tiles with 64-deep stages and two blocks per compute
-// unit put every unit to work on its own weight rows with 48 KiB of loads in flight.
+// tiles for the down-projection).  Small tiles with 64-deep stages and two blocks per compute
+// unit put every unit to work on its own weight rows: 64 x 64 for the down-projection, 128 x 32
+// (128 weight rows, 32 slots) for the up-projection, whose d_ff / 128 feature tiles per expert
+// still fill the GPU.  An expert with more than 32 kept rows then takes several token tiles,
+// which stream its weight rows again (mostly from L2: the tiles of one weight tile run side by
+// side on one XCD).
 static bool skinny(const moe_shape& s, int64_t rows_ub) {
   return rows_ub <= (int64_t)64 * s.n_experts;
 }
@@ -627,6 +632,12 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
   if constexpr (ACT == kActGated) {
     if (small)
       return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, GATHER, ACT, OUT, WP>(
+          A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  } else if constexpr (ACT == kActSilu) {
+    // the up-projection's many feature tiles: 128 weight rows x 32 slots, so a block streams
+    // twice the weight rows per stage and the grid is half as many blocks
+    if (small)
+      return launch_grouped_gemm<128, 32, 0, 64, 3, 2, true, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   } else {
     if (small)
