@@ -20,7 +20,7 @@
 //   k_dispatch_tilesort each 256-key tile of a bucket is sorted in LDS (bitonic network);
 //   k_dispatch_rank    rank of a key = number of smaller keys of its bucket: its position in
 //                      its own sorted tile plus a binary search in every other tile of the
-//                      bucket; blocks take (tile, group of 16 other tiles) work items and add
+//                      bucket; blocks take (tile, group of 4 other tiles) work items and add
 //                      their partial counts with integer atomics (exact and order-free);
 //   k_dispatch_emit    slot_of / drop_mask / row_token from the ranks and the capacity.
 // Up to 1024 assignments a single workgroup does all of it instead (k_dispatch_small: one
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(
 namespace {
 
 constexpr int kTile = 256;        // keys per sorted tile (one per thread)
-constexpr int kTilesPerItem = 16;  // other tiles one rank work item searches
+constexpr int kTilesPerItem = 4;  // other tiles one rank work item searches
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
 
