@@ -65,6 +65,7 @@ SHAPES = [
     (1000, 136, 72, 8, 3, 1.0),
     (517, 256, 264, 5, 1, 8.0),
     (1500, 64, 520, 64, 6, 1.0),
+    (200, 64, 264, 8, 2, 4.0),  # decode-sized tiles, experts past 64 rows
 ]
 
 

@@ -250,6 +250,10 @@ SMALL = [
     (1000, 64, 520, 64, 6, 1.5, "bf16"),
     (300, 128, 256, 16, 4, 0.25, "bf16"),
     (517, 256, 264, 5, 1, 8.0, "bf16"),
+    # decode-sized batches (at most 64 E kept rows) with experts past 32 and 64 rows: the
+    # up-projection's 32-row token tiles come several to an expert
+    (60, 72, 136, 4, 2, 2.0, "bf16"),
+    (200, 64, 264, 8, 2, 4.0, "bf16"),
     (1, 4, 8, 4, 1, 1.25, "f32"),
     (7, 5, 9, 3, 2, 1.0, "f32"),
     (65, 12, 20, 8, 2, 0.75, "f32"),
