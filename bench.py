@@ -279,6 +279,8 @@ def main():
         bench_pool(args, wl, inp)
         return
     d = L.upload(inp, dev)
+    if args.weights == "packed" and inp["dtype"] != "bf16":
+        args.weights = "rowmajor"  # the packed layout is bf16 only
     if args.weights == "packed":  # a one-time preparation of the weights, outside the timing
         d = L.pack_weights(d)
     shape = L.shape_of(d, wl.top_k, cap)
