@@ -554,14 +554,14 @@ constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
 
 // compute units of the current device (cached per device)
 int compute_units() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[kMaxDevices];  // 0 until first asked (same value from any thread)
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cus[dev].load(std::memory_order_relaxed) == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
   return cus[dev];
 }
@@ -579,13 +579,10 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
   auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT, WP>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_allowed[kMaxDevices];
+  if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
+      err != hipSuccess)
+    return err;
   // upper bound on groups for the shorter tile height: token tiles <= rows_ub / TM + E
   constexpr int tm_min = TMB > 0 && TMB < TMA ? TMB : TMA;
   const int64_t mt_ub = (rows_ub + tm_min - 1) / tm_min + E;

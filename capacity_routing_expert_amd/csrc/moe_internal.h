@@ -4,9 +4,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 
 namespace moe {
+
+// ---------------------------------------------------------------- host helpers
+constexpr int kMaxDevices = 64;
+
+// Lets kernel `kern` take `bytes` of dynamic LDS on the current device, once per device:
+// `done` is the kernel's own per-device flag array (a function-local static, zero at start).
+// Concurrent first calls may both set the attribute, which is harmless.
+inline hipError_t allow_dynamic_lds(const void* kern, int bytes,
+                                    std::atomic<bool> (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && cached) done[dev].store(true, std::memory_order_release);
+  return err;
+}
 
 typedef uint16_t bf16_t;  // bf16 stored as its bit pattern
 

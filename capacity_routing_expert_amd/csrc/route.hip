@@ -251,13 +251,10 @@ hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const fl
   constexpr int PF = 1;
   const size_t lds = (size_t)8 * ((NW - 1) * R * EBG * 256 + (size_t)s.n_experts * TT);
   auto kern = k_route_mfma<TIn, R, EBG, NW, PF>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_max());
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_allowed[kMaxDevices];
+  if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)route_lds_max(), lds_allowed);
+      err != hipSuccess)
+    return err;
   const int64_t blocks = (s.T + TT - 1) / TT;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, x, w, b_router, s.T,
                      s.d_model, s.n_experts, s.top_k, ids, gates, logits);
