@@ -506,6 +506,234 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
 }
 
+// ---------------------------------------------------------------- down-projection, loader waves
+// The large-batch down-projection (GEMM 2: no activation) runs on 512-thread blocks of 256 x 192
+// tiles.  Waves 4-7 only issue the direct-to-LDS loads of the NS-deep ring of 32-K stages;
+// waves 0-3 only read LDS fragments and run the MFMAs (128 features x 96 slots each, fp32
+// accumulators in VGPRs, two waves per SIMD).  The load issue, which can stall a wave behind a
+// busy memory pipeline, then no longer holds up the matrix cores.  One barrier per stage: the
+// loader waves pass it once this wave's loads of stage kt+1 have landed, the MFMA waves once
+// they have read all of stage kt, and right after it the loaders refill the freed slot with
+// stage kt+NS.  The stage layout, swizzle, MFMA blocks and K order are those of gemm_tile, so
+// every output element sums the same products in the same order (bit-identical results).
+template <int TN, int TM, int NS, bool GATHER, int OUT, bool WP>
+__device__ __forceinline__ void gemm_tile_loaders(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
+    const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
+    int a_rows, int e, int row0, int rows, int n0) {
+  constexpr int BK = 32, WN = 2, WM = 2, kChunks = 4, kRowsPerLoad = 16;
+  constexpr int FN = TN / WN / 32, FM = TM / WM / 32;
+  constexpr int kLoaders = 4, kThreads = 512;
+  constexpr int kWLoads = TN / kRowsPerLoad / kLoaders;  // per loader wave and stage
+  constexpr int kXLoads = TM / kRowsPerLoad / kLoaders;
+  constexpr int kLoads = kWLoads + kXLoads;
+  constexpr int kStageBytes = (TN + TM) * BK * 2;
+  static_assert(TN % (kRowsPerLoad * kLoaders) == 0 && TM % (kRowsPerLoad * kLoaders) == 0 &&
+                    FN >= 1 && FM >= 1 && NS >= 2 && (NS - 1) * kLoads < 64,
+                "tile shape");
+  static_assert(BK % kPackK == 0, "a stage reads whole packed blocks");
+  auto swz = [](int r) { return (r >> 2) & 3; };
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  const int nk = (K + BK - 1) / BK;
+  const int wrows = min(TN, N - n0);
+  constexpr int kPitch = TN * 2 + 16;  // epilogue staging tile [TM][TN] bf16, padded rows
+  unsigned char* stile = reinterpret_cast<unsigned char*>(smem);
+  int32_t* srow = reinterpret_cast<int32_t*>(stile + TM * kPitch);
+
+  if (wave >= 4) {
+    // ---- loader waves: the load plan of gemm_tile, split over 4 waves instead of 4 MFMA waves
+    const int lw = wave - 4;
+    const int lrow = lane / kChunks, pch = lane % kChunks;
+    const int KBW = (K + kPackK - 1) / kPackK;
+    const i32x4_t wsrc =
+        WP ? make_srd(W + (int64_t)e * KBW * N * kPackK, (uint32_t)KBW * (uint32_t)N * (kPackK * 2u))
+           : make_srd(W + ((int64_t)e * N + n0) * K, (uint32_t)(wrows * K * 2));
+    uint32_t woff[kWLoads];
+#pragma unroll
+    for (int j = 0; j < kWLoads; ++j) {
+      const int row = (lw * kWLoads + j) * kRowsPerLoad + lrow;
+      const int c = pch ^ swz(row);
+      if (WP)
+        woff[j] = n0 + row < N && c * 8 < K
+                      ? (uint32_t)(((c * 8 / kPackK) * N + n0 + row) * kPackK + (c * 8) % kPackK) * 2u
+                      : kOutOfRange;
+      else
+        woff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
+    }
+    i32x4_t xsrc;
+    uint32_t xoff[kXLoads];
+    if (GATHER) {
+      xsrc = make_srd(A, (uint32_t)a_rows * (uint32_t)K * 2u);
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int row = (lw * kXLoads + j) * kRowsPerLoad + lrow;
+        const int c = pch ^ swz(row);
+        const int rt = row < rows ? row_token[row0 + row] : -1;  // -1: a zero row (padding)
+        xoff[j] = rt >= 0 && c * 8 < K ? (uint32_t)(rt * K + c * 8) * 2u : kOutOfRange;
+      }
+    } else {
+      xsrc = make_srd(A + (int64_t)row0 * K, (uint32_t)(rows * K * 2));
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int row = (lw * kXLoads + j) * kRowsPerLoad + lrow;
+        const int c = pch ^ swz(row);
+        xoff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
+      }
+    }
+    // stage S into slot S % NS; chunks at or past K (K tail, stages past the last) read as zeros
+    auto issue = [&](int S) {
+      const int k0 = S * BK;
+      const uint32_t kb = (uint32_t)k0 * 2u;
+      const uint32_t kw = WP ? (uint32_t)(k0 / kPackK) * (uint32_t)N * (kPackK * 2u) : kb;
+      const uint32_t sb = lds0 + (uint32_t)((S % NS) * kStageBytes);
+#pragma unroll
+      for (int j = 0; j < kWLoads; ++j) {
+        const int g = lw * kWLoads + j;
+        const int c = pch ^ swz(g * kRowsPerLoad + lrow);
+        lds_dma16(wsrc, sb + (uint32_t)(g * 1024),
+                  (k0 + c * 8 < K && woff[j] != kOutOfRange) ? woff[j] + kw : kOutOfRange);
+      }
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int g = lw * kXLoads + j;
+        const int c = pch ^ swz(g * kRowsPerLoad + lrow);
+        lds_dma16(xsrc, sb + (uint32_t)(TN * BK * 2 + g * 1024),
+                  (k0 + c * 8 < K && xoff[j] != kOutOfRange) ? xoff[j] + kb : kOutOfRange);
+      }
+    };
+    for (int s0 = 0; s0 < NS; ++s0) issue(s0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kLoads));
+    __syncthreads();  // stage 0 is in
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kLoads));  // this wave's stage kt+1
+      __syncthreads();  // stage kt+1 is in, stage kt is read
+      issue(kt + NS);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the zero-fill loads land before the LDS reuse
+    __syncthreads();                           // the ring is free for the staging tile
+    if (OUT != kOutSlots)
+      for (int r = threadIdx.x - 256; r < rows; r += 256) srow[r] = out_row[row0 + r];
+  } else {
+    // ---- MFMA waves
+    const int wn = wave % WN, wm = wave / WN;
+    const int r32 = lane & 31, half = lane >> 5;
+    float rsc[FM];  // row scales of this lane's slot columns, fetched ahead of the K loop
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      rsc[j] = 1.0f;
+      if (OUT == kOutPairsScaled) {
+        const int tl = wm * (TM / WM) + j * 32 + r32;
+        rsc[j] = tl < rows ? row_scale[out_row[row0 + tl]] : 0.0f;
+      }
+    }
+    bf16x8_t fa[2][FN], fb[2][FM];
+    f32x16_t acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // fragments of 16-K step kk of stage S into register set F
+    auto read = [&](int S, int kk, int F) {
+      const uint4* sb = smem + (S % NS) * (kStageBytes / 16);
+      const int ch = kk * 2 + half;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int row = wn * (TN / WN) + i * 32 + r32;
+        fa[F][i] = as_bf16x8(sb[row * kChunks + (ch ^ swz(row))]);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int row = wm * (TM / WM) + j * 32 + r32;
+        fb[F][j] = as_bf16x8(sb[TN * kChunks + row * kChunks + (ch ^ swz(row))]);
+      }
+    };
+    auto mfma = [&](int F) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
+    };
+    __syncthreads();  // stage 0 is in
+    read(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      read(kt, 1, 1);
+      mfma(0);
+      __syncthreads();  // stage kt+1 is in, stage kt is read
+      read(kt + 1, 0, 0);  // past the last stage this reads a slot nobody uses
+      mfma(1);
+    }
+    __syncthreads();  // the ring is free for the staging tile
+    // bias (+ row scale) + bf16 into the staging tile: lane (r32, half) holds, for block (i, j),
+    // features 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      uint2 bb[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = n0 + wn * (TN / WN) + i * 32 + 8 * g4 + 4 * half;
+        bb[g4] = bias && n < N ? *reinterpret_cast<const uint2*>(bias + (int64_t)e * N + n)
+                               : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        __builtin_amdgcn_sched_barrier(0);  // one block's 16 accumulators at a time
+        const int tl = wm * (TM / WM) + j * 32 + r32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int fl = wn * (TN / WN) + i * 32 + 8 * g4 + 4 * half;
+          float v[4];
+          v[0] = acc[i][j][4 * g4 + 0] + __uint_as_float(bb[g4].x << 16);
+          v[1] = acc[i][j][4 * g4 + 1] + __uint_as_float(bb[g4].x & 0xFFFF0000u);
+          v[2] = acc[i][j][4 * g4 + 2] + __uint_as_float(bb[g4].y << 16);
+          v[3] = acc[i][j][4 * g4 + 3] + __uint_as_float(bb[g4].y & 0xFFFF0000u);
+          if (OUT == kOutPairsScaled) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] *= rsc[j];
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(stile + tl * kPitch + fl * 2) = o;
+        }
+      }
+    }
+  }
+  __syncthreads();  // staging tile and output rows complete
+  // coalesced 16-byte stores of whole output rows by all 512 threads
+  constexpr int kChunksPerRow = TN / 8;
+  const int ncols = min(TN, N - n0);
+  for (int c = threadIdx.x; c < rows * kChunksPerRow; c += kThreads) {
+    const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
+    const int64_t orow = OUT != kOutSlots ? (int64_t)srow[row] : (int64_t)(row0 + row);
+    if (ch * 8 < ncols)
+      *reinterpret_cast<uint4*>(out + orow * N + n0 + ch * 8) =
+          *reinterpret_cast<const uint4*>(stile + row * kPitch + ch * 16);
+  }
+}
+
+template <int TN, int TM, int NS, bool GATHER, int OUT, bool WP>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm_loaders(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
+    const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, const int32_t* __restrict__ out_row,
+    const float* __restrict__ row_scale, int E, int N, int K, int a_rows) {
+  const int lane = threadIdx.x & 63;
+  const int NT = (N + TN - 1) / TN;
+  const TokenTiles<TM> tt(offsets, E, lane);
+  int mt, nt, e, row0, rows;
+  if (!tile_of_block(tt.MT, NT, mt, nt)) return;  // block-uniform
+  tt.locate(offsets, lane, mt, e, row0, rows);
+  gemm_tile_loaders<TN, TM, NS, GATHER, OUT, WP>(A, row_token, W, bias, out, out_row, row_scale,
+                                                 N, K, a_rows, e, row0, rows, nt * TN);
+}
+
 // ---------------------------------------------------------------- weight packing
 // [E, rows, cols] row-major -> [E, ceil(cols / 32), rows, 32], K columns past cols zero.  One
 // thread per 16-byte chunk of the packed array (cols is a multiple of 8 in bf16).
@@ -596,6 +824,33 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   return hipGetLastError();
 }
 
+template <int TN, int TM, int NS, bool GATHER, int OUT, bool WP>
+hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token,
+                                       const int32_t* offsets, const bf16_t* W, const bf16_t* bias,
+                                       bf16_t* out, int E, int N, int K, int a_rows,
+                                       int64_t rows_ub, hipStream_t st,
+                                       const int32_t* out_row = nullptr,
+                                       const float* row_scale = nullptr) {
+  if (rows_ub <= 0) return hipSuccess;
+  constexpr size_t ring = (size_t)NS * (TN + TM) * 32 * 2;
+  constexpr size_t tile = (size_t)TM * (TN * 2 + 16) + (OUT != kOutSlots ? (size_t)TM * 4 : 0);
+  constexpr size_t lds = ring > tile ? ring : tile;
+  static_assert(lds <= 160 * 1024, "LDS per compute unit");
+  auto kern = k_grouped_gemm_loaders<TN, TM, NS, GATHER, OUT, WP>;
+  static std::atomic<bool> lds_allowed[kMaxDevices];
+  if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
+      err != hipSuccess)
+    return err;
+  const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;  // token tiles <= rows_ub / TM + E
+  const int64_t nt = (N + TN - 1) / TN;
+  const int64_t nq = (nt + kGroupN - 1) / kGroupN;
+  const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
+  const int64_t grid = (ng_ub + 7) / 8 * 256;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, A, row_token, offsets, W,
+                     bias, out, out_row, row_scale, E, N, K, a_rows);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* row_token,
@@ -641,8 +896,12 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
       return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   }
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, GATHER, ACT, OUT, WP>(
-      A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  if constexpr (ACT == kActNone)  // the down-projection: loader waves, 256 x 192 tiles
+    return launch_grouped_gemm_loaders<256, 192, 4, GATHER, OUT, WP>(
+        A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  else
+    return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, GATHER, ACT, OUT, WP>(
+        A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
 }
 
 // the weight layout of the shape picks the kernel
