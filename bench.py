@@ -380,11 +380,11 @@ def main():
     expert_s = (stage_ms["expert_up"] + stage_ms["expert_down"]) / 1e3
     dom = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
-                  "expert_down": "k_grouped_gemm (GEMM 2: W2 + b2)"}[dom]
+                  "expert_down": "k_grouped_gemm_loaders (GEMM 2: W2 + b2)"}[dom]
     if dropless:
         dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1 in pair order: row p // top_k in, "
                                    "row p out)",
-                      "expert_down": "k_grouped_gemm (GEMM 2 in pair order: x topk_weights[p])"}[dom]
+                      "expert_down": "k_grouped_gemm_loaders (GEMM 2 in pair order: x topk_weights[p])"}[dom]
     gemm_flop = gemm1_flop if dom == "expert_up" else gemm2_flop
     achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
     # the committed counter summaries are of the compact layout's launches
