@@ -5,10 +5,10 @@ One step = one moe_layer_forward over a batch of synthetic input already residen
 router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), expert GEMM 2
 (+bias), combine.  Prints ONE JSON line:
   value          tokens/s of the whole layer (T / wall-clock time per step)
-  roofline       the dominant kernel (the larger expert GEMM) against the bf16 MFMA peak,
-                 from HIP events recorded on the launch stream around it in a second run of
-                 the same number of steps (events between stages add launch gaps, so the
-                 steps `value` is timed on carry none)
+  roofline       the dominant kernel (the larger expert GEMM) against the bf16 MFMA peak; its
+                 duration comes from HIP events that the GEMM kernel launches of the timed
+                 steps record themselves (moe_set_gemm_timing, hipExtLaunchKernel), so the
+                 steps `value` is timed on carry no extra marker between launches
   cpu_baseline   the CPU oracle timed on this host on the same workload (a baseline only)
 Workload: the mid-size layer (T 4096, d_model 2048, d_ff 8192, 8 experts, top-2, capacity
 factor 1.25) unless --config names another.  --layout dropless times the dropless pair-order
@@ -20,6 +20,7 @@ is the consolidated run's tokens/s.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -153,22 +154,19 @@ def bench_pool(args, wl, inp):
     for cons in (False, True):
         for _ in range(args.warmup):
             run(cons)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            run(cons)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / args.steps
         evsets = []
         for _ in range(args.steps):
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             for ev in evs:
-                ev.record(stream)
+                ev.record(stream)  # creates the underlying hipEvent_t
             evsets.append(evs)
+        # timed region: the stage events are recorded by the timed steps themselves
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for evs in evsets:
             run(cons, evs)
         torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
         st = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evsets]))
               for j, name in enumerate(["route", "schedule", "batches", "scatter"])}
         active = [int(v) for v in bexp.cpu().numpy()]
@@ -205,7 +203,8 @@ def bench_pool(args, wl, inp):
         "consolidated": c,
         "original": o,
         "speedup_vs_original": c["tokens_per_s"] / o["tokens_per_s"],
-        "stage_timing": "HIP events: route, schedule + regroup, batch loop, scatter back",
+        "stage_timing": "HIP events recorded by the timed steps themselves: route, schedule + "
+                        "regroup, batch loop, scatter back",
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -339,29 +338,51 @@ def main():
                                          d["b1"], d["w2"], d["b2"], out, events,
                                          expert_counts=counts, ws=ws)
 
-    def new_events():
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    def new_events(n=6):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for ev in evs:
             ev.record(stream)  # creates the underlying hipEvent_t
         return evs
 
     log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup - 1, 0)):
         step()
+    # the last warm-up step times both expert GEMMs' kernels, to find the dominant one
+    probe = new_events(4)
     torch.cuda.synchronize()
+    B.moe_set_gemm_timing(probe)
+    step()
+    torch.cuda.synchronize()
+    dom = ("expert_up" if probe[0].elapsed_time(probe[1]) >= probe[2].elapsed_time(probe[3])
+           else "expert_down")
 
-    # timed region: K plain layer calls (no events between the stages), bracketed by a sync
+    # timed region: K plain layer calls bracketed by a sync.  Each is armed with
+    # moe_set_gemm_timing, so the dominant expert GEMM's kernel launch records its own start
+    # and end in HIP events on the launch stream (hipExtLaunchKernel); the roofline's kernel
+    # time comes from these very steps.
+    gemm_evsets = [new_events(2) for _ in range(args.steps)]
+
+    def arm_handles(evs):
+        h = [ctypes.c_void_p(ev.cuda_event) for ev in evs]
+        n = [ctypes.c_void_p(None)] * 2
+        return (ctypes.c_void_p * 4)(*(h + n if dom == "expert_up" else n + h))
+
+    arms = [arm_handles(evs) for evs in gemm_evsets]  # built ahead: the loop only passes them
+    set_timing = B.lib().moe_set_gemm_timing
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if set_timing(arms[i]) != 0:
+            raise RuntimeError(B.last_error())
         step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gemm_evsets]))
 
-    # stage breakdown: the same number of steps again, with HIP events recorded on the launch
-    # stream at the stage boundaries (each event adds a short gap before the next launch, so
-    # these steps are not the ones `value` is taken from)
+    # stage breakdown (route, dispatch, combine): the same number of steps again, with HIP
+    # events recorded between the stages (each such event adds a short launch gap, which is why
+    # these are not the timed steps)
     evsets = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -378,7 +399,6 @@ def main():
     gemm2_flop = 2.0 * n_kept * dm * ff
     gemm1_flop = 2.0 * gemm2_flop if gated else gemm2_flop
     expert_s = (stage_ms["expert_up"] + stage_ms["expert_down"]) / 1e3
-    dom = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
     dom_kernel = {"expert_up": "k_grouped_gemm (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm_loaders (GEMM 2: W2 + b2)"}[dom]
     if dropless:
@@ -386,7 +406,31 @@ def main():
                                    "row p out)",
                       "expert_down": "k_grouped_gemm_loaders (GEMM 2 in pair order: x topk_weights[p])"}[dom]
     gemm_flop = gemm1_flop if dom == "expert_up" else gemm2_flop
-    achieved = gemm_flop / (stage_ms[dom] / 1e3) / 1e12
+    achieved = gemm_flop / (dom_ms / 1e3) / 1e12  # the timed steps' kernel time
+    roof = {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "units_per_launch": f"{n_kept} kept rows x 2*{dm}*{ff}"
+                                f"{'*2' if gated and dom == 'expert_up' else ''} FLOP"}
+    # decode-sized batches (the library's small-tile rule: at most 64 rows per expert on
+    # average) stream the active experts' weights: the GEMM is bound by HBM
+    rows_ub = (wl.n_experts * cap if padded else wl.T * wl.top_k if dropless
+               else min(wl.T * wl.top_k, wl.n_experts * cap))
+    if rows_ub <= 64 * wl.n_experts:
+        esz = inp["x"].itemsize
+        active = int(np.count_nonzero(c if dropless else np.minimum(c, cap)))
+        rows = n_kept if not padded else wl.n_experts * cap
+        if dom == "expert_up":  # W1 (W13) + b1 of each active expert, x rows in, H rows out
+            w = ((2 if gated else 1) * ff * dm + (0 if gated else ff)) * esz
+            act = rows * (dm + ff) * esz
+        else:  # W2 + b2, H rows in, Y rows out
+            w = (dm * ff + (0 if gated else dm)) * esz
+            act = rows * (ff + dm) * esz
+        gbs = (active * w + act) / (dom_ms / 1e3) / 1e9
+        roof = {"kernel": dom_kernel + ", decode-sized tiles", "bound": "hbm", "achieved": gbs,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "units_per_launch": f"{active} active experts x {w} B of weights + {act} B of "
+                                    f"activations ({rows} rows)",
+                "tflops": achieved}
     # the committed counter summaries are of the compact layout's launches
     traffic = None if padded or dropless else traffic_from_profiles(
         "gemm1" if dom == "expert_up" else "gemm2", args.config)
@@ -423,14 +467,16 @@ def main():
         "expert_gemm_tflops": (gemm1_flop + gemm2_flop) / expert_s / 1e12,
         "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
                                          / PEAK_BF16_TFLOPS,
-        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic,
-                     "units_per_launch": f"{n_kept} kept rows x 2*{dm}*{ff}"
-                                         f"{'*2' if gated and dom == 'expert_up' else ''} FLOP"},
+        "roofline": dict(roof, traffic=traffic),
+        "dominant_kernel_ms": dom_ms,
+        "dominant_kernel_timing": "start and end of the dominant GEMM's kernel, recorded by its "
+                                  "launch in each timed step (moe_set_gemm_timing, "
+                                  "hipExtLaunchKernel), averaged over the K steps; the roofline "
+                                  "uses it, expert_gemm_* use the stage times below",
         "stages_ms": stage_ms,
         "stage_timing": "HIP events at the stage boundaries over a second run of the same number "
-                        "of steps, right after the timed region",
+                        "of steps right after the timed region (events between launches add "
+                        "short gaps, so these steps are not the timed ones)",
         "event_step_ms": step_ms,
         "route_GBps": route_bytes / (stage_ms["route"] / 1e3) / 1e9,
         "combine_GBps": combine_bytes / (stage_ms["combine"] / 1e3) / 1e9,

@@ -30,7 +30,7 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_stat
            "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
            "moe_layer_forward_dropless_gated", "moe_workspace_bytes_batches",
            "moe_schedule_batches", "moe_layer_forward_batches", "moe_packed_weights_bytes",
-           "moe_pack_weights")
+           "moe_pack_weights", "moe_set_gemm_timing")
 
 
 class MoeShape(ctypes.Structure):
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         # shape, n_batches, consolidate, x, w_router, b_router, w1, b1, w2, b2, out, ids, gates,
         # order, batch_experts, ws, ws_bytes, stream, events
         L.moe_layer_forward_batches.argtypes = [SP, I32, I32] + [P] * 13 + [SZ, P, P]
+        L.moe_set_gemm_timing.argtypes = [P]
+        L.moe_set_gemm_timing.restype = I32
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                      "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_padded",
                      "moe_layer_forward_gated", "moe_dispatch_pairs", "moe_expert_ffn_pairs",
@@ -250,6 +252,20 @@ def moe_layer_forward_profiled(shape, x, w_router, b_router, w1, b1, w2, b2, out
                          slot_of, drop_mask, expert_counts, ws)
     _check(lib().moe_layer_forward_profiled(*args, _stream(stream), handles),
            "moe_layer_forward_profiled")
+
+
+def moe_set_gemm_timing(events):
+    """Arms kernel timing of the two expert GEMMs for the next layer or expert-FFN call on this
+    thread: `events` are 4 torch.cuda.Event(enable_timing=True) objects (or None in place of
+    one GEMM's pair), already recorded once (so the underlying hipEvent_t exists), receiving
+    the up-projection's start and end and the down-projection's start and end; None
+    disarms."""
+    if events is None:
+        _check(lib().moe_set_gemm_timing(None), "moe_set_gemm_timing")
+        return
+    handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event if ev is not None else None)
+                                      for ev in events])
+    _check(lib().moe_set_gemm_timing(handles), "moe_set_gemm_timing")
 
 
 def moe_layer_forward_padded(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,

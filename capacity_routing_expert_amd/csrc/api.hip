@@ -29,6 +29,49 @@ moe_status device_error(hipError_t err, const char* where) {
   return fail(MOE_ERR_DEVICE, "%s: %s", where, hipGetErrorString(err));
 }
 
+// Expert-GEMM kernel timing armed by moe_set_gemm_timing for the next layer or expert-FFN call
+// on this thread: up-projection start / stop, down-projection start / stop.
+thread_local hipEvent_t g_timing[4] = {nullptr, nullptr, nullptr, nullptr};
+
+// The armed timing events, disarming them; false if none are armed.  A pair (start, stop) of
+// a GEMM that is not timed is NULL.
+bool take_timing(hipEvent_t (&ev)[4]) {
+  if (!g_timing[0] && !g_timing[2]) return false;
+  for (int i = 0; i < 4; ++i) {
+    ev[i] = g_timing[i];
+    g_timing[i] = nullptr;
+  }
+  return true;
+}
+
+// The events of one GEMM (pair 0: up-projection, 1: down-projection), or NULL if not timed.
+const hipEvent_t* timing_pair(bool timed, const hipEvent_t (&ev)[4], int pair) {
+  return timed && ev[2 * pair] ? ev + 2 * pair : nullptr;
+}
+
+// Records the non-NULL timing events among ev[0 .. n-1] where the stream stands (a GEMM that
+// launches nothing).
+moe_status record_now(const hipEvent_t* ev, int n, hipStream_t st) {
+  for (int i = 0; i < n; ++i)
+    if (ev[i])
+      if (hipError_t err = hipEventRecord(ev[i], st); err != hipSuccess)
+        return device_error(err, "hipEventRecord");
+  return MOE_OK;
+}
+
+// One expert GEMM launch, with its kernel start and stop recorded in ev[0], ev[1] when `ev` is
+// given (the events ride on the launch itself); a launch that turns out empty records them
+// back to back.
+template <typename F>
+moe_status run_gemm_stage(const hipEvent_t* ev, hipStream_t st, const char* what, F launch) {
+  if (ev) arm_gemm_events(ev[0], ev[1]);
+  const hipError_t err = launch();
+  hipEvent_t a, b;
+  const bool unused = ev && take_gemm_events(&a, &b);  // not taken: nothing was launched
+  if (err != hipSuccess) return device_error(err, what);
+  return unused ? record_now(ev, 2, st) : MOE_OK;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -197,6 +240,8 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
                          int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts, void* ws,
                          size_t ws_bytes, hipStream_t st, moe_event_t const* events,
                          bool padded = false, void* y_rows = nullptr, bool gated = false) {
+  hipEvent_t tev[4];
+  const bool timed = take_timing(tev);  // consumed by this call even if it fails
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   auto rec = [&](int i) -> moe_status {
@@ -206,7 +251,7 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   };
   if (s.T == 0) {  // empty batch: nothing to check or enqueue
     for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
-    return MOE_OK;
+    return timed ? record_now(tev, 4, st) : MOE_OK;
   }
   if (gated) {
     if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the gated expert is bf16 only");
@@ -246,15 +291,17 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
     rows = (int64_t)s.n_experts * s.capacity;
   }
   MOE_TRY(rec(2));
-  hipError_t err = gated ? launch_ffn_up_gated(s, x, row_token, offsets, w1, h, rows, st)
-                         : launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
-  if (err != hipSuccess) return device_error(err, "expert up-projection");
+  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
+    return gated ? launch_ffn_up_gated(s, x, row_token, offsets, w1, h, rows, st)
+                 : launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
+  }));
   MOE_TRY(rec(3));
-  err = gated ? launch_ffn_down_nobias(s, h, offsets, w2, y, rows, st)
-              : launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
-  if (err != hipSuccess) return device_error(err, "expert down-projection");
+  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
+    return gated ? launch_ffn_down_nobias(s, h, offsets, w2, y, rows, st)
+                 : launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
+  }));
   MOE_TRY(rec(4));
-  err = launch_combine(s, x, gates, slots, y, out, st);
+  hipError_t err = launch_combine(s, x, gates, slots, y, out, st);
   if (err != hipSuccess) return device_error(err, "combine");
   MOE_TRY(rec(5));
   return MOE_OK;
@@ -275,16 +322,21 @@ moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pa
                      const int32_t* row_token, const int32_t* offsets, const void* w1,
                      const void* b1, const void* w2, const void* b2, const float* weights,
                      bool gated, void* h, void* pair_rows, hipStream_t st,
-                     moe_event_t const* events) {
+                     moe_event_t const* events, const hipEvent_t* tev) {
   const int64_t rows = s.T * (int64_t)s.top_k;
-  hipError_t err = launch_ffn_up_pairs(s, x, row_token, sorted_pairs, offsets, w1,
-                                       gated ? nullptr : b1, h, rows, gated, st);
-  if (err != hipSuccess) return device_error(err, "expert up-projection (pair order)");
+  MOE_TRY(run_gemm_stage(tev && tev[0] ? tev : nullptr, st,
+                         "expert up-projection (pair order)", [&] {
+    return launch_ffn_up_pairs(s, x, row_token, sorted_pairs, offsets, w1, gated ? nullptr : b1,
+                               h, rows, gated, st);
+  }));
+  hipError_t err;
   if (events && (err = hipEventRecord((hipEvent_t)events[3], st)) != hipSuccess)
     return device_error(err, "hipEventRecord");
-  err = launch_ffn_down_pairs(s, h, sorted_pairs, offsets, w2, gated ? nullptr : b2, weights,
-                              pair_rows, rows, st);
-  if (err != hipSuccess) return device_error(err, "expert down-projection (pair order)");
+  MOE_TRY(run_gemm_stage(tev && tev[2] ? tev + 2 : nullptr, st,
+                         "expert down-projection (pair order)", [&] {
+    return launch_ffn_down_pairs(s, h, sorted_pairs, offsets, w2, gated ? nullptr : b2, weights,
+                                 pair_rows, rows, st);
+  }));
   return MOE_OK;
 }
 
@@ -294,6 +346,8 @@ moe_status layer_forward_dropless(const moe_shape* shape, const void* x, const v
                                   int32_t* topk_ids, float* topk_gates, int32_t* expert_counts,
                                   void* pair_rows, void* ws, size_t ws_bytes, hipStream_t st,
                                   moe_event_t const* events) {
+  hipEvent_t tev[4];
+  const bool timed = take_timing(tev);  // consumed by this call even if it fails
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   if (events)
@@ -306,7 +360,7 @@ moe_status layer_forward_dropless(const moe_shape* shape, const void* x, const v
   };
   if (s.T == 0) {  // empty batch: nothing to check or enqueue
     for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
-    return MOE_OK;
+    return timed ? record_now(tev, 4, st) : MOE_OK;
   }
   MOE_TRY(check_dropless(s, gated));
   MOE_TRY(check_data_ptr(s, x, "x"));
@@ -342,7 +396,7 @@ moe_status layer_forward_dropless(const moe_shape* shape, const void* x, const v
   if (err != hipSuccess) return device_error(err, "pair dispatch");
   MOE_TRY(rec(2));
   MOE_TRY(ffn_pairs(s, x, pairs, row_token, offsets, w1, b1, w2, b2, gates, gated,
-                    at<void>(ws, L.h), y, st, events));
+                    at<void>(ws, L.h), y, st, events, timed ? tev : nullptr));  // pairs may be NULL
   MOE_TRY(rec(4));
   err = launch_moe_sum(s, x, ids, y, out, st);
   if (err != hipSuccess) return device_error(err, "moe_sum");
@@ -631,9 +685,12 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
                           const int32_t* expert_offsets, const void* w1, const void* b1,
                           const void* w2, const void* b2, void* y_rows, void* ws,
                           size_t ws_bytes, moe_stream_t stream) {
+  hipEvent_t tev[4];
+  const bool timed = take_timing(tev);  // consumed by this call even if it fails
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
-  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  hipStream_t st = (hipStream_t)stream;
+  if (s.T == 0) return timed ? record_now(tev, 4, st) : MOE_OK;  // empty batch
   MOE_TRY(check_data_ptr(s, x, "x"));
   if (max_rows(s) > 0) {
     MOE_TRY(check_ptr(row_token, 4, "row_token"));
@@ -645,14 +702,15 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   MOE_TRY(check_data_ptr(s, w2, "w2"));
   MOE_TRY(check_data_ptr(s, b2, "b2"));
   MOE_TRY(check_ws(s, ws, ws_bytes));
-  if (max_rows(s) == 0) return MOE_OK;
+  if (max_rows(s) == 0) return timed ? record_now(tev, 4, st) : MOE_OK;
   const Workspace L = layout(s);
-  hipStream_t st = (hipStream_t)stream;
   void* h = at<void>(ws, L.h);
-  hipError_t err = launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, max_rows(s), st);
-  if (err != hipSuccess) return device_error(err, "expert up-projection");
-  err = launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, max_rows(s), st);
-  if (err != hipSuccess) return device_error(err, "expert down-projection");
+  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
+    return launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, max_rows(s), st);
+  }));
+  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
+    return launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, max_rows(s), st);
+  }));
   return MOE_OK;
 }
 
@@ -681,6 +739,21 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
                        slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
                        nullptr);
+}
+
+moe_status moe_set_gemm_timing(const moe_event_t* events) {
+  if (!events) {
+    for (int i = 0; i < 4; ++i) g_timing[i] = nullptr;
+    return MOE_OK;
+  }
+  for (int p = 0; p < 2; ++p)
+    if (!events[2 * p] != !events[2 * p + 1])
+      return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] and events[%d]: both or neither NULL",
+                  2 * p, 2 * p + 1);
+  if (!events[0] && !events[2])
+    return fail(MOE_ERR_INVALID_ARGUMENT, "events: no GEMM to time (all four NULL)");
+  for (int i = 0; i < 4; ++i) g_timing[i] = (hipEvent_t)events[i];
+  return MOE_OK;
 }
 
 moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
@@ -753,9 +826,11 @@ moe_status moe_expert_ffn_pairs(const moe_shape* shape, const void* x,
                                 const void* w2, const void* b2, const float* topk_weights,
                                 int32_t gated, void* pair_rows, void* ws, size_t ws_bytes,
                                 moe_stream_t stream) {
+  hipEvent_t tev[4];
+  const bool timed = take_timing(tev);  // consumed by this call even if it fails
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
-  if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
+  if (s.T == 0) return timed ? record_now(tev, 4, (hipStream_t)stream) : MOE_OK;
   MOE_TRY(check_dropless(s, gated != 0));
   MOE_TRY(check_data_ptr(s, x, "x"));
   MOE_TRY(check_ptr(sorted_pairs, 4, "sorted_pairs"));
@@ -772,7 +847,8 @@ moe_status moe_expert_ffn_pairs(const moe_shape* shape, const void* x,
   MOE_TRY(check_ws(s, ws, ws_bytes, kLayoutDropless));
   const Workspace L = layout(s, kLayoutDropless);
   return ffn_pairs(s, x, sorted_pairs, row_token, expert_offsets, w1, b1, w2, b2, topk_weights,
-                   gated != 0, at<void>(ws, L.h), pair_rows, (hipStream_t)stream, nullptr);
+                   gated != 0, at<void>(ws, L.h), pair_rows, (hipStream_t)stream, nullptr,
+                   timed ? tev : nullptr);
 }
 
 moe_status moe_sum(const moe_shape* shape, const void* x, const int32_t* topk_ids,

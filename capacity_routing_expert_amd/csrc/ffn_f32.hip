@@ -4,6 +4,8 @@
 // down-projection with bias.  A plain one-thread-per-output kernel pair with fp32
 // accumulation in column order; it serves small fp32 layers such as the worked example,
 // where the work is a few hundred FLOPs and latency is all that matters.
+#include <hip/hip_ext.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -65,9 +67,16 @@ hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* r
                              int64_t rows, hipStream_t st) {
   const int64_t n = rows * s.d_ff;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_ffn_up_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float*)x, row_token, offsets, s.n_experts, (const float*)w1,
-                     (const float*)b1, (float*)h, s.d_model, s.d_ff, rows);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipEvent_t t0, t1;
+  if (take_gemm_events(&t0, &t1))
+    hipExtLaunchKernelGGL(k_ffn_up_f32, grid, dim3(256), 0, st, t0, t1, 0, (const float*)x,
+                          row_token, offsets, s.n_experts, (const float*)w1, (const float*)b1,
+                          (float*)h, s.d_model, s.d_ff, rows);
+  else
+    hipLaunchKernelGGL(k_ffn_up_f32, grid, dim3(256), 0, st, (const float*)x, row_token, offsets,
+                       s.n_experts, (const float*)w1, (const float*)b1, (float*)h, s.d_model,
+                       s.d_ff, rows);
   return hipGetLastError();
 }
 
@@ -76,9 +85,16 @@ hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t*
                                hipStream_t st) {
   const int64_t n = rows * s.d_model;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_ffn_down_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float*)h, offsets, s.n_experts, (const float*)w2, (const float*)b2,
-                     (float*)y, s.d_model, s.d_ff, rows);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipEvent_t t0, t1;
+  if (take_gemm_events(&t0, &t1))
+    hipExtLaunchKernelGGL(k_ffn_down_f32, grid, dim3(256), 0, st, t0, t1, 0, (const float*)h,
+                          offsets, s.n_experts, (const float*)w2, (const float*)b2, (float*)y,
+                          s.d_model, s.d_ff, rows);
+  else
+    hipLaunchKernelGGL(k_ffn_down_f32, grid, dim3(256), 0, st, (const float*)h, offsets,
+                       s.n_experts, (const float*)w2, (const float*)b2, (float*)y, s.d_model,
+                       s.d_ff, rows);
   return hipGetLastError();
 }
 

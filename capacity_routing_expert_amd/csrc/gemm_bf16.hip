@@ -41,6 +41,8 @@
 // tiles, so the 32 blocks sharing an L2 share both operands' streams.  Each block finds the
 // expert of its token tile from expert_offsets with a wave prefix scan and exits if its tile
 // does not exist.
+#include <hip/hip_ext.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -772,6 +774,23 @@ hipError_t launch_pack_weights(const void* w, void* wp, int64_t E, int rows, int
 }
 
 namespace {
+thread_local hipEvent_t g_gemm_start = nullptr, g_gemm_stop = nullptr;
+}  // namespace
+
+void arm_gemm_events(hipEvent_t start, hipEvent_t stop) {
+  g_gemm_start = start;
+  g_gemm_stop = stop;
+}
+
+bool take_gemm_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_gemm_start && !g_gemm_stop) return false;
+  *start = g_gemm_start;
+  *stop = g_gemm_stop;
+  g_gemm_start = g_gemm_stop = nullptr;
+  return true;
+}
+
+namespace {
 
 constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
   const size_t ring = (size_t)NS * (TN + TM) * BK * 2;      // stage ring
@@ -819,8 +838,14 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   const int64_t nq = (nt + kGroupN - 1) / kGroupN;
   const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
   const int64_t grid = (ng_ub + 7) / 8 * 256;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, A, row_token, offsets, W,
-                     bias, out, out_row, row_scale, E, N, K, a_rows, compute_units() * MINB);
+  hipEvent_t t0, t1;
+  if (take_gemm_events(&t0, &t1))
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, t0, t1, 0, A,
+                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows,
+                          compute_units() * MINB);
+  else
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, A, row_token, offsets, W,
+                       bias, out, out_row, row_scale, E, N, K, a_rows, compute_units() * MINB);
   return hipGetLastError();
 }
 
@@ -846,8 +871,13 @@ hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token
   const int64_t nq = (nt + kGroupN - 1) / kGroupN;
   const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
   const int64_t grid = (ng_ub + 7) / 8 * 256;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, A, row_token, offsets, W,
-                     bias, out, out_row, row_scale, E, N, K, a_rows);
+  hipEvent_t t0, t1;
+  if (take_gemm_events(&t0, &t1))
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, t0, t1, 0, A,
+                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows);
+  else
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, A, row_token, offsets, W,
+                       bias, out, out_row, row_scale, E, N, K, a_rows);
   return hipGetLastError();
 }
 

@@ -111,6 +111,12 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
                            int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st);
 
+// Kernel timing for the expert GEMMs: arm_gemm_events(start, stop) makes the next expert-GEMM
+// launch on this thread record its own start and stop in the two events (hipExtLaunchKernel,
+// no marker between launches); take_gemm_events hands them to that launch and disarms.
+void arm_gemm_events(hipEvent_t start, hipEvent_t stop);
+bool take_gemm_events(hipEvent_t* start, hipEvent_t* stop);
+
 // rows_ub: an upper bound on the slot rows of the layout (max_rows(s) compact, E * capacity
 // padded); row_token entries < 0 are zero rows
 hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_token,

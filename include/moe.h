@@ -191,6 +191,21 @@ moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
                                       int32_t* expert_counts, void* ws, size_t ws_bytes,
                                       moe_stream_t stream, moe_event_t const* events);
 
+/* Kernel timing of the two expert GEMMs (the layer's expert-FFN stage, Worked Example: the
+ * expert computations whose slowest expert sets the wall-clock time), with nothing inserted
+ * between launches.  Arms the NEXT call on this thread of moe_layer_forward (or its _profiled,
+ * _padded or _gated form), moe_layer_forward_dropless(_gated), moe_expert_ffn or
+ * moe_expert_ffn_pairs:
+ *   events[0], [1]  start and end of the up-projection's kernel
+ *   events[2], [3]  start and end of the down-projection's kernel
+ * recorded by the kernel launches themselves (hipExtLaunchKernel).  The events are the
+ * caller's (hipEventCreate, timing enabled); a pair may be NULL (both handles) to time one GEMM
+ * only, which halves the markers the timing puts on the stream.  A GEMM that launches nothing
+ * (T = 0, no kept rows) gets its two events recorded back to back on the stream.  That next
+ * call consumes the arm even if it fails; other calls leave it armed.  events == NULL
+ * disarms.  Errors: MOE_ERR_INVALID_ARGUMENT for a half-NULL pair or four NULL handles. */
+moe_status moe_set_gemm_timing(const moe_event_t* events);
+
 /* ---- Padded fixed-buffer layout.  "Some Tokens Do Not Get In", "Why there is a buffer": each
  * expert gets a buffer of `capacity` slots whether it fills it or not, and the empty slots are
  * computed anyway.  Same layer and same result as moe_layer_forward; only the layout of the

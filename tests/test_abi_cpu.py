@@ -107,3 +107,18 @@ def test_weight_layout_checks_on_the_host(lib):
     bf = B.make_shape(8, 8, 8, 2, 1, 0, B.MOE_BF16)
     assert lib.moe_pack_weights(ctypes.byref(bf), ctypes.c_void_p(16), 8, 12, ctypes.c_void_p(4096),
                                 None) == 2
+
+
+def test_gemm_timing_arm_checks_on_the_host(lib):
+    """moe_set_gemm_timing only stores the handles: a half-NULL pair or four NULLs are refused,
+    one GEMM's pair may be NULL, NULL disarms (no GPU call is made, so stand-in handles are
+    enough here)."""
+    half = (ctypes.c_void_p * 4)(1, 2, 0, 4)
+    assert lib.moe_set_gemm_timing(half) == 1
+    assert "events[2] and events[3]" in B.last_error()
+    none = (ctypes.c_void_p * 4)(0, 0, 0, 0)
+    assert lib.moe_set_gemm_timing(none) == 1
+    assert lib.moe_set_gemm_timing(None) == 0
+    for ok in ((1, 2, 3, 4), (1, 2, 0, 0), (0, 0, 3, 4)):
+        assert lib.moe_set_gemm_timing((ctypes.c_void_p * 4)(*ok)) == 0
+    assert lib.moe_set_gemm_timing(None) == 0  # disarmed before any layer call
