@@ -429,7 +429,11 @@ def main():
             w = (dm * ff + (0 if gated else dm)) * esz
             act = rows * (ff + dm) * esz
         gbs = (active * w + act) / (dom_ms / 1e3) / 1e9
-        roof = {"kernel": dom_kernel + ", decode-sized tiles", "bound": "hbm", "achieved": gbs,
+        small_kernel = ("k_grouped_gemm, decode-sized tiles ("
+                        + ("GEMM 1: 128 x 32 tiles" if dom == "expert_up" and not gated else
+                           "GEMM 1: 128 x 64 gate/up tiles" if dom == "expert_up" else
+                           "GEMM 2: 64 x 64 tiles") + ")")
+        roof = {"kernel": small_kernel, "bound": "hbm", "achieved": gbs,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                 "units_per_launch": f"{active} active experts x {w} B of weights + {act} B of "
                                     f"activations ({rows} rows)",
