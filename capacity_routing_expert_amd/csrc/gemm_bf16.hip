@@ -13,8 +13,10 @@
 // v_mfma_f32_32x32x16_bf16 wants: each lane feeds 8 consecutive K values of one row.
 //
 // Block tile: TN output features x TM slots, 4 waves of (TN/2) x (TM/2) (or of (TN/4) x 32 for
-// 32-slot tiles), each made of 32x32 MFMA blocks with fp32 accumulators in AGPRs.  The weights are the MFMA "A" operand, the
-// token rows the "B" operand.
+// 32-slot tiles), each made of 32x32 MFMA blocks with fp32 accumulators in AGPRs.  The weights
+// are the MFMA "A" operand, the token rows the "B" operand.  A second kernel (loader waves,
+// below) runs the same stages with separate waves for the loads and for the MFMAs; it takes
+// the large-batch down-projection and, with many experts, the up-projection.
 //
 // K pipeline: stages of BK = 32 K (64-byte rows) in a ring of NS = 4 stage buffers in LDS
 // (32 KiB each for 256 x 256), filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ...
@@ -34,6 +36,9 @@
 //
 // Epilogue: bias + activation + bf16 rounding per 16-accumulator group into an LDS tile, then
 // coalesced 16-byte stores of whole output rows.
+//
+// Timing: a launch can record its own kernel start and end in two events handed over with
+// arm_gemm_events (hipExtLaunchKernel), so nothing is queued between launches to time them.
 //
 // Scheduling: the grid is an upper bound (the number of kept rows is only known on the
 // device).  Workgroups are dealt round-robin over the 8 XCDs, so block b runs on XCD b % 8;
@@ -509,9 +514,10 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
 }
 
-// ---------------------------------------------------------------- down-projection, loader waves
-// The large-batch down-projection (GEMM 2: no activation) runs on 512-thread blocks of 256 x 192
-// tiles.  Waves 4-7 only issue the direct-to-LDS loads of the NS-deep ring of 32-K stages;
+// ---------------------------------------------------------------- loader waves
+// The large-batch down-projection (GEMM 2: no activation), and the up-projection (SiLU) of
+// layers with many experts, run on 512-thread blocks of 256 x 192 tiles.  Waves 4-7 only issue
+// the direct-to-LDS loads of the NS-deep ring of 32-K stages;
 // waves 0-3 only read LDS fragments and run the MFMAs (128 features x 96 slots each, fp32
 // accumulators in VGPRs, two waves per SIMD).  The load issue, which can stall a wave behind a
 // busy memory pipeline, then no longer holds up the matrix cores.  One barrier per stage: the
