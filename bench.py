@@ -43,21 +43,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_digest(path: str) -> str:
+    """SHA-256 of a source file with its comments and blank space removed, so that a counter
+    summary stays tied to the code and survives comment-only edits."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(re.sub(r"\s+", " ", text).strip().encode()).hexdigest()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "capacity_routing_expert_amd", "csrc", "gemm_bf16.hip")
+
+
 def traffic_from_profiles(kernel_tag: str, config_key: str):
     """HBM bytes per launch of the dominant kernel from a committed counter summary, scaled by
-    the copy-kernel calibration, or None if no summary matches the current kernel source."""
+    the copy-kernel calibration, or None if no summary matches the current kernel code."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{config_key}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = {k: re.search(rf"^{k}\s*=\s*(\S+)", text, re.M) for k in
-         ("source_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch", "fetch_scale",
+         ("code_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch", "fetch_scale",
           "write_scale")}
     if not all(m.values()):
         return None
-    src = open(os.path.join(ROOT, "capacity_routing_expert_amd", "csrc", "gemm_bf16.hip"), "rb").read()
-    if hashlib.sha256(src).hexdigest() != m["source_sha256"].group(1):
-        return None  # the kernel changed since the counters were taken
+    if code_digest(GEMM_SOURCE) != m["code_sha256"].group(1):
+        return None  # the kernel code changed since the counters were taken
     kib = (float(m["fetch_kib_per_dispatch"].group(1)) * float(m["fetch_scale"].group(1)) +
            float(m["write_kib_per_dispatch"].group(1)) * float(m["write_scale"].group(1)))
     return kib * 1024.0
