@@ -14,9 +14,11 @@
 //
 // Block tile: TN output features x TM slots, 4 waves of (TN/2) x (TM/2) (or of (TN/4) x 32 for
 // 32-slot tiles), each made of 32x32 MFMA blocks with fp32 accumulators in AGPRs.  The weights
-// are the MFMA "A" operand, the token rows the "B" operand.  A second kernel (loader waves,
-// below) runs the same stages with separate waves for the loads and for the MFMAs; it takes
-// the large-batch down-projection and, with many experts, the up-projection.
+// are the MFMA "A" operand, the token rows the "B" operand.  The large-batch up-projection runs
+// 8 waves (2 x 4 of 128 x 64, two per SIMD) on its 256 x 256 tiles, so that one wave's MFMAs
+// go on while the other waits on a load.  A second kernel (loader waves, below) runs the same
+// stages with separate waves for the loads and for the MFMAs; it takes the large-batch
+// down-projection.
 //
 // K pipeline: stages of BK = 32 K (64-byte rows) in a ring of NS = 4 stage buffers in LDS
 // (32 KiB each for 256 x 256), filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ...
@@ -76,7 +78,6 @@ constexpr int kOutSlots = 0;        // output row = slot (row0 + r)
 constexpr int kOutPairs = 1;        // output row = out_row[slot] (dropless pair order)
 constexpr int kOutPairsScaled = 2;  // ... and the row times row_scale[out_row[slot]]
 
-constexpr int kManyExperts = 32;         // up-projection on loader waves from this many experts
 constexpr int kGroupM = 8;               // token tiles per XCD group
 constexpr int kGroupN = 32 / kGroupM;    // weight tiles per XCD group
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset beyond every buffer range used
@@ -174,14 +175,15 @@ __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) 
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT, bool WP>
+template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT, bool WP,
+          int NWV = 4>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
     const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
     int a_rows, int e, int row0, int rows, int n0) {
   // waves along slots / features: 2 x 2, or 1 x 4 for 32-slot tiles
-  constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
+  constexpr int WM = NWV == 8 ? 4 : TM >= 64 ? 2 : 1, WN = NWV / WM;
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
   constexpr int KS = BK / 16;                // 16-K MFMA steps per stage
@@ -482,8 +484,8 @@ __device__ __forceinline__ void gemm_tile(
 // better, so the shorter height must win by 15 %).  The result does not depend on the choice:
 // each output element accumulates the same products in the same K order.
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT, bool WP>
-__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
+          int ACT, int OUT, bool WP, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, const int32_t* __restrict__ out_row,
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
       int mt, nt, e, row0, rows;
       if (!tile_of_block(tb.MT, NT, mt, nt)) return;
       tb.locate(offsets, lane, mt, e, row0, rows);
-      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP>(
+      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>(
           A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
       return;
     }
@@ -510,14 +512,13 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
   int mt, nt, e, row0, rows;
   if (!tile_of_block(ta.MT, NT, mt, nt)) return;
   ta.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP>(
+  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
 }
 
 // ---------------------------------------------------------------- loader waves
-// The large-batch down-projection (GEMM 2: no activation), and the up-projection (SiLU) of
-// layers with many experts, run on 512-thread blocks of 256 x 192 tiles.  Waves 4-7 only issue
-// the direct-to-LDS loads of the NS-deep ring of 32-K stages;
+// The large-batch down-projection (GEMM 2: no activation) runs on 512-thread blocks of 256 x 192
+// tiles.  Waves 4-7 only issue the direct-to-LDS loads of the NS-deep ring of 32-K stages;
 // waves 0-3 only read LDS fragments and run the MFMAs (128 features x 96 slots each, fp32
 // accumulators in VGPRs, two waves per SIMD).  The load issue, which can stall a wave behind a
 // busy memory pipeline, then no longer holds up the matrix cores.  One barrier per stage: the
@@ -542,7 +543,7 @@ __device__ __forceinline__ void gemm_tile_loaders(
                     FN >= 1 && FM >= 1 && NS >= 2 && (NS - 1) * kLoads < 64,
                 "tile shape");
   static_assert(BK % kPackK == 0, "a stage reads whole packed blocks");
-  static_assert(ACT == kActNone || ACT == kActSilu, "no gated tiles on loader waves");
+  static_assert(ACT == kActNone, "loader waves run the down-projection (no activation)");
   auto swz = [](int r) { return (r >> 2) & 3; };
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63;
@@ -680,7 +681,7 @@ __device__ __forceinline__ void gemm_tile_loaders(
       mfma(1);
     }
     __syncthreads();  // the ring is free for the staging tile
-    // bias (+ SiLU, + row scale) + bf16 into the staging tile: lane (r32, half) holds, for block (i, j),
+    // bias (+ row scale) + bf16 into the staging tile: lane (r32, half) holds, for block (i, j),
     // features 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -703,10 +704,6 @@ __device__ __forceinline__ void gemm_tile_loaders(
           v[1] = acc[i][j][4 * g4 + 1] + __uint_as_float(bb[g4].x & 0xFFFF0000u);
           v[2] = acc[i][j][4 * g4 + 2] + __uint_as_float(bb[g4].y << 16);
           v[3] = acc[i][j][4 * g4 + 3] + __uint_as_float(bb[g4].y & 0xFFFF0000u);
-          if (ACT == kActSilu) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = v[u] * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u]));
-          }
           if (OUT == kOutPairsScaled) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] *= rsc[j];
@@ -826,7 +823,7 @@ int compute_units() {
 }
 
 template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT, bool WP>
+          int ACT, int OUT, bool WP, int NWV = 4>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st,
@@ -837,7 +834,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS, OUT != kOutSlots) : 0;
   constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT, WP>;
+  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>;
   static std::atomic<bool> lds_allowed[kMaxDevices];
   if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
       err != hipSuccess)
@@ -852,11 +849,11 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   const int64_t grid = (ng_ub + 7) / 8 * 256;
   hipEvent_t t0, t1;
   if (take_gemm_events(&t0, &t1))
-    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, t0, t1, 0, A,
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, t0, t1, 0, A,
                           row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows,
                           compute_units() * MINB);
   else
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, A, row_token, offsets, W,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, A, row_token, offsets, W,
                        bias, out, out_row, row_scale, E, N, K, a_rows, compute_units() * MINB);
   return hipGetLastError();
 }
@@ -938,19 +935,15 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
       return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   }
-  // Loader waves (256 x 192 tiles) for the down-projection, and for the up-projection of
-  // layers with many experts, whose ragged token tiles waste less in 192-row tiles (fine
-  // layer, 64 experts: 382 -> 359 us).  With few experts the up-projection keeps 256 x 256
-  // tiles (8 experts: the loader waves were 1-3 % slower there).
+  // Large batches.  The down-projection runs on loader waves (256 x 192 tiles); the
+  // up-projection on 8-wave blocks of 256 x 256 tiles, two waves of 128 x 64 per SIMD, so one
+  // wave's MFMAs run while the other waits on a load (mid layer GEMM 1: 215 -> 195 us).
   if constexpr (ACT == kActNone)
     return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
-  else if constexpr (ACT == kActSilu)
-    if (E >= kManyExperts)
-      return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
-          A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
-  return launch_grouped_gemm<256, 256, 192, 32, 4, 1, true, GATHER, ACT, OUT, WP>(
-      A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  else
+    return launch_grouped_gemm<256, 256, 0, 32, 4, 1, true, GATHER, ACT, OUT, WP, 8>(
+        A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
 }
 
 // the weight layout of the shape picks the kernel
