@@ -410,9 +410,7 @@ def main():
     gemm2_flop = 2.0 * n_kept * dm * ff
     gemm1_flop = 2.0 * gemm2_flop if gated else gemm2_flop
     expert_s = (stage_ms["expert_up"] + stage_ms["expert_down"]) / 1e3
-    # GEMM 1 runs on loader waves from 32 experts (and never for the gated expert)
-    up_kernel = ("k_grouped_gemm_loaders" if wl.n_experts >= 32 and not gated
-                 else "k_grouped_gemm")
+    up_kernel = "k_grouped_gemm, 8 waves"  # the large-batch up-projection
     dom_kernel = {"expert_up": f"{up_kernel} (GEMM 1: gather + W1 + b1 + SiLU)",
                   "expert_down": "k_grouped_gemm_loaders (GEMM 2: W2 + b2)"}[dom]
     if dropless:
