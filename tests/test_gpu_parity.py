@@ -300,28 +300,31 @@ def test_gate_ties(dt):
     assert P.max_abs_rel(P.to_np(res["out"]), full["out"]) <= P.TOL[dt]
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(15))
 def test_dispatch_forced_patterns(seed):
     """moe_dispatch on caller-made routings: ties, -0.0, big experts spanning several sort
     chunks, capacities from 0 to above T, and out-of-range ids (dropped, not counted).  Seeds
     0, 4, 6, 7 and 8 (at most 1024 assignments) take the one-workgroup path, the others the
-    bucketed multi-kernel path; seeds 8 and 9 sit on either side of the switch."""
+    bucketed multi-kernel path; seeds 8 and 9 sit on either side of the switch.  Seed 10 puts
+    all 8192 assignments into one expert, seeds 11 and 12 spread 8192 over 256 and 64 experts
+    with 5 % invalid ids, seed 13 has 8193 assignments over 3 experts, seed 14 keeps every
+    assignment (capacity above the count)."""
     rng = np.random.Generator(np.random.PCG64(100 + seed))
-    T = [5, 3000, 20000, 70000, 1, 9000, 400, 300, 512, 1025][seed]
-    E = [3, 8, 64, 4, 1, 256, 256, 5, 16, 7][seed]
-    k = min(E, [2, 2, 6, 2, 1, 3, 2, 3, 2, 1][seed])
+    T = [5, 3000, 20000, 70000, 1, 9000, 400, 300, 512, 1025, 8192, 8192, 2048, 2731, 1500][seed]
+    E = [3, 8, 64, 4, 1, 256, 256, 5, 16, 7, 8, 256, 64, 3, 2][seed]
+    k = min(E, [2, 2, 6, 2, 1, 3, 2, 3, 2, 1, 1, 1, 4, 3, 2][seed])
     ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32) if T < 5000 else \
         np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
-    if seed == 3:
-        ids[:, 0] = 0  # one hot expert with T assignments: several sort chunks
+    if seed in (3, 10):
+        ids[:, 0] = 0  # one hot expert with T assignments
     vals = np.array([0.5, 0.25, -0.0, 0.0, 0.125, 0.75], np.float32)
     gates = vals[rng.integers(len(vals), size=(T, k))] if seed % 2 == 0 else \
         rng.random((T, k)).astype(np.float32)
     bad = np.zeros((T, k), bool)
-    if seed in (1, 5, 6, 9):
+    if seed in (1, 5, 6, 9, 11, 12):
         bad = rng.random((T, k)) < (0.01 if seed in (1, 5) else 0.05)
         ids[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
-    cap = [0, 400, 1536, 16384, 1, 120, 3, 100, 40, 100][seed]
+    cap = [0, 400, 1536, 16384, 1, 120, 3, 100, 40, 100, 5000, 3, 0, 2000, 3000][seed]
     shape = B.make_shape(T, 8, 8, E, k, cap, B.MOE_BF16)
     res = L.dispatch(shape, torch.from_numpy(ids).to(DEV), torch.from_numpy(gates).to(DEV))
     # the oracle knows no invalid ids: give them an extra last expert E, which leaves the
