@@ -175,14 +175,13 @@ __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) 
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool INTERLEAVE, bool GATHER, int ACT, int OUT, bool WP,
-          int NWV = 4>
+template <int TN, int TM, int BK, int NS, bool GATHER, int ACT, int OUT, bool WP, int NWV = 4>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
     const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
     int a_rows, int e, int row0, int rows, int n0) {
-  // waves along slots / features: 2 x 2, or 1 x 4 for 32-slot tiles
+  // waves along slots / features: 2 x 2, 4 x 2 for 8 waves, or 1 x 4 for 32-slot tiles
   constexpr int WM = NWV == 8 ? 4 : TM >= 64 ? 2 : 1, WN = NWV / WM;
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
@@ -390,13 +389,8 @@ __device__ __forceinline__ void gemm_tile(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kLoads));
     __syncthreads();
     MOE_READ_FRAGS(kt + 1, 0, 0);  // past the last stage this reads a slot nobody uses
-    if (INTERLEAVE) {
-      __builtin_amdgcn_sched_barrier(0);
-      MOE_MFMA_STEP_ISSUE((KS - 1) % 2, kt + NS);
-    } else {
-      MOE_ISSUE_STAGE(kt + NS);
-      MOE_MFMA_STEP((KS - 1) % 2);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_MFMA_STEP_ISSUE((KS - 1) % 2, kt + NS);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the zero-fill loads land before the LDS reuse
 #undef MOE_STAGE_BASE
@@ -477,42 +471,23 @@ __device__ __forceinline__ void gemm_tile(
 }
 
 // The grouped GEMM kernel.  Each block works out the token tiles of every expert from
-// expert_offsets (device memory: the kept-row counts are only known on the device).  With
-// TMB > 0 it can run TMB-high token tiles instead of TMA-high ones; every block makes the same
-// choice from the same offsets: the height whose grid needs the fewest rounds over the `slots`
-// blocks the GPU runs at once, weighted by the tile height (taller tiles use the matrix cores
-// better, so the shorter height must win by 15 %).  The result does not depend on the choice:
-// each output element accumulates the same products in the same K order.
-template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT, bool WP, int NWV = 4>
+// expert_offsets (device memory: the kept-row counts are only known on the device), finds its
+// own (expert, token tile, feature tile) and exits if that tile does not exist.
+template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
+          int NWV = 4>
 __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, const int32_t* __restrict__ out_row,
-    const float* __restrict__ row_scale, int E, int N, int K, int a_rows, int slots) {
+    const float* __restrict__ row_scale, int E, int N, int K, int a_rows) {
   const int lane = threadIdx.x & 63;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;  // output features per tile
   const int NT = (N + TNO - 1) / TNO;
-  const TokenTiles<TMA> ta(offsets, E, lane);
-  bool use_b = false;
-  if constexpr (TMB > 0) {
-    const TokenTiles<TMB> tb(offsets, E, lane);
-    const int64_t ra = ((int64_t)ta.MT * NT + slots - 1) / slots;
-    const int64_t rb = ((int64_t)tb.MT * NT + slots - 1) / slots;
-    use_b = rb * TMB * 115 < ra * TMA * 100;
-    if (use_b) {
-      int mt, nt, e, row0, rows;
-      if (!tile_of_block(tb.MT, NT, mt, nt)) return;
-      tb.locate(offsets, lane, mt, e, row0, rows);
-      gemm_tile<TN, TMB, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>(
-          A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
-      return;
-    }
-  }
+  const TokenTiles<TM> tt(offsets, E, lane);
   int mt, nt, e, row0, rows;
-  if (!tile_of_block(ta.MT, NT, mt, nt)) return;
-  ta.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TMA, BK, NS, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>(
+  if (!tile_of_block(tt.MT, NT, mt, nt)) return;
+  tt.locate(offsets, lane, mt, e, row0, rows);
+  gemm_tile<TN, TM, BK, NS, GATHER, ACT, OUT, WP, NWV>(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
 }
 
@@ -808,40 +783,23 @@ constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
   return ring > tile ? ring : tile;
 }
 
-// compute units of the current device (cached per device)
-int compute_units() {
-  static std::atomic<int> cus[kMaxDevices];  // 0 until first asked (same value from any thread)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cus[dev].load(std::memory_order_relaxed) == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return cus[dev];
-}
-
-template <int TN, int TMA, int TMB, int BK, int NS, int MINB, bool INTERLEAVE, bool GATHER,
-          int ACT, int OUT, bool WP, int NWV = 4>
+template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
+          int NWV = 4>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st,
                                const int32_t* out_row = nullptr,
                                const float* row_scale = nullptr) {
   if (rows_ub <= 0) return hipSuccess;
-  constexpr size_t lds_a = tile_lds(TN, TMA, BK, NS, OUT != kOutSlots);
-  constexpr size_t lds_b = TMB > 0 ? tile_lds(TN, TMB, BK, NS, OUT != kOutSlots) : 0;
-  constexpr size_t lds = lds_a > lds_b ? lds_a : lds_b;
+  constexpr size_t lds = tile_lds(TN, TM, BK, NS, OUT != kOutSlots);
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TMA, TMB, BK, NS, MINB, INTERLEAVE, GATHER, ACT, OUT, WP, NWV>;
+  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, GATHER, ACT, OUT, WP, NWV>;
   static std::atomic<bool> lds_allowed[kMaxDevices];
   if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
       err != hipSuccess)
     return err;
-  // upper bound on groups for the shorter tile height: token tiles <= rows_ub / TM + E
-  constexpr int tm_min = TMB > 0 && TMB < TMA ? TMB : TMA;
-  const int64_t mt_ub = (rows_ub + tm_min - 1) / tm_min + E;
+  // upper bound on groups: token tiles <= rows_ub / TM + E
+  const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;
   const int64_t nt = (N + TNO - 1) / TNO;
   const int64_t nq = (nt + kGroupN - 1) / kGroupN;
@@ -850,11 +808,10 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   hipEvent_t t0, t1;
   if (take_gemm_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, t0, t1, 0, A,
-                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows,
-                          compute_units() * MINB);
+                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows);
   else
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, A, row_token, offsets, W,
-                       bias, out, out_row, row_scale, E, N, K, a_rows, compute_units() * MINB);
+                       bias, out, out_row, row_scale, E, N, K, a_rows);
   return hipGetLastError();
 }
 
@@ -922,17 +879,17 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
                     const float* row_scale) {
   if constexpr (ACT == kActGated) {
     if (small)
-      return launch_grouped_gemm<128, 64, 0, 64, 3, 2, true, GATHER, ACT, OUT, WP>(
+      return launch_grouped_gemm<128, 64, 64, 3, 2, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   } else if constexpr (ACT == kActSilu) {
     // the up-projection's many feature tiles: 128 weight rows x 32 slots, so a block streams
     // twice the weight rows per stage and the grid is half as many blocks
     if (small)
-      return launch_grouped_gemm<128, 32, 0, 64, 3, 2, true, GATHER, ACT, OUT, WP>(
+      return launch_grouped_gemm<128, 32, 64, 3, 2, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   } else {
     if (small)
-      return launch_grouped_gemm<64, 64, 0, 64, 4, 2, true, GATHER, ACT, OUT, WP>(
+      return launch_grouped_gemm<64, 64, 64, 4, 2, GATHER, ACT, OUT, WP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   }
   // Large batches.  The down-projection runs on loader waves (256 x 192 tiles); the
@@ -942,7 +899,7 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
     return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   else
-    return launch_grouped_gemm<256, 256, 0, 32, 4, 1, true, GATHER, ACT, OUT, WP, 8>(
+    return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
 }
 
