@@ -98,7 +98,11 @@ __device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
 // lds_base + 16 * lane.  Written in assembly so the compiler does not order its own LDS reads
 // behind these loads (it cannot tell which ring slot they fill); the kernel waits for them
 // explicitly (vmcnt) before the barrier that publishes each stage, and waits for all of them
-// before it exits.  The instruction has no destination registers.
+// before it exits.  The instruction has no destination registers.  M0 (the LDS address of the
+// load) is written here and so named as clobbered; clang warns on every use that M0 is a
+// reserved register, which is the point, so that warning is off for this function.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(i32x4_t srd, uint32_t lds_base, uint32_t voff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -108,6 +112,7 @@ __device__ __forceinline__ void lds_dma16(i32x4_t srd, uint32_t lds_base, uint32
       : "s"(lds_base), "v"(voff), "s"(srd)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are outstanding and leaves
 // the other counters unconstrained (gfx9 encoding: vmcnt bits 3:0 and 15:14).
