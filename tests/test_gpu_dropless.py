@@ -73,6 +73,8 @@ DROPLESS_SMALL = [
     (65, 264, 328, 8, 2, True),
     (300, 128, 200, 16, 4, True),
     (1000, 136, 72, 8, 3, True),
+    (700, 64, 96, 256, 8, False),  # 256 experts: multi-pass router, many small expert groups
+    (4000, 64, 96, 128, 4, True),
 ]
 
 

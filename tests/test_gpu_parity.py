@@ -380,6 +380,7 @@ PADDED_SMALL = [
     (65, 264, 328, 8, 2, 1.25, "bf16"),
     (1000, 136, 72, 8, 3, 1.0, "bf16"),
     (300, 128, 256, 16, 4, 0.25, "bf16"),
+    (700, 64, 96, 256, 8, 1.0, "bf16"),
     (65, 12, 20, 8, 2, 0.75, "f32"),
     (200, 16, 16, 200, 3, 2.0, "f32"),
 ]
@@ -454,6 +455,7 @@ GATED_SMALL = [
     (1000, 136, 72, 8, 3, 1.0),
     (517, 256, 264, 5, 1, 8.0),
     (300, 128, 200, 16, 4, 0.25),
+    (4000, 64, 96, 128, 4, 2.0),
 ]
 
 
