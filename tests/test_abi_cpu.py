@@ -62,6 +62,8 @@ def test_workspace_and_max_rows(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("top_k", 0, 1), ("top_k", 9, 1), ("n_experts", 0, 1), ("n_experts", 300, 2),
     ("capacity", -1, 1), ("T", -5, 1), ("d_model", 12, 2), ("dtype", 7, 2),
+    # 32-bit limits: T * top_k assignments, bytes of x, tile offsets into d_ff rows
+    ("T", 1 << 30, 2), ("T", 1 << 24, 2), ("d_ff", 1 << 22, 2),
 ])
 def test_shape_errors_before_any_launch(lib, field, value, status):
     s = B.make_shape(16, 64, 64, 8, 2, 4, B.MOE_BF16)
