@@ -123,11 +123,15 @@ def cpu_baseline(inp, wl, cap, dropless=False):
     t = float(np.mean(times))
     # the per-expert float64 weight conversion is inside the timed region: it is part of
     # what the oracle does to evaluate the layer
+    # expert-GEMM FLOP of the layer (a gated expert's GEMM 1 has 2 d_ff outputs) over the whole
+    # oracle layer's time
+    flop = 2 * int(res["n_kept"]) * wl.d_model * wl.d_ff * (3 if wl.expert == "gated" else 2)
     return {"value": wl.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"whole layer on the full {wl.name} batch ({wl.T} tokens), "
                       f"{len(times)} runs, {t:.2f} s each, float64 NumPy/BLAS",
             "seconds": round(t, 3),
-            "n_kept": int(res["n_kept"])}
+            "n_kept": int(res["n_kept"]),
+            "expert_gemm_gflops": round(flop / t / 1e9, 1)}
 
 
 def bench_pool(args, wl, inp):
