@@ -155,12 +155,18 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma(
   const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x, (uint32_t)(T * d * (int64_t)sizeof(TIn)));
   const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(w, (uint32_t)((int64_t)E * d * sizeof(TIn)));
 
+  // with a single 16 x 16 tile per wave, even and odd MFMA steps go to two accumulators, so
+  // consecutive MFMAs do not wait on each other (the two are added at the end: a permutation of
+  // the summation order only)
+  constexpr int NACC = R * EBG == 1 ? 2 : 1;
   for (int b0 = 0; b0 < EB; b0 += EBG) {
-    f64x4_t acc[R][EBG];
+    f64x4_t accs[NACC][R][EBG];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int a = 0; a < NACC; ++a)
 #pragma unroll
-      for (int bb = 0; bb < EBG; ++bb) acc[r][bb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int bb = 0; bb < EBG; ++bb) accs[a][r][bb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
     // wave w takes chunk quads w, w + NW, ... in that order, with PF quads in flight: the raw
     // loads of quad cq + PF NW are issued as soon as quad cq is widened (quads past the end
@@ -196,11 +202,16 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma(
           for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int bb = 0; bb < EBG; ++bb)
-              acc[r][bb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[r][s8], wb[bb][s8],
-                                                                acc[r][bb], 0, 0, 0);
+              accs[s8 % NACC][r][bb] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                  xa[r][s8], wb[bb][s8], accs[s8 % NACC][r][bb], 0, 0, 0);
       }
     }
 
+    auto& acc = accs[0];
+    if constexpr (NACC == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[0][0][j] += accs[1][0][0][j];
+    }
     // lane l, register j of a tile holds token 4 j + l / 16, expert l % 16 of the tile
     if (wave > 0) {
       double* mine = lds + (wave - 1) * kPart;
