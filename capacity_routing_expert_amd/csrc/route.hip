@@ -51,7 +51,7 @@ __device__ void finish_group(double* lds, const float* __restrict__ b_router, in
   }
   __syncthreads();
 
-  // softmax + top-k: LPT = S lanes per token (a power of two <= 4, inside one wave);
+  // softmax + top-k: LPT = S lanes per token (a power of two, inside one wave);
   // lane `sub` owns experts e = sub (mod LPT)
   const int LPT = S;
   const int ti = threadIdx.x / LPT, sub = threadIdx.x % LPT;
@@ -253,10 +253,10 @@ constexpr size_t route_lds_max() { return (size_t)8 * (7 * 2 * 256 + 256 * 16); 
 
 namespace {
 
-template <typename TIn, int EBG>
+template <typename TIn, int EBG, int NW>
 hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                         int32_t* ids, float* gates, float* logits, hipStream_t st) {
-  constexpr int R = 1, NW = 8, TT = 16 * R;
+  constexpr int R = 1, TT = 16 * R;
   // chunk quads in flight per wave besides the one being multiplied: with branch-free loads one
   // is enough (4 and 8 measured no faster, and 8 slower on the large layers)
   constexpr int PF = 1;
@@ -272,16 +272,25 @@ hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const fl
   return hipGetLastError();
 }
 
-// Tile plan: 16 tokens per block of 8 waves; one or two tiles of 16 experts per pass over x,
-// more experts take more passes (the block's x rows come back from L2).  Two tiles need about
-// 120 VGPRs, so two blocks share a CU and one block's cross-wave sum and softmax overlap the
-// other's MFMAs; four tiles per pass (252 VGPRs, one block per CU) ran the 64-expert fine
-// layer's router at 118 us against 97 us.
+// Tile plan: 16 tokens per block; one or two tiles of 16 experts per pass over x, more experts
+// take more passes (the block's x rows come back from L2).  Two tiles need about 120 VGPRs, so
+// several blocks share a CU and one block's cross-wave sum and softmax overlap another's MFMAs
+// (four tiles per pass, 252 VGPRs and one block per CU, ran the 64-expert fine layer's router
+// at 118 us against 97 us).  Batches of at least 8192 tokens (two blocks or more per CU) use
+// 4-wave blocks, which fit more blocks per CU (fine 104 -> 95 us); smaller ones use 8 waves,
+// which shortens each wave's walk over d (decode 10.7 -> 10.4 us).
+template <typename TIn, int EBG>
+hipError_t route_waves(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
+                       int32_t* ids, float* gates, float* logits, hipStream_t st) {
+  if (s.T >= 8192) return route_launch<TIn, EBG, 4>(s, x, w, b_router, ids, gates, logits, st);
+  return route_launch<TIn, EBG, 8>(s, x, w, b_router, ids, gates, logits, st);
+}
+
 template <typename TIn>
 hipError_t route_any(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                      int32_t* ids, float* gates, float* logits, hipStream_t st) {
-  if (s.n_experts <= 16) return route_launch<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
-  return route_launch<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);
+  if (s.n_experts <= 16) return route_waves<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
+  return route_waves<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);
 }
 
 }  // namespace

@@ -254,15 +254,18 @@ SMALL = [
     # up-projection's 32-row token tiles come several to an expert
     (60, 72, 136, 4, 2, 2.0, "bf16"),
     (200, 64, 264, 8, 2, 4.0, "bf16"),
-    # more than 64 experts: the router takes several passes of 64 over x (bf16 inputs)
+    # more than 32 experts: the router takes several passes of 32 over x (bf16 inputs)
     (700, 64, 96, 256, 8, 1.0, "bf16"),
     (90, 32, 64, 160, 4, 2.0, "bf16"),
     (4000, 64, 96, 128, 4, 2.0, "bf16"),  # ... with the large-batch expert tiles
+    # 8192 tokens or more: 4-wave router blocks; 40 experts leave the last pass half empty
+    (8192, 32, 48, 40, 3, 1.0, "bf16"),
     (1, 4, 8, 4, 1, 1.25, "f32"),
     (7, 5, 9, 3, 2, 1.0, "f32"),
     (65, 12, 20, 8, 2, 0.75, "f32"),
     (333, 24, 40, 64, 8, 1.0, "f32"),
     (200, 16, 16, 200, 3, 2.0, "f32"),
+    (8200, 8, 12, 24, 2, 1.0, "f32"),
 ]
 
 
