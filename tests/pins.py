@@ -14,6 +14,8 @@ What pins what:
     special case, scipy's softmax;
   * brute force: integer-valued router logits summed exactly in Python integers; top-k by
     enumerating all k-subsets; slot ranks by an independent counting definition;
+  * the rounding of the gates to fp32 before top-k: two probabilities 0.5 -/+ 2.5e-10 both
+    round to 0.5, so the tie goes to the lower expert although the float64 values differ;
   * invariants: counts sum to T*k, slot map is a bijection, kept gates dominate dropped
     gates, permutation equivariance, capacity 0 returns the input;
   * the gated expert: SiLU(ln 3) = (3/4) ln 3 through a gate and an up row, a zero gate
@@ -181,6 +183,33 @@ def check_gates_unrenormalised(o):
         assert r["ids"][t, 0] == int(np.argmax(p[t]))
     # with 6 experts the two chosen gates cannot sum to one
     assert np.all(r["gates"].astype(np.float64).sum(axis=1) < 1.0)
+
+
+def check_gates_rounded_before_topk(o):
+    """Top-k ranks the fp32 gates, not the float64 probabilities.  Logits (0, 1e-9) give
+    probabilities 0.5 -/+ 2.5e-10; both lie within half an fp32 ulp of 0.5 (the fp32 neighbours
+    of 0.5 are 0.5 - 2^-25 and 0.5 + 2^-24), so both gates are exactly 0.5 and the tie goes to
+    the lower expert, although expert 1's float64 probability is the larger."""
+    x = np.array([[1.0]])
+    w = np.array([[0.0], [1e-9]])
+    r = o.route(x, w, None, 1)
+    assert r["probs"][0, 1] > r["probs"][0, 0]
+    assert int(r["ids"][0, 0]) == 0
+    assert r["gates"].dtype == np.float32 and float(r["gates"][0, 0]) == 0.5
+    r2 = o.route(x, w, None, 2)
+    assert list(r2["ids"][0]) == [0, 1] and list(r2["gates"][0]) == [0.5, 0.5]
+    # (0, ln 3): 0.25 and 0.75 exactly after the rounding, whatever the last float64 bits
+    r3 = o.route(np.array([[1.0]]), np.array([[0.0], [math.log(3.0)]]), None, 2)
+    assert list(r3["ids"][0]) == [1, 0] and list(r3["gates"][0]) == [0.75, 0.25]
+    # the fill order compares the rounded gates too: two tokens whose float64 probabilities for
+    # expert 1 differ below fp32 resolution tie, and the lower token takes the single slot
+    x2 = np.array([[1.0], [1.0 + 2.0 ** -20]])
+    w2 = np.array([[0.0], [2.0 ** -12]])
+    r4 = o.route(x2, w2, None, 1)
+    assert list(r4["ids"][:, 0]) == [1, 1] and r4["probs"][1, 1] > r4["probs"][0, 1]
+    assert r4["gates"][0, 0] == r4["gates"][1, 0]
+    d = o.dispatch(r4["ids"], r4["gates"], 2, 1)
+    assert list(d["drop_mask"][:, 0]) == [0, 1]
 
 
 # ----------------------------------------------------------------------------- dispatch
@@ -686,6 +715,7 @@ def check_batches_output(o):
 ALL_CHECKS = [
     check_capacity_page, check_capacity_closed_forms, check_softmax_closed_forms,
     check_router_logits_exact, check_topk_bruteforce, check_gates_unrenormalised,
+    check_gates_rounded_before_topk,
     check_worked_example_dispatch, check_dispatch_exhaustive, check_dispatch_invariants,
     check_permutation_equivariance, check_silu_closed_forms, check_expert_ffn_vs_torch,
     check_worked_example_outputs, check_dense_special_case, check_dropless_per_token,

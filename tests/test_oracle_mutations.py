@@ -53,6 +53,10 @@ def _topk_tie_high(g32, k):
     return ids, np.take_along_axis(g32, ids, axis=1)
 
 
+def _gates_unrounded(p):
+    return np.asarray(p, np.float64)  # top-k on the float64 probabilities
+
+
 def _topk_renorm(g32, k):
     ids, gates = _orig["top_k"](g32, k)
     return ids, (gates / gates.sum(axis=1, keepdims=True)).astype(np.float32)
@@ -334,6 +338,7 @@ MUTATIONS = {
     "router_dropped_bias": {"router_logits": _logits_no_bias},
     "softmax_no_denominator": {"softmax": _softmax_no_norm},
     "softmax_wrong_axis": {"softmax": _softmax_wrong_axis},
+    "gates_not_rounded_to_fp32": {"gates_fp32": _gates_unrounded},
     "topk_ties_to_higher_expert": {"top_k": _topk_tie_high},
     "topk_renormalised": {"top_k": _topk_renorm},
     "topk_smallest": {"top_k": _topk_ascending},
