@@ -1,8 +1,9 @@
 """Thin ctypes binding of libmoe (include/moe.h): argument marshalling only.
 
 Every step of the layer runs in the HIP library; this module only turns torch tensors into
-device pointers, picks torch's current stream, checks dtypes/devices/shapes of the tensors
-it is handed, and raises on a non-OK status.  torch is imported before the library is
+device pointers, picks torch's current stream, checks the dtype, device, contiguity and size
+(number of elements against what the shape needs) of every tensor it is handed, and raises on
+a non-OK status.  torch is imported before the library is
 loaded so that both use torch's HIP runtime (one runtime per process).
 
 The library is loaded on first use; if it has not been built the call raises, there is no
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_route.argtypes = [SP, P, P, P, P, P, P, P, SZ, P]
-        L.moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_expert_ffn.argtypes = [SP, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [SP, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -148,13 +149,18 @@ def last_error() -> str:
     return lib().moe_last_error().decode()
 
 
-def _ptr(t: torch.Tensor | None, name: str, dtype=None, device=None) -> ctypes.c_void_p | None:
+def _ptr(t: torch.Tensor | None, name: str, dtype=None, device=None,
+         numel: int | None = None) -> ctypes.c_void_p | None:
+    """Device pointer of `t` after checking its dtype, device, contiguity and that it holds at
+    least `numel` elements (the library writes or reads that many through the raw pointer)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the shape needs {numel}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     if device is not None and t.device != device:
@@ -162,6 +168,22 @@ def _ptr(t: torch.Tensor | None, name: str, dtype=None, device=None) -> ctypes.c
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _n(shape: MoeShape) -> dict:
+    """Element counts the shape needs per argument kind."""
+    T, d, f, E, k = int(shape.T), int(shape.d_model), int(shape.d_ff), int(shape.n_experts), int(shape.top_k)
+    rows = max(int(max_kept_rows(shape)), 0)
+    return {"x": T * d, "wr": E * d, "E": E, "E1": E + 1, "Tk": T * k, "TE": T * E,
+            "rows": rows, "yrows": rows * d, "f": f, "d": d, "T": T, "k": k}
+
+
+def _w(shape: MoeShape, rows: int, cols: int) -> int:
+    """Elements of one expert weight array of [E, rows, cols] in the shape's layout."""
+    E = int(shape.n_experts)
+    if shape.weight_layout == MOE_WEIGHTS_PACKED and shape.dtype == MOE_BF16:
+        return E * ((cols + 31) // 32) * rows * 32
+    return E * rows * cols  # row-major (other layouts and dtypes are refused by the library)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -179,59 +201,77 @@ def _dtype_of(shape: MoeShape):
 
 
 def moe_route(shape, x, w_router, b_router, topk_ids, topk_gates, logits, ws, stream=None):
-    dt = _dtype_of(shape)
-    _check(lib().moe_route(ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
-                           _ptr(b_router, "b_router", torch.float32),
-                           _ptr(topk_ids, "topk_ids", torch.int32),
-                           _ptr(topk_gates, "topk_gates", torch.float32),
-                           _ptr(logits, "logits", torch.float32), _ptr(ws, "ws", torch.uint8),
-                           ws.numel(), _stream(stream)), "moe_route")
+    dt, n = _dtype_of(shape), _n(shape)
+    _check(lib().moe_route(ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+                           _ptr(w_router, "w_router", dt, numel=n["wr"]),
+                           _ptr(b_router, "b_router", torch.float32, numel=n["E"]),
+                           _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+                           _ptr(topk_gates, "topk_gates", torch.float32, numel=n["Tk"]),
+                           _ptr(logits, "logits", torch.float32, numel=n["TE"]),
+                           _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "moe_route")
 
 
 def moe_dispatch(shape, topk_ids, topk_gates, expert_counts, expert_offsets, slot_of, row_token,
-                 drop_mask, ws, stream=None):
-    _check(lib().moe_dispatch(ctypes.byref(shape), _ptr(topk_ids, "topk_ids", torch.int32),
-                              _ptr(topk_gates, "topk_gates", torch.float32),
-                              _ptr(expert_counts, "expert_counts", torch.int32),
-                              _ptr(expert_offsets, "expert_offsets", torch.int32),
-                              _ptr(slot_of, "slot_of", torch.int32),
-                              _ptr(row_token, "row_token", torch.int32) if row_token.numel() else None,
-                              _ptr(drop_mask, "drop_mask", torch.uint8),
+                 drop_mask, ws, x=None, x_routed=None, stream=None):
+    """x and x_routed (optional, together): the token rows copied into slot order."""
+    dt, n = _dtype_of(shape), _n(shape)
+    _check(lib().moe_dispatch(ctypes.byref(shape),
+                              _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+                              _ptr(topk_gates, "topk_gates", torch.float32, numel=n["Tk"]),
+                              _ptr(expert_counts, "expert_counts", torch.int32, numel=n["E"]),
+                              _ptr(expert_offsets, "expert_offsets", torch.int32, numel=n["E1"]),
+                              _ptr(slot_of, "slot_of", torch.int32, numel=n["Tk"]),
+                              _ptr(row_token, "row_token", torch.int32, numel=n["rows"])
+                              if row_token.numel() else None,
+                              _ptr(drop_mask, "drop_mask", torch.uint8, numel=n["Tk"]),
+                              _ptr(x, "x", dt, numel=n["x"]),
+                              _ptr(x_routed, "x_routed", dt, numel=n["yrows"])
+                              if x_routed is not None and x_routed.numel() else None,
                               _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
            "moe_dispatch")
 
 
 def moe_expert_ffn(shape, x, row_token, expert_offsets, w1, b1, w2, b2, y_rows, ws, stream=None):
-    dt = _dtype_of(shape)
-    _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x, "x", dt),
-                                _ptr(row_token, "row_token", torch.int32) if row_token.numel() else None,
-                                _ptr(expert_offsets, "expert_offsets", torch.int32),
-                                _ptr(w1, "w1", dt), _ptr(b1, "b1", dt), _ptr(w2, "w2", dt),
-                                _ptr(b2, "b2", dt),
-                                _ptr(y_rows, "y_rows", dt) if y_rows.numel() else None,
+    dt, n = _dtype_of(shape), _n(shape)
+    f, d = n["f"], n["d"]
+    _check(lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+                                _ptr(row_token, "row_token", torch.int32, numel=n["rows"])
+                                if row_token.numel() else None,
+                                _ptr(expert_offsets, "expert_offsets", torch.int32, numel=n["E1"]),
+                                _ptr(w1, "w1", dt, numel=_w(shape, f, d)),
+                                _ptr(b1, "b1", dt, numel=n["E"] * f),
+                                _ptr(w2, "w2", dt, numel=_w(shape, d, f)),
+                                _ptr(b2, "b2", dt, numel=n["E"] * d),
+                                _ptr(y_rows, "y_rows", dt, numel=n["yrows"]) if y_rows.numel() else None,
                                 _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
            "moe_expert_ffn")
 
 
 def moe_combine(shape, x, topk_gates, slot_of, y_rows, out, stream=None):
-    dt = _dtype_of(shape)
-    _check(lib().moe_combine(ctypes.byref(shape), _ptr(x, "x", dt),
-                             _ptr(topk_gates, "topk_gates", torch.float32),
-                             _ptr(slot_of, "slot_of", torch.int32),
-                             _ptr(y_rows, "y_rows", dt) if y_rows.numel() else None,
-                             _ptr(out, "out", dt), _stream(stream)), "moe_combine")
+    dt, n = _dtype_of(shape), _n(shape)
+    _check(lib().moe_combine(ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+                             _ptr(topk_gates, "topk_gates", torch.float32, numel=n["Tk"]),
+                             _ptr(slot_of, "slot_of", torch.int32, numel=n["Tk"]),
+                             _ptr(y_rows, "y_rows", dt, numel=n["yrows"]) if y_rows.numel() else None,
+                             _ptr(out, "out", dt, numel=n["x"]), _stream(stream)), "moe_combine")
 
 
 def _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
-                  slot_of, drop_mask, expert_counts, ws):
-    dt = _dtype_of(shape)
-    return [ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
-            _ptr(b_router, "b_router", torch.float32), _ptr(w1, "w1", dt), _ptr(b1, "b1", dt),
-            _ptr(w2, "w2", dt), _ptr(b2, "b2", dt), _ptr(out, "out", dt),
-            _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_gates, "topk_gates", torch.float32),
-            _ptr(slot_of, "slot_of", torch.int32), _ptr(drop_mask, "drop_mask", torch.uint8),
-            _ptr(expert_counts, "expert_counts", torch.int32), _ptr(ws, "ws", torch.uint8),
-            ws.numel()]
+                  slot_of, drop_mask, expert_counts, ws, gated=False):
+    dt, n = _dtype_of(shape), _n(shape)
+    f, d, E = n["f"], n["d"], n["E"]
+    return [ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+            _ptr(w_router, "w_router", dt, numel=n["wr"]),
+            _ptr(b_router, "b_router", torch.float32, numel=E),
+            _ptr(w1, "w1", dt, numel=_w(shape, 2 * f if gated else f, d)),
+            _ptr(b1, "b1", dt, numel=E * f), _ptr(w2, "w2", dt, numel=_w(shape, d, f)),
+            _ptr(b2, "b2", dt, numel=E * d), _ptr(out, "out", dt, numel=n["x"]),
+            _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+            _ptr(topk_gates, "topk_gates", torch.float32, numel=n["Tk"]),
+            _ptr(slot_of, "slot_of", torch.int32, numel=n["Tk"]),
+            _ptr(drop_mask, "drop_mask", torch.uint8, numel=n["Tk"]),
+            _ptr(expert_counts, "expert_counts", torch.int32, numel=E), _ptr(ws, "ws", torch.uint8),
+            ws.numel() if ws is not None else 0]
 
 
 def moe_layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
@@ -279,7 +319,8 @@ def moe_layer_forward_padded(shape, x, w_router, b_router, w1, b1, w2, b2, out, 
     handles = None
     if events is not None:
         handles = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
-    y = _ptr(y_rows, "y_rows", dt) if y_rows is not None and y_rows.numel() else None
+    y = (_ptr(y_rows, "y_rows", dt, numel=int(shape.n_experts) * int(shape.capacity) * int(shape.d_model))
+         if y_rows is not None and y_rows.numel() else None)
     # the padded call takes y_rows before the workspace
     _check(lib().moe_layer_forward_padded(*args[:-2], y, args[-2], args[-1], _stream(stream),
                                           handles), "moe_layer_forward_padded")
@@ -290,18 +331,14 @@ def moe_layer_forward_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids
                             ws=None, events=None, stream=None):
     """Gated experts: w13 [E, 2 d_ff, d_model] (gate rows first), w2 [E, d_model, d_ff], no
     biases; bf16 only.  `events` None or 6 recorded torch.cuda.Event(enable_timing=True)."""
-    dt = _dtype_of(shape)
     handles = None
     if events is not None:
         handles = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in events])
-    _check(lib().moe_layer_forward_gated(
-        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
-        _ptr(b_router, "b_router", torch.float32), _ptr(w13, "w13", dt), _ptr(w2, "w2", dt),
-        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
-        _ptr(topk_gates, "topk_gates", torch.float32), _ptr(slot_of, "slot_of", torch.int32),
-        _ptr(drop_mask, "drop_mask", torch.uint8), _ptr(expert_counts, "expert_counts", torch.int32),
-        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), handles),
-        "moe_layer_forward_gated")
+    a = _forward_args(shape, x, w_router, b_router, w13, None, w2, None, out, topk_ids,
+                      topk_gates, slot_of, drop_mask, expert_counts, ws, gated=True)
+    # the gated call has no biases: shape, x, w_router, b_router, w13, w2, out, ...
+    _check(lib().moe_layer_forward_gated(*a[:5], a[6], *a[8:], _stream(stream), handles),
+           "moe_layer_forward_gated")
 
 
 def _events(events, n=6):
@@ -314,11 +351,14 @@ def _events(events, n=6):
 
 def moe_dispatch_pairs(shape, topk_ids, expert_counts, expert_offsets, sorted_pairs, row_token,
                        ws, stream=None):
-    _check(lib().moe_dispatch_pairs(ctypes.byref(shape), _ptr(topk_ids, "topk_ids", torch.int32),
-                                    _ptr(expert_counts, "expert_counts", torch.int32),
-                                    _ptr(expert_offsets, "expert_offsets", torch.int32),
-                                    _ptr(sorted_pairs, "sorted_pairs", torch.int32),
-                                    _ptr(row_token, "row_token", torch.int32),
+    n = _n(shape)
+    _check(lib().moe_dispatch_pairs(ctypes.byref(shape),
+                                    _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+                                    _ptr(expert_counts, "expert_counts", torch.int32, numel=n["E"]),
+                                    _ptr(expert_offsets, "expert_offsets", torch.int32,
+                                         numel=n["E1"]),
+                                    _ptr(sorted_pairs, "sorted_pairs", torch.int32, numel=n["Tk"]),
+                                    _ptr(row_token, "row_token", torch.int32, numel=n["Tk"]),
                                     _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
            "moe_dispatch_pairs")
 
@@ -326,24 +366,44 @@ def moe_dispatch_pairs(shape, topk_ids, expert_counts, expert_offsets, sorted_pa
 def moe_expert_ffn_pairs(shape, x, sorted_pairs, row_token, expert_offsets, w1, b1, w2, b2,
                          topk_weights, pair_rows, ws, gated=False, stream=None):
     """gated: w1 is w13 [E, 2 d_ff, d_model] and b1, b2 are ignored (pass None)."""
-    dt = _dtype_of(shape)
+    dt, n = _dtype_of(shape), _n(shape)
+    f, d, E = n["f"], n["d"], n["E"]
     _check(lib().moe_expert_ffn_pairs(
-        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(sorted_pairs, "sorted_pairs", torch.int32),
-        _ptr(row_token, "row_token", torch.int32),
-        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", dt),
-        _ptr(b1, "b1", dt), _ptr(w2, "w2", dt), _ptr(b2, "b2", dt),
-        _ptr(topk_weights, "topk_weights", torch.float32), int(bool(gated)),
-        _ptr(pair_rows, "pair_rows", dt), _ptr(ws, "ws", torch.uint8), ws.numel(),
-        _stream(stream)), "moe_expert_ffn_pairs")
+        ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+        _ptr(sorted_pairs, "sorted_pairs", torch.int32, numel=n["Tk"]),
+        _ptr(row_token, "row_token", torch.int32, numel=n["Tk"]),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, numel=n["E1"]),
+        _ptr(w1, "w1", dt, numel=_w(shape, 2 * f if gated else f, d)),
+        _ptr(b1, "b1", dt, numel=E * f), _ptr(w2, "w2", dt, numel=_w(shape, d, f)),
+        _ptr(b2, "b2", dt, numel=E * d),
+        _ptr(topk_weights, "topk_weights", torch.float32, numel=n["Tk"]), int(bool(gated)),
+        _ptr(pair_rows, "pair_rows", dt, numel=n["Tk"] * d), _ptr(ws, "ws", torch.uint8),
+        ws.numel(), _stream(stream)), "moe_expert_ffn_pairs")
 
 
 def moe_sum(shape, x, topk_ids, pair_rows, out, stream=None):
     """out[t] = (x[t] +) the sum of pair rows t*k .. t*k + k - 1; x and topk_ids may be None."""
-    dt = _dtype_of(shape)
-    _check(lib().moe_sum(ctypes.byref(shape), _ptr(x, "x", dt),
-                         _ptr(topk_ids, "topk_ids", torch.int32),
-                         _ptr(pair_rows, "pair_rows", dt), _ptr(out, "out", dt),
-                         _stream(stream)), "moe_sum")
+    dt, n = _dtype_of(shape), _n(shape)
+    _check(lib().moe_sum(ctypes.byref(shape), _ptr(x, "x", dt, numel=n["x"]),
+                         _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+                         _ptr(pair_rows, "pair_rows", dt, numel=n["Tk"] * n["d"]),
+                         _ptr(out, "out", dt, numel=n["x"]), _stream(stream)), "moe_sum")
+
+
+def _dropless_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                   expert_counts, pair_rows, ws, gated):
+    dt, n = _dtype_of(shape), _n(shape)
+    f, d, E = n["f"], n["d"], n["E"]
+    return [_ptr(x, "x", dt, numel=n["x"]), _ptr(w_router, "w_router", dt, numel=n["wr"]),
+            _ptr(b_router, "b_router", torch.float32, numel=E),
+            _ptr(w1, "w1", dt, numel=_w(shape, 2 * f if gated else f, d)),
+            _ptr(b1, "b1", dt, numel=E * f), _ptr(w2, "w2", dt, numel=_w(shape, d, f)),
+            _ptr(b2, "b2", dt, numel=E * d), _ptr(out, "out", dt, numel=n["x"]),
+            _ptr(topk_ids, "topk_ids", torch.int32, numel=n["Tk"]),
+            _ptr(topk_gates, "topk_gates", torch.float32, numel=n["Tk"]),
+            _ptr(expert_counts, "expert_counts", torch.int32, numel=E),
+            _ptr(pair_rows, "pair_rows", dt, numel=n["Tk"] * d), _ptr(ws, "ws", torch.uint8),
+            ws.numel()]
 
 
 def moe_layer_forward_dropless(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
@@ -351,29 +411,21 @@ def moe_layer_forward_dropless(shape, x, w_router, b_router, w1, b1, w2, b2, out
                                events=None, stream=None):
     """Dropless pair-order layer; `pair_rows` [T * k, d_model] optional; `events` None or 6
     recorded torch.cuda.Event(enable_timing=True)."""
-    dt = _dtype_of(shape)
-    _check(lib().moe_layer_forward_dropless(
-        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
-        _ptr(b_router, "b_router", torch.float32), _ptr(w1, "w1", dt), _ptr(b1, "b1", dt),
-        _ptr(w2, "w2", dt), _ptr(b2, "b2", dt), _ptr(out, "out", dt),
-        _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_gates, "topk_gates", torch.float32),
-        _ptr(expert_counts, "expert_counts", torch.int32), _ptr(pair_rows, "pair_rows", dt),
-        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), _events(events)),
-        "moe_layer_forward_dropless")
+    a = _dropless_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                       expert_counts, pair_rows, ws, False)
+    _check(lib().moe_layer_forward_dropless(ctypes.byref(shape), *a, _stream(stream),
+                                            _events(events)), "moe_layer_forward_dropless")
 
 
 def moe_layer_forward_dropless_gated(shape, x, w_router, b_router, w13, w2, out, topk_ids=None,
                                      topk_gates=None, expert_counts=None, pair_rows=None,
                                      ws=None, events=None, stream=None):
-    dt = _dtype_of(shape)
-    _check(lib().moe_layer_forward_dropless_gated(
-        ctypes.byref(shape), _ptr(x, "x", dt), _ptr(w_router, "w_router", dt),
-        _ptr(b_router, "b_router", torch.float32), _ptr(w13, "w13", dt), _ptr(w2, "w2", dt),
-        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
-        _ptr(topk_gates, "topk_gates", torch.float32),
-        _ptr(expert_counts, "expert_counts", torch.int32), _ptr(pair_rows, "pair_rows", dt),
-        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), _events(events)),
-        "moe_layer_forward_dropless_gated")
+    a = _dropless_args(shape, x, w_router, b_router, w13, None, w2, None, out, topk_ids,
+                       topk_gates, expert_counts, pair_rows, ws, True)
+    # no biases: x, w_router, b_router, w13, w2, out, ...
+    _check(lib().moe_layer_forward_dropless_gated(ctypes.byref(shape), *a[:4], a[5], *a[7:],
+                                                  _stream(stream), _events(events)),
+           "moe_layer_forward_dropless_gated")
 
 
 def workspace_bytes_batches(batch_shape: MoeShape, n_batches: int) -> int:
@@ -382,11 +434,14 @@ def workspace_bytes_batches(batch_shape: MoeShape, n_batches: int) -> int:
 
 def moe_schedule_batches(batch_shape, n_batches, topk_ids, order, batch_experts=None,
                          orig_batch_experts=None, stream=None):
+    Tp = int(batch_shape.T) * int(n_batches)
     _check(lib().moe_schedule_batches(
-        ctypes.byref(batch_shape), int(n_batches), _ptr(topk_ids, "topk_ids", torch.int32),
-        _ptr(order, "order", torch.int32), _ptr(batch_experts, "batch_experts", torch.int32),
-        _ptr(orig_batch_experts, "orig_batch_experts", torch.int32), _stream(stream)),
-        "moe_schedule_batches")
+        ctypes.byref(batch_shape), int(n_batches),
+        _ptr(topk_ids, "topk_ids", torch.int32, numel=Tp * int(batch_shape.top_k)),
+        _ptr(order, "order", torch.int32, numel=Tp),
+        _ptr(batch_experts, "batch_experts", torch.int32, numel=int(n_batches)),
+        _ptr(orig_batch_experts, "orig_batch_experts", torch.int32, numel=int(n_batches)),
+        _stream(stream)), "moe_schedule_batches")
 
 
 def moe_layer_forward_batches(batch_shape, n_batches, consolidate, x, w_router, b_router, w1, b1,
@@ -395,14 +450,21 @@ def moe_layer_forward_batches(batch_shape, n_batches, consolidate, x, w_router, 
     """A pool of n_batches batches of batch_shape.T tokens, one batch after another, regrouped
     by the Token Scheduler when `consolidate`; `events` None or 5 recorded
     torch.cuda.Event(enable_timing=True)."""
-    dt = _dtype_of(batch_shape)
+    dt, n = _dtype_of(batch_shape), _n(batch_shape)
+    M = int(n_batches)
+    Tp = n["T"] * M
+    f, d, E = n["f"], n["d"], n["E"]
     _check(lib().moe_layer_forward_batches(
-        ctypes.byref(batch_shape), int(n_batches), int(bool(consolidate)), _ptr(x, "x", dt),
-        _ptr(w_router, "w_router", dt), _ptr(b_router, "b_router", torch.float32),
-        _ptr(w1, "w1", dt), _ptr(b1, "b1", dt), _ptr(w2, "w2", dt), _ptr(b2, "b2", dt),
-        _ptr(out, "out", dt), _ptr(topk_ids, "topk_ids", torch.int32),
-        _ptr(topk_gates, "topk_gates", torch.float32), _ptr(order, "order", torch.int32),
-        _ptr(batch_experts, "batch_experts", torch.int32), _ptr(ws, "ws", torch.uint8),
+        ctypes.byref(batch_shape), M, int(bool(consolidate)), _ptr(x, "x", dt, numel=Tp * d),
+        _ptr(w_router, "w_router", dt, numel=n["wr"]),
+        _ptr(b_router, "b_router", torch.float32, numel=E),
+        _ptr(w1, "w1", dt, numel=_w(batch_shape, f, d)), _ptr(b1, "b1", dt, numel=E * f),
+        _ptr(w2, "w2", dt, numel=_w(batch_shape, d, f)), _ptr(b2, "b2", dt, numel=E * d),
+        _ptr(out, "out", dt, numel=Tp * d),
+        _ptr(topk_ids, "topk_ids", torch.int32, numel=Tp * n["k"]),
+        _ptr(topk_gates, "topk_gates", torch.float32, numel=Tp * n["k"]),
+        _ptr(order, "order", torch.int32, numel=Tp),
+        _ptr(batch_experts, "batch_experts", torch.int32, numel=M), _ptr(ws, "ws", torch.uint8),
         ws.numel(), _stream(stream), _events(events, 5)), "moe_layer_forward_batches")
 
 

@@ -83,7 +83,7 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "d_model = %d, d_ff = %d must be >= 1", s->d_model, s->d_ff);
   if (s->n_experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d < 1", s->n_experts);
   if (s->n_experts > 256)
-    return fail(MOE_ERR_UNSUPPORTED, "n_experts = %d > 256", s->n_experts);
+    return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d > 256", s->n_experts);
   if (s->top_k < 1 || s->top_k > s->n_experts)
     return fail(MOE_ERR_INVALID_ARGUMENT, "top_k = %d not in [1, n_experts = %d]", s->top_k,
                 s->n_experts);
@@ -664,8 +664,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
 
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const float* topk_gates,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_of,
-                        int32_t* row_token, uint8_t* drop_mask, void* ws, size_t ws_bytes,
-                        moe_stream_t stream) {
+                        int32_t* row_token, uint8_t* drop_mask, const void* x, void* x_routed,
+                        void* ws, size_t ws_bytes, moe_stream_t stream) {
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   if (s.T == 0) return MOE_OK;  // empty batch: nothing to check or enqueue
@@ -676,9 +676,27 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const f
   MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
   if (max_rows(s) > 0) MOE_TRY(check_ptr(row_token, 4, "row_token"));
   MOE_TRY(check_ptr(drop_mask, 1, "drop_mask"));
+  if (!x != !x_routed)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x and x_routed: both or neither NULL");
+  const bool gather = x && max_rows(s) > 0;
+  if (gather) {
+    MOE_TRY(check_data_ptr(s, x, "x"));
+    MOE_TRY(check_data_ptr(s, x_routed, "x_routed"));
+    const size_t row = (size_t)s.d_model * elem_bytes(s);
+    const char* a = static_cast<const char*>(x);
+    const char* b = static_cast<const char*>(x_routed);
+    if (a < b + (size_t)max_rows(s) * row && b < a + (size_t)s.T * row)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "x_routed overlaps x");
+  }
   MOE_TRY(check_ws(s, ws, ws_bytes));
-  return do_dispatch(s, topk_ids, topk_gates, expert_counts, expert_offsets, slot_of, row_token,
-                     drop_mask, ws, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY(do_dispatch(s, topk_ids, topk_gates, expert_counts, expert_offsets, slot_of, row_token,
+                      drop_mask, ws, st));
+  if (gather) {
+    hipError_t err = launch_gather_rows(s, x, row_token, expert_offsets, x_routed, st);
+    if (err != hipSuccess) return device_error(err, "routed rows");
+  }
+  return MOE_OK;
 }
 
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* row_token,

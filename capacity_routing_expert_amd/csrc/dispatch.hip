@@ -461,6 +461,63 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
   }
 }
 
+// ---------------------------------------------------------------- routed token rows
+// x_routed[s] = x[row_token[s]] for every kept slot s < offsets[E]: the token rows copied into
+// expert-slot order, the rows the first expert GEMM reads (fused-MoE flow diagram, GEMM 1 box:
+// the reorder happens on the way into the expert GEMMs).  HBM-bound copy: one wave per slot
+// row, 16-byte chunks (row_bytes a multiple of 16 and both bases 16-byte aligned) or 4-byte
+// words, every load of a batch issued before its stores.  The grid covers an upper bound on the
+// kept rows; waves past offsets[E] return.
+__global__ __launch_bounds__(256) void k_gather_rows(const char* __restrict__ x,
+                                                     const int32_t* __restrict__ row_token,
+                                                     const int32_t* __restrict__ offsets, int E,
+                                                     int row_bytes, bool vec16,
+                                                     char* __restrict__ out) {
+  constexpr int kB = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (s >= offsets[E]) return;
+  const int64_t t = row_token[s];
+  const char* src = x + t * row_bytes;
+  char* dst = out + s * row_bytes;
+  if (vec16) {
+    const int nch = row_bytes / 16;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)row_bytes);
+    for (int c0 = lane; c0 < nch; c0 += 64 * kB) {
+      uint4 v[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) v[b] = buffer_load16(r, (uint32_t)(c0 + 64 * b) * 16u);
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (c0 + 64 * b < nch) reinterpret_cast<uint4*>(dst)[c0 + 64 * b] = v[b];
+    }
+  } else {
+    const int nw = row_bytes / 4;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)row_bytes);
+    for (int c0 = lane; c0 < nw; c0 += 64 * kB) {
+      uint32_t v[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        v[b] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)((c0 + 64 * b) * 4), 0, 0);
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (c0 + 64 * b < nw) reinterpret_cast<uint32_t*>(dst)[c0 + 64 * b] = v[b];
+    }
+  }
+}
+
+hipError_t launch_gather_rows(const moe_shape& s, const void* x, const int32_t* row_token,
+                              const int32_t* offsets, void* x_routed, hipStream_t st) {
+  const int64_t rows_ub = max_rows(s);
+  if (rows_ub <= 0) return hipSuccess;
+  const int row_bytes = s.d_model * (s.dtype == MOE_BF16 ? 2 : 4);
+  const bool vec16 = row_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x_routed % 16 == 0;
+  hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)((rows_ub + 3) / 4)), dim3(256), 0, st,
+                     (const char*)x, row_token, offsets, s.n_experts, row_bytes, vec16,
+                     (char*)x_routed);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- padded fixed buffers
 // "Some Tokens Do Not Get In", "Why there is a buffer": each expert owns a buffer of `cap`
 // slots whether or not it fills them, and the unused slots are computed anyway.  From the

@@ -111,6 +111,11 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
                            int32_t* row_token, uint8_t* drop, int32_t* seg_start,
                            int32_t* blk_hist, uint64_t* keys, int32_t* rank, hipStream_t st);
 
+// x_routed[s] = x[row_token[s]] for the kept slots s < offsets[E] (rows of d_model elements of
+// the shape's dtype); the grid covers max_rows(s) slots
+hipError_t launch_gather_rows(const moe_shape& s, const void* x, const int32_t* row_token,
+                              const int32_t* offsets, void* x_routed, hipStream_t st);
+
 // Kernel timing for the expert GEMMs: arm_gemm_events(start, stop) makes the next expert-GEMM
 // launch on this thread record its own start and stop in the two events (hipExtLaunchKernel,
 // no marker between launches); take_gemm_events hands them to that launch and disarms.

@@ -144,19 +144,24 @@ def route(dev: dict, top_k: int, capacity: int, ws=None, want_logits=False) -> d
     return {"ids": ids, "gates": gates, "logits": logits}
 
 
-def dispatch(shape: B.MoeShape, ids: torch.Tensor, gates: torch.Tensor, ws=None) -> dict:
+def dispatch(shape: B.MoeShape, ids: torch.Tensor, gates: torch.Tensor, ws=None,
+             x: torch.Tensor | None = None) -> dict:
+    """moe_dispatch; with `x`, also the token rows in slot order (`x_routed`)."""
     device = ids.device
     T, k, E = shape.T, shape.top_k, shape.n_experts
     ws = workspace(shape, device) if ws is None else ws
+    rows = max(B.max_kept_rows(shape), 0)
     res = {
         "counts": torch.empty((E,), dtype=torch.int32, device=device),
         "offsets": torch.empty((E + 1,), dtype=torch.int32, device=device),
         "slot_of": torch.empty((T, k), dtype=torch.int32, device=device),
-        "row_token": torch.empty((max(B.max_kept_rows(shape), 0),), dtype=torch.int32, device=device),
+        "row_token": torch.empty((rows,), dtype=torch.int32, device=device),
         "drop_mask": torch.empty((T, k), dtype=torch.uint8, device=device),
     }
+    if x is not None:
+        res["x_routed"] = torch.empty((rows, shape.d_model), dtype=x.dtype, device=device)
     B.moe_dispatch(shape, ids, gates, res["counts"], res["offsets"], res["slot_of"],
-                   res["row_token"], res["drop_mask"], ws)
+                   res["row_token"], res["drop_mask"], ws, x=x, x_routed=res.get("x_routed"))
     return res
 
 

@@ -32,8 +32,9 @@
  *   - Layouts: W_r [E, d_model]; W1 [E, d_ff, d_model]; b1 [E, d_ff]; W2 [E, d_model, d_ff];
  *     b2 [E, d_model]; x and out [T, d_model]; per-assignment arrays [T, top_k], with
  *     choice 0 the largest gate.  Biases have the weight dtype; the router bias is fp32.
- *   - Limits: 1 <= top_k <= n_experts <= 256; capacity >= 0; T * top_k < 2^31;
- *     bf16 needs d_model and d_ff multiples of 8; x must be smaller than 2 GiB.
+ *   - Limits: 1 <= top_k <= n_experts <= 256 (MOE_ERR_INVALID_ARGUMENT otherwise: the slot
+ *     keys pack the expert id in 8 bits); capacity >= 0; T * top_k < 2^31; bf16 needs d_model
+ *     and d_ff multiples of 8; x must be smaller than 2 GiB (MOE_ERR_UNSUPPORTED otherwise).
  *   - shape->weight_layout says how w1 (w13) and w2 are stored (row-major as above, or packed
  *     by moe_pack_weights); every call that reads them honours it.
  */
@@ -52,8 +53,10 @@ typedef struct ihipEvent_t* moe_event_t;   /* hipEvent_t  */
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad sizes, k > E, capacity < 0 */
-  MOE_ERR_UNSUPPORTED = 2,      /* misaligned pointer, d not a multiple of 8 for bf16, E > 256 */
+  MOE_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad sizes, k > E, E > 256,
+                                   capacity < 0 */
+  MOE_ERR_UNSUPPORTED = 2,      /* misaligned pointer, d not a multiple of 8 for bf16, 32-bit
+                                   size limits */
   MOE_ERR_WORKSPACE = 3,        /* ws_bytes < moe_workspace_bytes(shape) */
   MOE_ERR_DEVICE = 4            /* a HIP call failed; moe_last_error() has its text */
 } moe_status;
@@ -137,11 +140,16 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
  *   slot_of        [T, k] int32 out: slot of the assignment, or -1 if dropped
  *   row_token      [moe_max_kept_rows] int32 out: token of each slot (first N_kept valid)
  *   drop_mask      [T, k] uint8 out: 1 if dropped
+ *   x              [T, d_model] dtype in, or NULL
+ *   x_routed       [moe_max_kept_rows, d_model] dtype out, or NULL: row s = x[row_token[s]] for
+ *                  s < N_kept (the token rows in slot order, as the first expert GEMM reads
+ *                  them: fused-MoE flow diagram, GEMM 1 box); rows past N_kept unspecified.
+ *                  x and x_routed are given together or both NULL; they must not overlap.
  * Within an expert, slot off[e] + r holds the assignment of rank r in the fill order. */
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_ids, const float* topk_gates,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_of,
-                        int32_t* row_token, uint8_t* drop_mask, void* ws, size_t ws_bytes,
-                        moe_stream_t stream);
+                        int32_t* row_token, uint8_t* drop_mask, const void* x, void* x_routed,
+                        void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Step 3, expert FFN over the routed rows.  Worked Example, trace of token 0: h = W1 x + b1,
  * a = SiLU(h), y = W2 a + b2.  Fused-MoE flow diagram (moe-vllm flow), GEMM 1 box: the first

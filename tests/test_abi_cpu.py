@@ -60,7 +60,7 @@ def test_workspace_and_max_rows(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("top_k", 0, 1), ("top_k", 9, 1), ("n_experts", 0, 1), ("n_experts", 300, 2),
+    ("top_k", 0, 1), ("top_k", 9, 1), ("n_experts", 0, 1), ("n_experts", 300, 1),
     ("capacity", -1, 1), ("T", -5, 1), ("d_model", 12, 2), ("dtype", 7, 2),
     # 32-bit limits: T * top_k assignments, bytes of x, tile offsets into d_ff rows
     ("T", 1 << 30, 2), ("T", 1 << 24, 2), ("d_ff", 1 << 22, 2),
@@ -124,3 +124,82 @@ def test_gemm_timing_arm_checks_on_the_host(lib):
     for ok in ((1, 2, 3, 4), (1, 2, 0, 0), (0, 0, 3, 4)):
         assert lib.moe_set_gemm_timing((ctypes.c_void_p * 4)(*ok)) == 0
     assert lib.moe_set_gemm_timing(None) == 0  # disarmed before any layer call
+
+
+def test_dispatch_gather_argument_checks(lib):
+    """moe_dispatch takes x and x_routed together or not at all, and refuses overlapping ones,
+    before anything is launched."""
+    s = B.make_shape(16, 64, 64, 8, 2, 4, B.MOE_BF16)
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    args = [ctypes.byref(s), p, p, p, p, p, p, p]
+    assert lib.moe_dispatch(*args, p, None, ws, 1 << 30, None) == 1
+    assert "x_routed" in B.last_error()
+    assert lib.moe_dispatch(*args, None, p, ws, 1 << 30, None) == 1
+    # x [16, 64] bf16 = 2 KiB at 4096, x_routed [max_rows = 16 * 2 ... 32 rows] overlapping it
+    assert lib.moe_dispatch(*args, ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 1024), ws,
+                            1 << 30, None) == 1
+    assert "overlaps" in B.last_error()
+
+
+def _cpu(n, dtype):
+    import torch
+    return torch.zeros(n, dtype=dtype)
+
+
+ROUTE_ARGS = ["x", "w_router", "b_router", "topk_ids", "topk_gates", "logits"]
+
+
+@pytest.mark.parametrize("which", ROUTE_ARGS)
+def test_binding_refuses_undersized_route_tensors(lib, which):
+    """The binding checks every tensor's size against the shape before its pointer reaches the
+    library.  Only the tensor under test is passed (a CPU tensor: its size is checked before
+    its device), every other argument is None."""
+    import torch
+    T, d, E, k = 16, 64, 8, 2
+    s = B.make_shape(T, d, 64, E, k, 4, B.MOE_BF16)
+    need = {"x": (T * d, torch.bfloat16), "w_router": (E * d, torch.bfloat16),
+            "b_router": (E, torch.float32), "topk_ids": (T * k, torch.int32),
+            "topk_gates": (T * k, torch.float32), "logits": (T * E, torch.float32)}
+    n, dt = need[which]
+    for size, msg in ((n - 1, f"{which} holds {n - 1} elements, the shape needs {n}"),
+                      (n, "must be on the GPU")):
+        args = {a: None for a in ROUTE_ARGS}
+        args[which] = _cpu(size, dt)
+        with pytest.raises(ValueError, match=msg):
+            B.moe_route(s, *[args[a] for a in ROUTE_ARGS], _cpu(256, torch.uint8))
+
+
+LAYER_ARGS = ["x", "w_router", "b_router", "w1", "b1", "w2", "b2", "out"]
+
+
+@pytest.mark.parametrize("which", ["x", "w1", "b1", "w2", "b2", "out", "topk_ids",
+                                   "expert_counts", "slot_of"])
+def test_binding_refuses_undersized_layer_tensors(lib, which):
+    import torch
+    T, d, f, E, k = 16, 64, 96, 8, 2
+    s = B.make_shape(T, d, f, E, k, 4, B.MOE_BF16)
+    bf = torch.bfloat16
+    need = {"x": (T * d, bf), "w1": (E * f * d, bf), "b1": (E * f, bf), "w2": (E * d * f, bf),
+            "b2": (E * d, bf), "out": (T * d, bf), "topk_ids": (T * k, torch.int32),
+            "expert_counts": (E, torch.int32), "slot_of": (T * k, torch.int32)}
+    n, dt = need[which]
+    pos = {a: None for a in LAYER_ARGS}
+    kw = {"topk_ids": None, "expert_counts": None, "slot_of": None}
+    (pos if which in pos else kw)[which] = _cpu(n - 1, dt)
+    with pytest.raises(ValueError, match=f"{which} holds {n - 1} elements"):
+        B.moe_layer_forward(s, *[pos[a] for a in LAYER_ARGS], ws=_cpu(256, torch.uint8), **kw)
+
+
+def test_binding_packed_weight_sizes(lib):
+    """Packed weights need ceil(cols / 32) * 32 columns: a row-major-sized W2 is refused."""
+    import torch
+    T, d, f, E, k = 16, 72, 104, 4, 2  # W2's 104 columns pack into 4 blocks of 32
+    s = B.make_shape(T, d, f, E, k, 4, B.MOE_BF16, B.MOE_WEIGHTS_PACKED)
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="w2 holds"):
+        B.moe_expert_ffn(s, None, _cpu(0, torch.int32), None, None, None, _cpu(E * d * f, bf),
+                         None, _cpu(0, bf), _cpu(256, torch.uint8))
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        B.moe_expert_ffn(s, None, _cpu(0, torch.int32), None, None, None,
+                         _cpu(E * 4 * d * 32, bf), None, _cpu(0, bf), _cpu(256, torch.uint8))

@@ -91,7 +91,7 @@ def test_dropless_small_shapes(T, d, f, E, k, gated):
     res = L.layer_forward_dropless(dev, k, gated=gated)
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
     r = O.route(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], k)
-    P.compare_route(ids, gates, r)
+    P.compare_route(ids, gates, r, x=f64(inp["x"]), w=f64(inp["w_router"]), b=inp["b_router"])
     full = O.forward_dropless_with_routing(f64(inp["x"]), ids, gates, E, _expert(inp, gated))
     assert np.array_equal(P.to_np(res["counts"]), full["counts"])
     rows_err = P.max_abs_rel(P.to_np(res["pair_rows"]), full["pair_rows"])
@@ -168,8 +168,9 @@ def test_moe_sum_variants(dt):
 # --------------------------------------------------------------------------- full sizes
 @pytest.mark.parametrize("key", ["mid", "decode", "fine", "gated"])
 def test_dropless_config_end_to_end(key):
-    """The workloads run dropless at full size: routing and pair grouping exact, sampled pair
-    rows and token outputs against the oracle (every pair kept: no capacity)."""
+    """The workloads run dropless at full size: routing and pair grouping exact, then every
+    pair row and every token's output against the oracle's flow (no capacity: every pair
+    kept)."""
     inp = W.make_inputs(key)
     wl = inp["workload"]
     dt = inp["dtype"]
@@ -179,37 +180,22 @@ def test_dropless_config_end_to_end(key):
     res = L.layer_forward_dropless(dev, wl.top_k, gated=gated)
     torch.cuda.synchronize()
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
-    r = O.route(W.to_float64(inp["x"], dt), W.to_float64(inp["w_router"], dt), inp["b_router"],
-                wl.top_k)
-    P.compare_route(ids, gates, r)
+    x64, wr64 = W.to_float64(inp["x"], dt), W.to_float64(inp["w_router"], dt)
+    r = O.route(x64, wr64, inp["b_router"], wl.top_k)
+    info = P.compare_route(ids, gates, r, x=x64, w=wr64, b=inp["b_router"])
     ref = O.dispatch_pairs(ids, wl.n_experts)
     shape = L.shape_of(dev, wl.top_k, 0)
     compare_pairs(L.dispatch_pairs(shape, res["ids"]), ref, wl.n_experts)
     assert np.array_equal(P.to_np(res["counts"]), ref["counts"])
-    say(f"    pair grouping exact; largest expert {int(ref['counts'].max())} of "
-        f"{wl.T * wl.top_k} pairs")
-
-    rng = np.random.default_rng(5)
-    sample = np.unique(np.concatenate([rng.choice(wl.T, size=min(160, wl.T), replace=False),
-                                       [0, wl.T - 1]]))
-    expert = _expert(inp, gated)
-    x64 = W.to_float64(inp["x"][sample], dt)
-    k = wl.top_k
-    want_rows = np.zeros((len(sample) * k, wl.d_model))
-    e_of = ids[sample].reshape(-1)  # expert of sampled pair i * k + c
-    for e in np.unique(e_of):  # one oracle call per expert
-        sel = np.nonzero(e_of == e)[0]
-        w = gates[sample].reshape(-1)[sel].astype(np.float64)
-        want_rows[sel] = w[:, None] * expert(int(e), x64[sel // k])
-    want_out = x64.copy()
-    for c in range(k):
-        want_out += want_rows[c::k]
-    pidx = (sample[:, None] * wl.top_k + np.arange(wl.top_k)[None, :]).reshape(-1)
-    rows_err = P.max_abs_rel(P.to_np(res["pair_rows"][torch.as_tensor(pidx, device=DEV)]),
-                             want_rows)
-    out_err = P.max_abs_rel(P.to_np(res["out"][torch.as_tensor(sample, device=DEV)]), want_out)
-    say(f"    sampled pair rows max-abs-rel {rows_err:.3e}, out {out_err:.3e} over "
-        f"{len(sample)} tokens")
+    say(f"    route certified {info['certified']}; pair grouping exact; largest expert "
+        f"{int(ref['counts'].max())} of {wl.T * wl.top_k} pairs")
+    full = O.forward_dropless_with_routing(x64, ids, gates, wl.n_experts, _expert(inp, gated))
+    got_rows, got_out = P.to_np(res["pair_rows"]), P.to_np(res["out"])
+    rows_err = P.max_abs_rel(got_rows, full["pair_rows"])
+    out_err = P.max_abs_rel(got_out, full["out"])
+    say(f"    pair rows max-abs-rel {rows_err:.3e} (element-wise "
+        f"{P.elementwise_rel(got_rows, full['pair_rows']):.3e}), out {out_err:.3e} (element-wise "
+        f"{P.elementwise_rel(got_out, full['out']):.3e}) over all {wl.T} tokens")
     assert rows_err <= P.TOL[dt] and out_err <= P.TOL[dt]
     del dev, res
     torch.cuda.empty_cache()

@@ -61,65 +61,37 @@ def case(key):
     return _CACHE[key]
 
 
-def check_sampled_outputs(inp, out_gpu, ids, gates, dref, n_sample=192, seed=0):
-    """out[t] = x[t] + sum_c kept g * FFN_e(x[t]) on sampled tokens; all-dropped rows bitwise."""
+def route_inputs(inp):
+    """The router inputs in float64 (x, W_r, b_r), for the rounding bound of compare_route."""
     dt = inp["dtype"]
-    x = inp["x"]
-    T, k = ids.shape
-    slot_of = dref["slot_of"]
-    kept_any = np.any(slot_of >= 0, axis=1)
-    rng = np.random.Generator(np.random.PCG64(seed))
-    cand = np.nonzero(kept_any)[0]
-    sample = np.unique(np.concatenate([
-        rng.choice(cand, size=min(n_sample, len(cand)), replace=False) if len(cand) else np.zeros(0, int),
-        cand[:1], cand[-1:]]).astype(np.int64))
-    if len(sample):
-        slots = slot_of[sample][slot_of[sample] >= 0]
-        y = O.expert_ffn_slots(W.to_float64(x, dt), dref["row_token"], dref["offsets"],
-                               F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
-                               F64(inp["b2"], dt), slots=slots)
-        ymap = {int(s): y[i] for i, s in enumerate(slots)}
-        x64 = W.to_float64(x[sample], dt)
-        ref = x64.copy()
-        for i, t in enumerate(sample):
-            for c in range(k):
-                s = slot_of[t, c]
-                if s >= 0:
-                    ref[i] = ref[i] + float(gates[t, c]) * ymap[int(s)]
-        got = P.to_np(out_gpu[torch.as_tensor(sample, device=out_gpu.device)])
-        err = P.max_abs_rel(got, ref)
-        say(f"    sampled out max-abs-rel {err:.3e} over {len(sample)} tokens")
-        assert err <= P.TOL[dt], err
-    # tokens with every choice dropped: bit copy of x
-    dropped = np.nonzero(~kept_any)[0]
+    return dict(x=W.to_float64(inp["x"], dt), w=W.to_float64(inp["w_router"], dt),
+                b=inp["b_router"])
+
+
+def check_all_outputs(inp, res, y_rows, ids, gates, dref, tag):
+    """Every kept slot's expert output and every token's layer output against the oracle
+    (max-abs-rel within the dtype's tolerance; the element-wise diagnostic reported), and the
+    tokens with every choice dropped bit for bit equal to x."""
+    dt = inp["dtype"]
+    x64 = W.to_float64(inp["x"], dt)
+    n = dref["n_kept"]
+    Y = O.expert_ffn_slots(x64, dref["row_token"], dref["offsets"], F64(inp["w1"], dt),
+                           F64(inp["b1"], dt), F64(inp["w2"], dt), F64(inp["b2"], dt))
+    out_ref, all_dropped = O.combine(x64, gates, dref["slot_of"], Y)
+    y_got = P.to_np(y_rows[:n])
+    out_got = P.to_np(res["out"])
+    y_err, y_el = P.max_abs_rel(y_got, Y), P.elementwise_rel(y_got, Y)
+    o_err, o_el = P.max_abs_rel(out_got, out_ref), P.elementwise_rel(out_got, out_ref)
+    say(f"    {tag}: Y max-abs-rel {y_err:.3e} (element-wise {y_el:.3e}) over {n} rows; "
+        f"out max-abs-rel {o_err:.3e} (element-wise {o_el:.3e}) over {len(out_ref)} tokens")
+    assert y_err <= P.TOL[dt], y_err
+    assert o_err <= P.TOL[dt], o_err
+    dropped = np.nonzero(all_dropped)[0]
     if len(dropped):
-        xb = L.to_device(x, dt, DEV)
-        idx = torch.as_tensor(dropped, device=DEV)
-        assert np.array_equal(P.bits(out_gpu[idx]), P.bits(xb[idx])), "dropped rows differ from x"
+        idx = torch.as_tensor(dropped, device=res["out"].device)
+        xb = L.to_device(inp["x"], dt, res["out"].device)
+        assert np.array_equal(P.bits(res["out"][idx]), P.bits(xb[idx])), "dropped rows differ from x"
     return len(dropped)
-
-
-def check_sampled_y(inp, y_gpu, dref, seed=1):
-    dt = inp["dtype"]
-    off = dref["offsets"]
-    E = len(off) - 1
-    rng = np.random.Generator(np.random.PCG64(seed))
-    slots = []
-    for e in range(E):
-        a, b = int(off[e]), int(off[e + 1])
-        if b > a:
-            slots += [a, b - 1] + list(rng.integers(a, b, size=min(4, b - a)))
-            slots += [s for s in range(a + 255, b, 256)][:4]  # tile boundaries
-    slots = np.unique(np.asarray(slots, dtype=np.int64))
-    if len(slots) == 0:
-        return
-    ref = O.expert_ffn_slots(W.to_float64(inp["x"], dt), dref["row_token"], off,
-                             F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
-                             F64(inp["b2"], dt), slots=slots)
-    got = P.to_np(y_gpu[torch.as_tensor(slots, device=y_gpu.device)])
-    err = P.max_abs_rel(got, ref)
-    say(f"    sampled Y max-abs-rel {err:.3e} over {len(slots)} slots")
-    assert err <= P.TOL[dt], err
 
 
 # --------------------------------------------------------------------------- worked example
@@ -171,7 +143,8 @@ def test_worked_example_forced_end_to_end():
     dev = L.upload(inp, DEV)
     res = L.layer_forward(dev, 1, ref["cap"])
     assert list(P.to_np(res["ids"])[:, 0]) == g["assignment"]["ids"]
-    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), ref)
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), ref, x=f64(inp["x"]),
+                    w=f64(inp["w_router"]))
     P.compare_dispatch(res, ref)
     err = P.max_abs_rel(P.to_np(res["out"]), ref["out"])
     assert err <= P.TOL["f32"], err
@@ -188,7 +161,8 @@ def test_worked_example_config_end_to_end():
                      f64(inp["w2"]), f64(inp["b2"]), wl.top_k, wl.capacity_factor)
     dev = L.upload(inp, DEV)
     res = L.layer_forward(dev, wl.top_k, cap)
-    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full)
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full, x=f64(inp["x"]),
+                    w=f64(inp["w_router"]))
     P.compare_dispatch(res, full)
     assert P.max_abs_rel(P.to_np(res["out"]), full["out"]) <= P.TOL["f32"]
     dropped = np.nonzero(full["all_dropped"])[0]
@@ -199,6 +173,9 @@ def test_worked_example_config_end_to_end():
 # --------------------------------------------------------------------------- full-size configs
 @pytest.mark.parametrize("key", ["mid", "decode", "fine", "collapse"])
 def test_config_end_to_end(key):
+    """The workload at full size: routing and dispatch bit-exact against the oracle, then every
+    kept slot's expert output and every token's output against the oracle's float64 layer;
+    the staged calls return the layer's bits."""
     inp, ref, cap = case(key)
     wl = inp["workload"]
     say(f"[{key}] {wl.name} cap={cap}")
@@ -206,23 +183,24 @@ def test_config_end_to_end(key):
     res = L.layer_forward(dev, wl.top_k, cap)
     torch.cuda.synchronize()
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
-    info = P.compare_route(ids, gates, ref)
-    say(f"    route: {len(info['mismatched_tokens'])} tokens differ (certified ambiguous)")
+    info = P.compare_route(ids, gates, ref, **route_inputs(inp))
+    say(f"    route: {info['certified']} tokens differ (each certified by the rounding bound), "
+        f"max gate difference {info['max_gate_ulp']} fp32 ulp")
     dref = O.dispatch(ids, gates, wl.n_experts, cap)
     P.compare_dispatch(res, dref)
     say(f"    dispatch exact; kept {dref['n_kept']} of {wl.T * wl.top_k}")
-    n_dropped = check_sampled_outputs(inp, res["out"], ids, gates, dref)
-    say(f"    {n_dropped} tokens fully dropped, bitwise equal to x")
 
-    # staged calls: same kernels, bitwise-identical results, and Y rows against the oracle
+    # staged calls: same kernels, bitwise-identical results; their Y rows go to the oracle
     shape = L.shape_of(dev, wl.top_k, cap)
     st = L.dispatch(shape, res["ids"], res["gates"])
     P.compare_dispatch(st, dref)
     y = L.expert_ffn(shape, dev, st["row_token"], st["offsets"])
-    check_sampled_y(inp, y, dref)
     out2 = L.combine(shape, dev["x"], res["gates"], st["slot_of"], y)
     assert torch.equal(out2.view(torch.int16), res["out"].view(torch.int16))
-    del dev, res, st, y, out2
+    del out2, st
+    n_dropped = check_all_outputs(inp, res, y, ids, gates, dref, key)
+    say(f"    {n_dropped} tokens fully dropped, bitwise equal to x")
+    del dev, res, y
     torch.cuda.empty_cache()
 
 
@@ -278,7 +256,7 @@ def test_random_small_shapes(T, d, f, E, k, C, dt):
     dev = L.upload(inp, DEV)
     res = L.layer_forward(dev, k, full["cap"])
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
-    P.compare_route(ids, gates, full)
+    P.compare_route(ids, gates, full, x=f64(inp["x"]), w=f64(inp["w_router"]), b=inp["b_router"])
     dref = O.dispatch(ids, gates, E, full["cap"])
     P.compare_dispatch(res, dref)
     Y = O.expert_ffn_slots(f64(inp["x"]), dref["row_token"], dref["offsets"], f64(inp["w1"]),
@@ -302,7 +280,8 @@ def test_gate_ties(dt):
     assert n_tied > 100
     dev = L.upload(inp, DEV)
     res = L.layer_forward(dev, k, full["cap"])
-    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full)
+    P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), full, x=f64(inp["x"]),
+                    w=f64(inp["w_router"]))
     P.compare_dispatch(res, full)
     assert P.max_abs_rel(P.to_np(res["out"]), full["out"]) <= P.TOL[dt]
 
@@ -401,7 +380,7 @@ def test_padded_small_shapes(T, d, f, E, k, C, dt):
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
     full = O.forward(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], f64(inp["w1"]),
                      f64(inp["b1"]), f64(inp["w2"]), f64(inp["b2"]), k, C)
-    P.compare_route(ids, gates, full)
+    P.compare_route(ids, gates, full, x=f64(inp["x"]), w=f64(inp["w_router"]), b=inp["b_router"])
     pref = O.dispatch_padded(ids, gates, E, cap)
     assert np.array_equal(P.to_np(res["slot_of"]), pref["slot_of"])
     Y = O.expert_ffn_padded(f64(inp["x"]), pref["row_token"], E, cap, f64(inp["w1"]),
@@ -474,7 +453,7 @@ def test_gated_small_shapes(T, d, f, E, k, C):
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
     full = O.forward_gated(f64(inp["x"]), f64(inp["w_router"]), inp["b_router"], f64(inp["w1"]),
                            f64(inp["w2"]), k, C)
-    P.compare_route(ids, gates, full)
+    P.compare_route(ids, gates, full, x=f64(inp["x"]), w=f64(inp["w_router"]), b=inp["b_router"])
     dref = O.dispatch(ids, gates, E, cap)
     P.compare_dispatch(res, dref)
     Y = O.expert_ffn_slots_gated(f64(inp["x"]), dref["row_token"], dref["offsets"], f64(inp["w1"]),
@@ -486,34 +465,30 @@ def test_gated_small_shapes(T, d, f, E, k, C):
 
 
 def test_gated_config_end_to_end():
-    """The gated workload at full size: routing and dispatch exact, sampled outputs."""
+    """The gated workload at full size: routing and dispatch exact, every token's output
+    against the oracle's gated layer."""
     inp = W.make_inputs("gated")
     wl = inp["workload"]
     cap = O.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
     dt = inp["dtype"]
-    ref = O.route(W.to_float64(inp["x"], dt), W.to_float64(inp["w_router"], dt), inp["b_router"],
-                  wl.top_k)
+    ri = route_inputs(inp)
+    ref = O.route(ri["x"], ri["w"], inp["b_router"], wl.top_k)
     dev = L.upload(inp, DEV)
     res = L.layer_forward_gated(dev, wl.top_k, cap)
     ids, gates = P.to_np(res["ids"]), P.to_np(res["gates"])
-    P.compare_route(ids, gates, ref)
+    info = P.compare_route(ids, gates, ref, **ri)
     dref = O.dispatch(ids, gates, wl.n_experts, cap)
     P.compare_dispatch(res, dref)
-    rng = np.random.default_rng(7)
-    kept_any = np.nonzero(np.any(dref["slot_of"] >= 0, axis=1))[0]
-    sample = rng.choice(kept_any, size=min(128, len(kept_any)), replace=False)
-    x64 = W.to_float64(inp["x"][sample], dt)
-    want = x64.copy()
-    w13, w2 = F64(inp["w1"], dt), F64(inp["w2"], dt)
-    for i, t in enumerate(sample):
-        for c in range(wl.top_k):
-            if dref["slot_of"][t, c] >= 0:
-                e = int(ids[t, c])
-                want[i] += float(gates[t, c]) * O.expert_ffn_gated(x64[i:i + 1], w13[e], w2[e])[0]
-    got = P.to_np(res["out"][torch.as_tensor(sample, device=DEV)])
-    err = P.max_abs_rel(got, want)
-    say(f"[gated] sampled out max-abs-rel {err:.3e} over {len(sample)} tokens")
+    Y = O.expert_ffn_slots_gated(ri["x"], dref["row_token"], dref["offsets"], F64(inp["w1"], dt),
+                                 F64(inp["w2"], dt))
+    want, all_dropped = O.combine(ri["x"], gates, dref["slot_of"], Y)
+    got = P.to_np(res["out"])
+    err, el = P.max_abs_rel(got, want), P.elementwise_rel(got, want)
+    say(f"[gated] route certified {info['certified']}; out max-abs-rel {err:.3e} "
+        f"(element-wise {el:.3e}) over {wl.T} tokens")
     assert err <= P.TOL[dt]
+    for t in np.nonzero(all_dropped)[0]:
+        assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
     del dev, res
     torch.cuda.empty_cache()
 
@@ -555,3 +530,71 @@ def test_layer_forward_in_a_captured_graph(key):
         torch.cuda.synchronize()
     del g, dev, ws, out
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- staged router
+ROUTE_SHAPES = [
+    # T, d, E, k, dtype  (one expert tile; two tiles per pass; 4-wave blocks from 8192 tokens
+    # with several passes and a half-empty last tile)
+    (100, 136, 8, 2, "bf16"),
+    (300, 64, 40, 6, "bf16"),
+    (8192, 64, 40, 3, "bf16"),
+    (8200, 24, 70, 4, "f32"),
+    (65, 12, 5, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,dt", ROUTE_SHAPES)
+def test_route_staged_with_logits(T, d, E, k, dt):
+    """moe_route on its own, with the optional fp32 logits: ids and gates bit-exact (certified
+    rounding differences only), every logit the fp32 rounding of the oracle's float64 logit
+    (bias included), except where that float64 value lies within the summation-order bound of
+    an fp32 rounding midpoint."""
+    say(f"[route] T={T} d={d} E={E} k={k} {dt}")
+    inp = W.make_shape_inputs(T, d, 8, E, dt, seed=T + E, router_bias_std=1.0)
+    f64 = lambda a: W.to_float64(a, dt)
+    x64, w64 = f64(inp["x"]), f64(inp["w_router"])
+    ref = O.route(x64, w64, inp["b_router"], k)
+    dev = L.upload(inp, DEV)
+    res = L.route(dev, k, 0, want_logits=True)
+    info = P.compare_route(P.to_np(res["ids"]), P.to_np(res["gates"]), ref, x=x64, w=w64,
+                           b=inp["b_router"])
+    got = P.to_np(res["logits"])
+    want = ref["logits"]
+    diff = got != want.astype(np.float32)
+    if diff.any():
+        # each differing logit: adjacent fp32 values, the oracle's value within the bound of
+        # their midpoint (both sides sum the same exact products in different orders)
+        n = d + 1
+        gamma = n * P.U64 / (1 - n * P.U64)
+        A = np.abs(x64) @ np.abs(w64).T + np.abs(inp["b_router"])[None, :]
+        g, r = got[diff].astype(np.float32), want.astype(np.float32)[diff]
+        assert np.all(np.abs(g.view(np.int32).astype(np.int64) - r.view(np.int32).astype(np.int64)) == 1)
+        mid = (g.astype(np.float64) + r.astype(np.float64)) / 2
+        assert np.all(np.abs(want[diff] - mid) <= 2 * gamma * A[diff])
+    say(f"    {int(diff.sum())} logits differ (certified), {info['certified']} tokens' routing")
+
+
+@pytest.mark.parametrize("T,d,E,k,C,dt", [(700, 136, 8, 2, 1.0, "bf16"),
+                                          (3000, 264, 64, 6, 0.5, "bf16"),
+                                          (65, 13, 4, 2, 1.0, "f32"),
+                                          (1500, 20, 16, 3, 2.0, "f32")])
+def test_dispatch_gathers_routed_rows(T, d, E, k, C, dt):
+    """moe_dispatch with x: x_routed row s is x[row_token[s]] bit for bit for every kept slot
+    (16-byte rows and 4-byte-word rows); the dispatch outputs are those of the call without x."""
+    say(f"[x_routed] T={T} d={d} E={E} k={k} C={C} {dt}")
+    inp = W.make_shape_inputs(T, d, 8, E, dt, seed=2 * T + E, router_bias_std=1.0)
+    dev = L.upload(inp, DEV)
+    cap = O.capacity(T, k, E, C)
+    r = L.route(dev, k, cap)
+    shape = L.shape_of(dev, k, cap)
+    a = L.dispatch(shape, r["ids"], r["gates"])
+    b = L.dispatch(shape, r["ids"], r["gates"], x=dev["x"])
+    for name in ("counts", "offsets", "slot_of", "row_token", "drop_mask"):
+        n = int(a["offsets"][-1]) if name == "row_token" else None
+        assert torch.equal(a[name][:n], b[name][:n]), name
+    n = int(b["offsets"][-1].item())
+    want = dev["x"][b["row_token"][:n].long()]
+    assert np.array_equal(P.bits(b["x_routed"][:n]), P.bits(want))
+    dref = O.dispatch(P.to_np(r["ids"]), P.to_np(r["gates"]), E, cap)
+    assert np.array_equal(P.to_np(b["row_token"])[:n], dref["row_token"])
