@@ -31,7 +31,7 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_stat
            "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
            "moe_layer_forward_dropless_gated", "moe_workspace_bytes_batches",
            "moe_schedule_batches", "moe_layer_forward_batches", "moe_packed_weights_bytes",
-           "moe_pack_weights", "moe_set_gemm_timing")
+           "moe_pack_weights", "moe_set_gemm_timing", "moe_layer_forward_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [SP, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_layer_forward_profiled.argtypes = L.moe_layer_forward.argtypes + [P]
+        # moe_layer_forward's arguments without ws and ws_bytes
+        L.moe_layer_forward_noalloc.argtypes = [SP] + [P] * 13 + [P]
         L.moe_workspace_bytes_padded.argtypes = [SP]
         L.moe_workspace_bytes_padded.restype = SZ
         # shape, x, w_router, b_router, w1, b1, w2, b2, out, ids, gates, slot_of, drop, counts,
@@ -111,6 +113,7 @@ def lib() -> ctypes.CDLL:
         L.moe_set_gemm_timing.restype = I32
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                      "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_padded",
+                     "moe_layer_forward_noalloc",
                      "moe_layer_forward_gated", "moe_dispatch_pairs", "moe_expert_ffn_pairs",
                      "moe_sum", "moe_layer_forward_dropless", "moe_layer_forward_dropless_gated",
                      "moe_schedule_batches", "moe_layer_forward_batches"):
@@ -280,6 +283,20 @@ def moe_layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_id
     args = _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
                          slot_of, drop_mask, expert_counts, ws)
     _check(lib().moe_layer_forward(*args, _stream(stream)), "moe_layer_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_layer_forward_noalloc(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,
+                              topk_gates=None, slot_of=None, drop_mask=None, expert_counts=None,
+                              stream=None):
+    """moe_layer_forward with the library's fixed device scratch as its workspace (no
+    allocation anywhere in the call)."""
+    args = _forward_args(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                         slot_of, drop_mask, expert_counts, None)
+    _check(lib().moe_layer_forward_noalloc(*args[:-2], _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_profiled(shape, x, w_router, b_router, w1, b1, w2, b2, out, events,

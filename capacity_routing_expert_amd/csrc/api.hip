@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -561,6 +562,35 @@ moe_status layer_forward_batches(const moe_shape* batch_shape, int32_t n_batches
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free entry point
+// The workspace of moe_layer_forward_noalloc: a fixed array in device memory that the library
+// holds on every device it runs on until the process ends.  Host code never uses the array's
+// own name as an address (on the host that name is only a stand-in); it takes the per-device
+// address that hipGetSymbolAddress returns, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call on it).
+moe_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return device_error(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return device_error(err, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -757,6 +787,26 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
                        slot_of, drop_mask, expert_counts, ws, ws_bytes, (hipStream_t)stream,
                        nullptr);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                                     const float* b_router, const void* w1, const void* b1,
+                                     const void* w2, const void* b2, void* out,
+                                     int32_t* topk_ids, float* topk_gates, int32_t* slot_of,
+                                     uint8_t* drop_mask, int32_t* expert_counts,
+                                     moe_stream_t stream) {
+  MOE_TRY(check_shape(shape));
+  const size_t need = layout(*shape).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch; the fixed scratch holds %zu bytes "
+                "(use moe_layer_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (shape->T > 0) MOE_TRY(scratch_address(&ws));
+  return layer_forward(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids, topk_gates,
+                       slot_of, drop_mask, expert_counts, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
+                       (hipStream_t)stream, nullptr);
 }
 
 moe_status moe_set_gemm_timing(const moe_event_t* events) {

@@ -185,6 +185,28 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              int32_t* expert_counts, void* ws, size_t ws_bytes,
                              moe_stream_t stream);
 
+/* Bytes of the fixed device scratch that moe_layer_forward_noalloc uses as its workspace. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_layer_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per device, held from the first use on a device until the process ends; its
+ * address is looked up once per device (hipGetSymbolAddress).  The call makes no allocation
+ * (no hipMalloc, hipFree or allocating library routine) and needs nothing in the scratch to
+ * start at zero.  Same kernels and results as moe_layer_forward.
+ * Errors: as moe_layer_forward; MOE_ERR_WORKSPACE when moe_workspace_bytes(shape) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (decode-sized batches fit: T = 64, d_model 2048, d_ff 8192, top-2
+ * needs under 3 MiB).  Every call on one device shares that device's scratch: calls that
+ * overlap on a device (other streams or threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. */
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                                     const float* b_router, const void* w1, const void* b1,
+                                     const void* w2, const void* b2, void* out,
+                                     int32_t* topk_ids, float* topk_gates, int32_t* slot_of,
+                                     uint8_t* drop_mask, int32_t* expert_counts,
+                                     moe_stream_t stream);
+
 /* moe_layer_forward, also recording caller-created events on the stream at the stage
  * boundaries, so the cost of each stage can be read back (the pages ask for the routing
  * decision's own overhead to be watched):
