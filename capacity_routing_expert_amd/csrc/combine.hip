@@ -7,7 +7,8 @@
 // reaches the next layer exactly as it entered), so x + 0 never turns -0.0 into +0.0.
 //
 // HBM-bound stream: one wave per token row, 16-byte loads and streaming (nontemporal) stores;
-// the slot numbers and gates of the row are wave-uniform (scalar loads).
+// the row's x is requested first, then its slots and gates (one vector load of all choices),
+// then the kept rows of Y.
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,9 +51,41 @@ __device__ __forceinline__ void store_nt(uint4 v, uint4* p) {
 
 }  // namespace
 
+// The kept choices of row t, in choice order: lane c of each 64-choice chunk loads slot and gate
+// of choice c, so all of a row's choices arrive in one round trip; a ballot gives the kept ones.
+// Returns the number kept and the first two (slot, gate) pairs (all wave-uniform).
+__device__ __forceinline__ int kept_choices(const int32_t* __restrict__ slot_of,
+                                            const float* __restrict__ gates, int64_t t, int k,
+                                            int& s0, float& g0, int& s1, float& g1) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  s0 = s1 = 0;
+  g0 = g1 = 0.0f;
+  for (int c0 = 0; c0 < k; c0 += 64) {
+    const int m = min(64, k - c0);
+    const __amdgpu_buffer_rsrc_t sr = row_rsrc(slot_of + t * k + c0, (uint32_t)m * 4u);
+    const __amdgpu_buffer_rsrc_t gr = row_rsrc(gates + t * k + c0, (uint32_t)m * 4u);
+    const int sl = lane < m ? (int)__builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, 0, 0) : -1;
+    const float gl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, lane * 4, 0, 0));
+    uint64_t kept = __ballot(sl >= 0);
+    while (kept && n < 2) {
+      const int c = __builtin_amdgcn_readfirstlane(__ffsll((long long)kept) - 1);
+      const int sc = __builtin_amdgcn_readlane(sl, c);
+      const float gc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gl), c));
+      if (n == 0) { s0 = sc; g0 = gc; } else { s1 = sc; g1 = gc; }
+      ++n;
+      kept &= kept - 1;
+    }
+    n += __popcll(kept);
+  }
+  return n;
+}
+
 // One wave per token row; each lane takes 16-byte chunks lane, lane + 64, ... in batches of
-// kB.  The x chunks of a batch and the y chunks of the first two kept choices are loaded
-// together, so a row costs one memory round trip per batch (plus one per further kept choice).
+// kB.  The first batch of x is loaded before the row's slots are looked up (it depends on
+// nothing); the y chunks of the first two kept choices follow as soon as the slots are known,
+// so a row costs one memory round trip after the slot lookup per batch (plus one per further
+// kept choice).
 __global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__ x,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_of,
@@ -67,40 +100,34 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__
   if (t >= T) return;
   const int nch = d / 8;
   uint4* orow = reinterpret_cast<uint4*>(out + t * (int64_t)d);
-  // the first two kept choices (choice order) and the number kept; all wave-uniform
-  int n_kept = 0, s0 = 0, s1 = 0;
-  float g0 = 0.0f, g1 = 0.0f;
-  for (int c = 0; c < k; ++c) {
-    const int sc = slot_of[t * k + c];
-    if (sc < 0) continue;
-    if (n_kept == 0) {
-      s0 = sc;
-      g0 = gates[t * k + c];
-    } else if (n_kept == 1) {
-      s1 = sc;
-      g1 = gates[t * k + c];
-    }
-    ++n_kept;
-  }
   // rows as buffer ranges: chunks past the row, and the rows of absent choices, read as zeros
   const uint32_t row_bytes = (uint32_t)d * 2u;
   const __amdgpu_buffer_rsrc_t xb = row_rsrc(x + t * (int64_t)d, row_bytes);
+  uint4 xv[kB];
+#pragma unroll
+  for (int b = 0; b < kB; ++b) xv[b] = load16(xb, lane + 64 * b);
+  int s0, s1;
+  float g0, g1;
+  const int n_kept = kept_choices(slot_of, gates, t, k, s0, g0, s1, g1);
   const __amdgpu_buffer_rsrc_t y0 = row_rsrc(y + (int64_t)s0 * d, n_kept >= 1 ? row_bytes : 0u);
   const __amdgpu_buffer_rsrc_t y1 = row_rsrc(y + (int64_t)s1 * d, n_kept >= 2 ? row_bytes : 0u);
 
   for (int base = lane; base < nch; base += 64 * kB) {
-    uint4 xv[kB], v0[kB], v1[kB];
+    if (base != lane) {
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      xv[b] = load16(xb, base + 64 * b);
-      v0[b] = load16(y0, base + 64 * b);
-      v1[b] = load16(y1, base + 64 * b);
+      for (int b = 0; b < kB; ++b) xv[b] = load16(xb, base + 64 * b);
     }
     if (n_kept == 0) {  // every choice dropped: the row leaves bit for bit
 #pragma unroll
       for (int b = 0; b < kB; ++b)
         if (base + 64 * b < nch) store_nt(xv[b], orow + base + 64 * b);
       continue;
+    }
+    uint4 v0[kB], v1[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      v0[b] = load16(y0, base + 64 * b);
+      v1[b] = load16(y1, base + 64 * b);
     }
     float acc[kB][8];
 #pragma unroll
