@@ -269,6 +269,10 @@ def main():
                          "cols]; the results are bit-identical")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time K steps each preceded by a 512 MiB write on the stream (the "
+                         "Infinity Cache and the L2s hold none of the step's data), reporting the "
+                         "median and mean per-step time beside the steady-state value")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
@@ -460,6 +464,36 @@ def main():
     combine_bytes = ((2 * wl.T + n_kept) * dm * inp["x"].itemsize
                      + (4 if dropless else 8) * wl.T * wl.top_k)
 
+    flush_res = None
+    if args.flush:
+        # cold-cache steps: a 512 MiB write (twice the 256 MiB Infinity Cache) before each one;
+        # events bracket the step alone, so the flush is not counted
+        fbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fev = [new_events(2) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            fbuf.fill_(i & 0xFF)
+            fev[i][0].record(stream)
+            step()
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([e[0].elapsed_time(e[1]) for e in fev])
+        flush_res = {"median_ms": float(np.median(per)), "mean_ms": float(np.mean(per)),
+                     "min_ms": float(per.min()), "max_ms": float(per.max()),
+                     "tokens_per_s_median": wl.T / (float(np.median(per)) / 1e3),
+                     "steady_state_median_ms": None,
+                     "flush_bytes": 512 << 20}
+        del fbuf
+        # the same per-step event timing without the flush, for a like-for-like median
+        sev = [new_events(2) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            sev[i][0].record(stream)
+            step()
+            sev[i][1].record(stream)
+        torch.cuda.synchronize()
+        flush_res["steady_state_median_ms"] = float(np.median([e[0].elapsed_time(e[1]) for e in sev]))
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -488,6 +522,7 @@ def main():
         "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
                                          / PEAK_BF16_TFLOPS,
         "roofline": dict(roof, traffic=traffic),
+        "flush": flush_res,
         "dominant_kernel_ms": dom_ms,
         "dominant_kernel_timing": "start and end of the dominant GEMM's kernel, recorded by its "
                                   "launch in each timed step (moe_set_gemm_timing, "

@@ -44,8 +44,9 @@
 //
 // Scheduling: the grid is an upper bound (the number of kept rows is only known on the
 // device).  Workgroups are dealt round-robin over the 8 XCDs, so block b runs on XCD b % 8;
-// blocks (b / 8) % 32 of round b / 256 on one XCD take one group of 8 token tiles x 4 weight
-// tiles, so the 32 blocks sharing an L2 share both operands' streams.  Each block finds the
+// blocks (b / 8) % 32 of round b / 256 on one XCD take one group of token tiles x weight tiles
+// (8 x 4, or 4 x 8 for the large up-projection), so the 32 blocks sharing an L2 share both
+// operands' streams.  Each block finds the
 // expert of its token tile from expert_offsets with a wave prefix scan and exits if its tile
 // does not exist.
 #include <hip/hip_ext.h>
@@ -78,8 +79,9 @@ constexpr int kOutSlots = 0;        // output row = slot (row0 + r)
 constexpr int kOutPairs = 1;        // output row = out_row[slot] (dropless pair order)
 constexpr int kOutPairsScaled = 2;  // ... and the row times row_scale[out_row[slot]]
 
-constexpr int kGroupM = 8;               // token tiles per XCD group
-constexpr int kGroupN = 32 / kGroupM;    // weight tiles per XCD group
+// XCD groups of 32 blocks: GM token tiles x (32 / GM) weight tiles (template parameter of the
+// kernels; 8 unless a launch says otherwise)
+constexpr int kGroupBlocks = 32;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset beyond every buffer range used
 
 // Buffer resource for raw (stride 0) loads of `bytes` bytes from `base`; reads past the range
@@ -165,17 +167,27 @@ struct TokenTiles {
 };
 
 // Block -> (token tile, weight tile) of a grid of MT x NT tiles: block b runs on XCD b % 8, and
-// the 32 blocks (b / 8) % 32 of round b / 256 on one XCD take one group of kGroupM token tiles x
-// kGroupN weight tiles.  False if the block has no tile.
+// the 32 blocks (b / 8) % 32 of round b / 256 on one XCD take one group of GM token tiles x
+// 32 / GM weight tiles.  False if the block has no tile.
+template <int GM>
 __device__ __forceinline__ bool tile_of_block(int MT, int NT, int& mt, int& nt) {
-  const int NQ = (NT + kGroupN - 1) / kGroupN;
-  const int NG = ((MT + kGroupM - 1) / kGroupM) * NQ;
+  constexpr int GN = kGroupBlocks / GM;
+  const int NQ = (NT + GN - 1) / GN;
+  const int NG = ((MT + GM - 1) / GM) * NQ;
   const int xcd = blockIdx.x & 7, slot = (blockIdx.x >> 3) & 31, round = blockIdx.x >> 8;
   const int g = round * 8 + xcd;
   if (g >= NG) return false;
-  mt = (g / NQ) * kGroupM + slot % kGroupM;
-  nt = (g % NQ) * kGroupN + slot / kGroupM;
+  mt = (g / NQ) * GM + slot % GM;
+  nt = (g % NQ) * GN + slot / GM;
   return mt < MT && nt < NT;
+}
+
+// Blocks to launch for MT_ub x NT tiles in groups of GM x (32 / GM): whole rounds of 256.
+template <int GM>
+int64_t group_grid(int64_t mt_ub, int64_t nt) {
+  constexpr int GN = kGroupBlocks / GM;
+  const int64_t ng_ub = (mt_ub + GM - 1) / GM * ((nt + GN - 1) / GN);
+  return (ng_ub + 7) / 8 * 256;
 }
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
@@ -479,7 +491,7 @@ __device__ __forceinline__ void gemm_tile(
 // expert_offsets (device memory: the kept-row counts are only known on the device), finds its
 // own (expert, token tile, feature tile) and exits if that tile does not exist.
 template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
-          int NWV = 4>
+          int NWV = 4, int GM = 8>
 __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
   const int NT = (N + TNO - 1) / TNO;
   const TokenTiles<TM> tt(offsets, E, lane);
   int mt, nt, e, row0, rows;
-  if (!tile_of_block(tt.MT, NT, mt, nt)) return;
+  if (!tile_of_block<GM>(tt.MT, NT, mt, nt)) return;
   tt.locate(offsets, lane, mt, e, row0, rows);
   gemm_tile<TN, TM, BK, NS, GATHER, ACT, OUT, WP, NWV>(
       A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
@@ -719,7 +731,7 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_loaders(
   const int NT = (N + TN - 1) / TN;
   const TokenTiles<TM> tt(offsets, E, lane);
   int mt, nt, e, row0, rows;
-  if (!tile_of_block(tt.MT, NT, mt, nt)) return;  // block-uniform
+  if (!tile_of_block<8>(tt.MT, NT, mt, nt)) return;  // block-uniform
   tt.locate(offsets, lane, mt, e, row0, rows);
   gemm_tile_loaders<TN, TM, NS, GATHER, ACT, OUT, WP>(A, row_token, W, bias, out, out_row, row_scale,
                                                  N, K, a_rows, e, row0, rows, nt * TN);
@@ -789,7 +801,7 @@ constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
 }
 
 template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
-          int NWV = 4>
+          int NWV = 4, int GM = 8>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st,
@@ -798,7 +810,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   if (rows_ub <= 0) return hipSuccess;
   constexpr size_t lds = tile_lds(TN, TM, BK, NS, OUT != kOutSlots);
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, GATHER, ACT, OUT, WP, NWV>;
+  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, GATHER, ACT, OUT, WP, NWV, GM>;
   static std::atomic<bool> lds_allowed[kMaxDevices];
   if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
       err != hipSuccess)
@@ -806,10 +818,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   // upper bound on groups: token tiles <= rows_ub / TM + E
   const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;
-  const int64_t nt = (N + TNO - 1) / TNO;
-  const int64_t nq = (nt + kGroupN - 1) / kGroupN;
-  const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
-  const int64_t grid = (ng_ub + 7) / 8 * 256;
+  const int64_t grid = group_grid<GM>(mt_ub, (N + TNO - 1) / TNO);
   hipEvent_t t0, t1;
   if (take_gemm_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, t0, t1, 0, A,
@@ -838,10 +847,7 @@ hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token
       err != hipSuccess)
     return err;
   const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;  // token tiles <= rows_ub / TM + E
-  const int64_t nt = (N + TN - 1) / TN;
-  const int64_t nq = (nt + kGroupN - 1) / kGroupN;
-  const int64_t ng_ub = (mt_ub + kGroupM - 1) / kGroupM * nq;
-  const int64_t grid = (ng_ub + 7) / 8 * 256;
+  const int64_t grid = group_grid<8>(mt_ub, (N + TN - 1) / TN);
   hipEvent_t t0, t1;
   if (take_gemm_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, t0, t1, 0, A,
@@ -899,12 +905,15 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
   }
   // Large batches.  The down-projection runs on loader waves (256 x 192 tiles); the
   // up-projection on 8-wave blocks of 256 x 256 tiles, two waves of 128 x 64 per SIMD, so one
-  // wave's MFMAs run while the other waits on a load (mid layer GEMM 1: 215 -> 195 us).
+  // wave's MFMAs run while the other waits on a load (mid layer GEMM 1: 215 -> 195 us).  The
+  // up-projection's XCD groups are 4 token tiles x 8 weight tiles: a token tile's 8 weight tiles
+  // then share its gathered rows in one L2 (64-expert fine layer GEMM 1: 395 -> 350 us, collapse
+  // 5.20 -> 5.01 ms, mid unchanged; the down-projection keeps 8 x 4).
   if constexpr (ACT == kActNone)
     return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   else
-    return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8>(
+    return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
 }
 
