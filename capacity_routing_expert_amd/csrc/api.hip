@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -165,8 +166,8 @@ Workspace layout(const moe_shape& s, LayoutKind kind) {
   Workspace w;
   const int64_t N = s.T * (int64_t)s.top_k;
   const int64_t E = s.n_experts;
-  const int64_t nb_a = dispatch_blocks(N), nb_p = dispatch_blocks(N, true);
-  const int64_t nb = nb_a > nb_p ? nb_a : nb_p;
+  const int64_t nb_a = dispatch_blocks(N), nb_p = dispatch_blocks(N, true), nb_r = dispatch_runs(N);
+  const int64_t nb = std::max(nb_a, std::max(nb_p, nb_r));
   const bool padded = kind == kLayoutPadded, dropless = kind == kLayoutDropless;
   const int64_t rows = padded ? E * s.capacity : dropless ? N : max_rows(s);
   size_t o = 0;
@@ -183,7 +184,7 @@ Workspace layout(const moe_shape& s, LayoutKind kind) {
   w.offsets = take((size_t)(E + 1) * 4);
   w.seg_start = take(dropless ? 0 : (size_t)(E + 2) * 4);
   w.blk_hist = take((size_t)nb * (E + 1) * 4);
-  w.keys = take(dropless ? 0 : (size_t)N * 8);
+  w.keys = take(dropless ? 0 : (size_t)N * 8);  // read in 16-byte pairs up to its 256-B end
   w.rank = take(dropless ? 0 : (size_t)N * 4);
   w.row_token = take((size_t)(dropless ? N : max_rows(s)) * 4);
   w.pairs = take(dropless ? (size_t)N * 4 : 0);

@@ -25,7 +25,9 @@
 //   k_dispatch_emit    slot_of / drop_mask / row_token from the ranks and the capacity.
 // Up to 1024 assignments a single workgroup does all of it instead (k_dispatch_small: one
 // bitonic sort of the (expert, fill order) keys, one per thread), which saves four dependent
-// launches.
+// launches.  Up to 16384 assignments two launches do it: runs of 512 keys sorted in LDS
+// (k_dispatch_runs), then every key ranked against all runs held in one workgroup's LDS and its
+// slot written (k_dispatch_merge).
 // Integer results only, no order-dependent reductions: the output is deterministic.
 #include "moe_internal.h"
 
@@ -56,6 +58,18 @@ __device__ __forceinline__ uint64_t sort_key(float g, uint32_t i) {
   if (u == 0x80000000u) u = 0u;
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)(~ord) << 32) | (uint64_t)i;
+}
+
+// (expert, fill order) key of assignment i < 2^24 with expert e in [0, E): ascending order is the
+// expert, then gate descending, then i ascending
+__device__ __forceinline__ uint64_t expert_key(int e, float g, uint32_t i) {
+  return ((uint64_t)e << 56) | ((sort_key(g, 0u) >> 32) << 24) | (uint64_t)i;
+}
+// key of an assignment i whose id lies outside [0, E): kInvalidKey | i sorts after every valid
+// key (~ord(gate) < 0xFFFFFFFF for any non-NaN gate), and padding (~0) after both
+constexpr uint64_t kInvalidKey = 0xFFFFFFFFFF000000ull;
+__device__ __forceinline__ bool key_is_valid(uint64_t key) {
+  return (key >> 24) != 0xFFFFFFFFFFull;
 }
 
 // Exclusive scan of n ints in LDS by one wave; each lane reads and rewrites only its own
@@ -237,6 +251,62 @@ __device__ void expert_prefix(const int32_t* __restrict__ counts, int E, int* s_
   __syncthreads();
 }
 
+// 32-bit DPP lane move within rows of 16 lanes (all rows and banks enabled)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
+}
+// The key of lane (lane ^ stride), stride < 64.  Strides 1 and 2 are quad permutations and 8 a
+// rotation by half a row, all DPP moves; stride 4 takes the rotations by 12 and by 4 (lane
+// i reads lane i + 4 or i - 4 of its row) and keeps the one that lands on the partner; 16 and 32
+// go through ds_bpermute.
+__device__ __forceinline__ uint64_t xor_partner(uint64_t v, int stride) {
+  switch (stride) {
+    case 1: return dpp64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    case 2: return dpp64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    case 4: {
+      const uint64_t up = dpp64<0x12C>(v), down = dpp64<0x124>(v);  // row_ror 12, row_ror 4
+      return (threadIdx.x & 4) ? down : up;
+    }
+    case 8: return dpp64<0x128>(v);  // row_ror 8
+    default: return __shfl_xor(v, stride, 64);
+  }
+}
+
+// Bitonic sort of n keys (n a power of two, at most NMAX and the workgroup size), one per
+// thread: returns the key that lands at this thread's index in ascending order within its
+// aligned group of n threads.  Partners closer than 64 are in the same wave (xor_partner),
+// farther ones trade keys through `sk` (one key per thread of LDS).  The network is unrolled
+// for NMAX keys and stops after the stage of size n.
+template <int NMAX>
+__device__ __forceinline__ uint64_t block_bitonic_sort(uint64_t v, uint64_t* sk, int n) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int size = 2; size <= NMAX; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (size > n) continue;  // workgroup-uniform
+      uint64_t other;
+      if (stride >= 64) {
+        sk[t] = v;
+        __syncthreads();
+        other = sk[t ^ stride];
+        __syncthreads();
+      } else {
+        other = xor_partner(v, stride);
+      }
+      const bool up = (t & size) == 0, lower = (t & stride) == 0;
+      // keep the smaller key at the lower index of an ascending pair, the larger otherwise
+      v = (lower == up) ? (v < other ? v : other) : (v < other ? other : v);
+    }
+  }
+  return v;
+}
+
 // the e with s_pre[e] <= w < s_pre[e+1] (s_pre non-decreasing, w < s_pre[E])
 __device__ __forceinline__ int find_expert(const int* s_pre, int E, int w) {
   int lo = 0, hi = E - 1;
@@ -265,24 +335,7 @@ __global__ __launch_bounds__(kTile) void k_dispatch_tilesort(uint64_t* __restric
   const int64_t base = (int64_t)seg_start[e] + (int64_t)a * kTile;
   const int t = threadIdx.x;
   uint64_t v = t < m ? keys[base + t] : ~0ull;  // padding sorts last
-  // bitonic network, one key per thread: partners closer than 64 are in the same wave and trade
-  // keys by shuffle, farther ones through LDS
-  for (int size = 2; size <= kTile; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t other;
-      if (stride >= 64) {
-        sk[t] = v;
-        __syncthreads();
-        other = sk[t ^ stride];
-        __syncthreads();
-      } else {
-        other = __shfl_xor(v, stride, 64);
-      }
-      const bool up = (t & size) == 0, lower = (t & stride) == 0;
-      // keep the smaller key at the lower index of an ascending pair, the larger otherwise
-      v = (lower == up) ? (v < other ? v : other) : (v < other ? other : v);
-    }
-  }
+  v = block_bitonic_sort<kTile>(v, sk, kTile);
   if (t < m) keys[base + t] = v;
 }
 
@@ -380,11 +433,11 @@ __global__ __launch_bounds__(256) void k_dispatch_emit(const uint64_t* __restric
 
 // ---------------------------------------------------------------- small batches
 // Up to kSmallN assignments: the whole dispatch in one workgroup.  Key of assignment i with
-// expert e: (e << 56) | (~ord(gate) << 24) | i (i < 2^24); ascending order is expert, then the
-// fill order of that expert.  Ids outside [0, E) get (0xFFFFFFFFFF << 24) | i, after every valid
-// key (~ord(gate) < 0xFFFFFFFF for any non-NaN gate).  The keys are unique, so the bitonic sort
-// in LDS has one result, the same order the bucketed multi-kernel path produces; the rank of a
-// key in its expert is its sorted position minus the expert's first position.
+// expert e: (e << 56) | (~ord(gate) << 24) | i (expert_key); ascending order is expert, then the
+// fill order of that expert.  Ids outside [0, E) get kInvalidKey | i, after every valid key.
+// The keys are unique, so the bitonic sort in LDS has one result, the same order the bucketed
+// multi-kernel path produces; the rank of a key in its expert is its sorted position minus the
+// expert's first position.
 constexpr int kSmallN = 1024;  // one key per thread of a 1024-thread workgroup
 
 __global__ __launch_bounds__(1024) void k_dispatch_small(
@@ -402,30 +455,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
   if (tid < N) {
     const int e = ids[tid];
     if (e >= 0 && e < E) {
-      const uint64_t g = sort_key(gates[tid], 0u) >> 32;  // ~ord(gate)
-      v = ((uint64_t)e << 56) | (g << 24) | (uint64_t)tid;
+      v = expert_key(e, gates[tid], (uint32_t)tid);
       atomicAdd(&cnt[e], 1);
     } else {
-      v = 0xFFFFFFFFFF000000ull | (uint64_t)tid;
+      v = kInvalidKey | (uint64_t)tid;
     }
   }
-  // bitonic sort over threads 0 .. P-1 (threads past P only meet each other): partners closer
-  // than 64 are in the same wave and trade keys by shuffle, farther ones through LDS
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int j = size >> 1; j > 0; j >>= 1) {
-      uint64_t other;
-      if (j >= 64) {
-        sk[tid] = v;
-        __syncthreads();
-        other = sk[tid ^ j];
-        __syncthreads();
-      } else {
-        other = __shfl_xor(v, j, 64);
-      }
-      const bool up = (tid & size) == 0, lower = (tid & j) == 0;
-      v = (lower == up) ? (v < other ? v : other) : (v < other ? other : v);
-    }
-  }
+  // bitonic sort over threads 0 .. P-1 (threads past P only meet each other)
+  v = block_bitonic_sort<kSmallN>(v, sk, P);
   sk[tid] = v;
   __syncthreads();
   // expert starts in sorted order and kept-slot offsets
@@ -447,7 +484,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
     const uint64_t key = sk[p];
     const int i = (int)(key & 0xFFFFFFull);
     const int e = (int)(key >> 56);
-    const bool valid = (key >> 24) != 0xFFFFFFFFFFull;
+    const bool valid = key_is_valid(key);
     const int r = p - start[e];
     if (valid && r < cap) {
       const int slot = koff[e] + r;
@@ -460,6 +497,187 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
     }
   }
 }
+
+// ---------------------------------------------------------------- mid-sized batches
+// kSmallN < N <= kMidN assignments: two launches.  The assignments are cut into runs of kRun
+// consecutive ones.  k_dispatch_runs sorts each run by the same (expert, fill order) keys as the
+// one-workgroup path and records where each expert's keys begin in the sorted run.
+// k_dispatch_merge: every workgroup loads all sorted runs into LDS and ranks kMergeKeys of the
+// keys.  The rank of a key within its expert is its position in its own run's segment of that
+// expert plus, for every other run, the number of that run's keys of the same expert that are
+// smaller: branch-free binary searches, four runs side by side so that four LDS reads are in
+// flight, kSplit threads per key that each take every kSplit-th run.  The searches are bound by LDS
+// throughput, hence few keys per workgroup and many workgroups.  The keys are unique, so these
+// ranks are the fill-order positions the other paths compute, and the kernel emits the slots
+// straight from them.
+constexpr int kRun = 512;
+constexpr int kMidN = 16384;
+constexpr int kMidRuns = kMidN / kRun;
+constexpr int kMergeKeys = 128;  // keys ranked per merge workgroup
+constexpr int kSplit = 4;        // threads per key
+constexpr int kMergeThreads = kSplit * kMergeKeys;
+// k_dispatch_merge's dynamic LDS: every key (a multiple of 2 * kMergeThreads of them, as the
+// keys arrive in pairs), then each run's expert starts as 16-bit values (room for the most runs
+// and experts, so that every thread stores its share without a guard)
+constexpr int merge_key_slots(int n) {
+  return (n + 2 * kMergeThreads - 1) / (2 * kMergeThreads) * (2 * kMergeThreads);
+}
+constexpr int kOffRounds = (kMidRuns * 257 + kMergeThreads - 1) / kMergeThreads;
+constexpr size_t merge_lds_bytes(int n) {
+  return (size_t)merge_key_slots(n) * 8 + (size_t)kOffRounds * kMergeThreads * 2;
+}
+
+__global__ __launch_bounds__(kRun) void k_dispatch_runs(const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ gates, int N,
+                                                        int E, uint64_t* __restrict__ keys,
+                                                        int32_t* __restrict__ run_off,
+                                                        int32_t* __restrict__ slot_of,
+                                                        uint8_t* __restrict__ drop) {
+  __shared__ uint64_t sk[kRun];
+  __shared__ int sex[kRun];
+  const int t = threadIdx.x;
+  const int base = blockIdx.x * kRun, i = base + t;
+  const uint32_t n_bytes = (uint32_t)min(kRun, N - base) * 4u;  // both loads issued at once
+  const int e = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ids + base, n_bytes),
+                                                          t * 4, 0, 0);
+  const float g = buffer_load_f32(buffer_rsrc(gates + base, n_bytes), (uint32_t)t * 4u);
+  uint64_t v = ~0ull;  // padding past N sorts last
+  if (i < N) {
+    if (e >= 0 && e < E) {
+      v = expert_key(e, g, (uint32_t)i);
+    } else {  // out-of-range id: dropped here, never ranked
+      v = kInvalidKey | (uint64_t)i;
+      slot_of[i] = -1;
+      drop[i] = 1;
+    }
+  }
+  v = block_bitonic_sort<kRun>(v, sk, kRun);
+  if (i < N) keys[i] = v;  // sorted position t of this run
+  // run_off[run][e] = keys of experts below e in the run (e = 0 .. E; invalid keys and padding
+  // count as expert E): the thread holding the first key of a larger expert writes the starts
+  // of every expert it passes
+  const int ex = key_is_valid(v) ? (int)(v >> 56) : E;
+  sex[t] = ex;
+  __syncthreads();
+  int32_t* off = run_off + (int64_t)blockIdx.x * (E + 1);
+  const int prev = t ? sex[t - 1] : -1;
+  for (int e2 = prev + 1; e2 <= ex; ++e2) off[e2] = t;
+  if (t == kRun - 1)
+    for (int e2 = ex + 1; e2 <= E; ++e2) off[e2] = kRun;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void k_dispatch_merge(
+    const uint64_t* __restrict__ keys, const int32_t* __restrict__ run_off, int N, int nb, int E,
+    int k, int cap, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token, uint8_t* __restrict__ drop) {
+  extern __shared__ uint64_t s_keys[];  // merge_lds_bytes(N)
+  __shared__ int s_tot[258], s_koff[258], s_part[kSplit - 1][kMergeKeys];
+  const int t = threadIdx.x, E1 = E + 1;
+  uint16_t* s_off = reinterpret_cast<uint16_t*>(s_keys + merge_key_slots(N));
+  // Every load in flight at once, the expert starts first: the totals below need only them and
+  // run while the keys arrive.  Keys come in pairs as 16-byte loads.  With N odd the last
+  // pair's second key is the workspace word after the keys (the keys' slice ends on a 256-byte
+  // boundary); it and the zeros past it are never searched.
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(run_off, (uint32_t)(nb * E1) * 4u);
+  int ov[kOffRounds];  // zeros past the nb * E1 starts
+#pragma unroll
+  for (int q = 0; q < kOffRounds; ++q)
+    ov[q] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        ro, (uint32_t)((q * kMergeThreads + t) * 4), 0, 0);
+  constexpr int kKeyRounds = kMidN / (2 * kMergeThreads);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(keys, (uint32_t)((N + 1) / 2) * 16u);
+  const int rounds = (N + 2 * kMergeThreads - 1) / (2 * kMergeThreads);
+  uint4 kv[kKeyRounds];
+#pragma unroll
+  for (int q = 0; q < kKeyRounds; ++q)
+    kv[q] = buffer_load16(
+        rk, q < rounds ? (uint32_t)((q * kMergeThreads + t) * 16) : kBufferOOR);
+#pragma unroll
+  for (int q = 0; q < kOffRounds; ++q) s_off[q * kMergeThreads + t] = (uint16_t)ov[q];
+  __syncthreads();
+  // s_tot[e] = valid keys of the experts below e over all runs
+  for (int e = t; e <= E; e += kMergeThreads) {
+    int sum = 0;
+    for (int b = 0; b < nb; ++b) sum += s_off[b * E1 + e];
+    s_tot[e] = sum;
+  }
+  __syncthreads();
+  for (int e = t; e <= E; e += kMergeThreads)
+    s_koff[e] = e < E ? min(s_tot[e + 1] - s_tot[e], cap) : 0;
+  __syncthreads();
+  if (t < 64) wave_exclusive_scan(s_koff, E1, nullptr);  // kept-slot offsets
+  uint4* s_pairs = reinterpret_cast<uint4*>(s_keys);
+#pragma unroll
+  for (int q = 0; q < kKeyRounds; ++q)
+    if (q < rounds) s_pairs[q * kMergeThreads + t] = kv[q];
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = t; e <= E; e += kMergeThreads) {
+      if (e < E) counts[e] = s_tot[e + 1] - s_tot[e];
+      offsets[e] = s_koff[e];
+    }
+  // key p: thread `share` of its kSplit counts the runs b = share, share + kSplit, ...; share 0
+  // also counts the key's own position in its own run
+  const int tk = t % kMergeKeys, share = t / kMergeKeys;
+  const int p = blockIdx.x * kMergeKeys + tk;
+  const uint64_t key = s_keys[p < N ? p : 0];
+  const bool act = p < N && key_is_valid(key);  // out-of-range ids: dropped by k_dispatch_runs
+  const int e = act ? (int)(key >> 56) : 0, run = p / kRun;
+  int part = act && share == 0 ? p % kRun - s_off[run * E1 + e] : 0;
+  constexpr int G = 4;  // runs searched side by side
+  for (int b0 = share; act && b0 < nb; b0 += kSplit * G) {
+    int lo[G], len[G], from[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {  // reads of runs past nb land on run 0 and are discarded
+      const int b = b0 + kSplit * j;
+      const bool other = b < nb && b != run;
+      const int bo = (b < nb ? b : 0) * E1 + e;
+      const int a = s_off[bo], z = s_off[bo + 1];
+      lo[j] = from[j] = other ? b * kRun + a : 0;
+      len[j] = other ? z - a : 0;
+    }
+    // lower bound: lo[j] ends at the first key of run b's segment that is not below `key`.
+    // Branch-free steps, so that the G reads of a step are in flight together; a finished
+    // search (len 0) reads key 0 and keeps its state.
+    int any = 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) any |= len[j];
+    while (any > 0) {
+      uint64_t sv[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) sv[j] = s_keys[len[j] > 0 ? lo[j] + (len[j] >> 1) : 0];
+      any = 0;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int h = len[j] >> 1;
+        const bool below = len[j] > 0 && sv[j] < key;
+        lo[j] = below ? lo[j] + h + 1 : lo[j];
+        len[j] = below ? len[j] - h - 1 : h;
+        any |= len[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) part += lo[j] - from[j];
+  }
+  if (share > 0) s_part[share - 1][tk] = part;
+  __syncthreads();
+  if (share > 0 || !act) return;
+  int rank = part;
+#pragma unroll
+  for (int j = 0; j < kSplit - 1; ++j) rank += s_part[j][tk];
+  const int i = (int)(key & 0xFFFFFFull);
+  if (rank < cap) {
+    const int slot = s_koff[e] + rank;
+    slot_of[i] = slot;
+    drop[i] = 0;
+    row_token[slot] = i / k;
+  } else {
+    slot_of[i] = -1;
+    drop[i] = 1;
+  }
+}
+
+int64_t dispatch_runs(int64_t n) { return n > kSmallN && n <= kMidN ? (n + kRun - 1) / kRun : 0; }
 
 // ---------------------------------------------------------------- routed token rows
 // x_routed[s] = x[row_token[s]] for every kept slot s < offsets[E]: the token rows copied into
@@ -681,6 +899,20 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
   if (N <= kSmallN) {
     hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), 0, st, ids, gates, (int)N, E,
                        s.top_k, s.capacity, counts, offsets, slot_of, row_token, drop);
+    return hipGetLastError();
+  }
+  if (N <= kMidN) {
+    static std::atomic<bool> lds_allowed[kMaxDevices];
+    if (hipError_t err = allow_dynamic_lds((const void*)k_dispatch_merge,
+                                           (int)merge_lds_bytes(kMidN), lds_allowed);
+        err != hipSuccess)
+      return err;
+    const int nb = (int)dispatch_runs(N);
+    hipLaunchKernelGGL(k_dispatch_runs, dim3(nb), dim3(kRun), 0, st, ids, gates, (int)N, E, keys,
+                       blk_hist, slot_of, drop);
+    hipLaunchKernelGGL(k_dispatch_merge, dim3((unsigned)((N + kMergeKeys - 1) / kMergeKeys)),
+                       dim3(kMergeThreads), merge_lds_bytes((int)N), st, keys, blk_hist, (int)N,
+                       nb, E, s.top_k, s.capacity, counts, offsets, slot_of, row_token, drop);
     return hipGetLastError();
   }
   const int chunk = dispatch_chunk(N);

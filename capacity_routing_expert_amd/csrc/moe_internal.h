@@ -96,6 +96,9 @@ constexpr int kDispatchChunk = 2048;  // most assignments per block in the count
 // to kDispatchChunk assignments.
 int dispatch_chunk(int64_t n, bool pairs = false);
 int64_t dispatch_blocks(int64_t n, bool pairs = false);
+// Runs of the two-launch dispatch for n assignments (0 where n takes another path); the
+// blk_hist buffer holds runs * (E + 1) expert starts there.
+int64_t dispatch_runs(int64_t n);
 
 int64_t max_rows(const moe_shape& s);
 enum LayoutKind { kLayoutCompact = 0, kLayoutPadded = 1, kLayoutDropless = 2 };
