@@ -238,6 +238,9 @@ SMALL = [
     (4000, 64, 96, 128, 4, 2.0, "bf16"),  # ... with the large-batch expert tiles
     # 8192 tokens or more: 4-wave router blocks; 40 experts leave the last pass half empty
     (8192, 32, 48, 40, 3, 1.0, "bf16"),
+    # at most 8 experts with many tokens: 8-wave and 4-wave router blocks, ragged counts
+    (4100, 64, 96, 6, 2, 1.0, "bf16"),
+    (17000, 40, 24, 8, 3, 0.9, "bf16"),
     (1, 4, 8, 4, 1, 1.25, "f32"),
     (7, 5, 9, 3, 2, 1.0, "f32"),
     (65, 12, 20, 8, 2, 0.75, "f32"),
@@ -267,11 +270,12 @@ def test_random_small_shapes(T, d, f, E, k, C, dt):
         assert np.array_equal(P.bits(res["out"][int(t)]), P.bits(dev["x"][int(t)]))
 
 
+@pytest.mark.parametrize("T", [500, 5000])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_gate_ties(dt):
+def test_gate_ties(dt, T):
     """Integer-valued x and router weights: many tokens share exactly the same gates, so the
     fill order's token and choice tie-breaks decide the slots."""
-    T, d, f, E, k = 500, 16, 24, 6, 2
+    d, f, E, k = 16, 24, 6, 2
     inp = W.make_shape_inputs(T, d, f, E, dt, seed=5, x_values=(-1.0, 0.0, 1.0))
     f64 = lambda a: W.to_float64(a, dt)
     full = O.forward(f64(inp["x"]), f64(inp["w_router"]), None, f64(inp["w1"]), f64(inp["b1"]),
@@ -547,6 +551,15 @@ ROUTE_SHAPES = [
     (8192, 64, 40, 3, "bf16"),
     (8200, 24, 70, 4, "f32"),
     (65, 12, 5, 2, "f32"),
+    # at most 8 experts (8-token x 8-expert matrix-core tiles): 4- and 8-wave blocks, ragged
+    # token counts, fewer column quads than waves (d 72, d 8), fewer than 8 experts (padding
+    # columns), a single expert, every expert chosen
+    (4097, 72, 8, 2, "bf16"),
+    (5000, 8, 3, 1, "bf16"),
+    (16385, 136, 7, 3, "bf16"),
+    (16384, 512, 1, 1, "bf16"),
+    (20000, 264, 8, 8, "bf16"),
+    (16400, 24, 6, 2, "f32"),
 ]
 
 
