@@ -198,8 +198,10 @@ __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
     const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
     int a_rows, int e, int row0, int rows, int n0) {
-  // waves along slots / features: 2 x 2, 4 x 2 for 8 waves, or 1 x 4 for 32-slot tiles
-  constexpr int WM = NWV == 8 ? 4 : TM >= 64 ? 2 : 1, WN = NWV / WM;
+  // waves along slots / features: 2 x 2; 4 x 2 for 8 waves (1 x 8 when the tile is at least
+  // twice as wide as it is tall: every wave then holds 64 features x all the tile's slots); or
+  // 1 x 4 for 32-slot tiles
+  constexpr int WM = NWV == 8 ? (TN >= 2 * TM ? 1 : 4) : TM >= 64 ? 2 : 1, WN = NWV / WM;
   constexpr int kWaves = WN * WM;
   constexpr int kThreads = kWaves * 64;
   constexpr int KS = BK / 16;                // 16-K MFMA steps per stage
@@ -239,9 +241,10 @@ __device__ __forceinline__ void gemm_tile(
   const int pch = lane % kChunks;
   // Weight rows.  Non-gated: rows n0 .. n0 + TN - 1 of expert e's [N, K] block (rows past N
   // are out of the resource's range).  Gated: expert e's block is [2N, K], gate rows first;
-  // LDS row rho of wave half wv = rho / (TN / 2) holds gate row n0 + wv TN/4 + m (m < TN/4) or
-  // the up row N + n0 + wv TN/4 + (m - TN/4), so gate block i and up block i + FN/2 of a wave
-  // cover the same output features; features past N are out of range.
+  // LDS row rho of the feature portion wv = rho / P of wave column wv (P = TN / WN rows) holds
+  // gate row n0 + wv P/2 + m (m = rho % P < P/2) or the up row N + n0 + wv P/2 + (m - P/2), so
+  // gate block i and up block i + FN/2 of a wave cover the same output features; features past
+  // N are out of range.
   static_assert(BK % kPackK == 0, "a stage reads whole packed blocks");
   const int NW = GATED ? 2 * N : N;                 // weight rows per expert
   const int KBW = (K + kPackK - 1) / kPackK;        // packed blocks per expert
@@ -259,9 +262,10 @@ __device__ __forceinline__ void gemm_tile(
     const int row = (wave * kWLoads + j) * kRowsPerLoad + lrow;
     const int c = pch ^ swz(row);
     if (GATED) {
-      const int wv = row / (TN / 2), m = row % (TN / 2);
-      const int feat = n0 + wv * (TN / 4) + (m % (TN / 4));
-      const int grow = feat + (m >= TN / 4 ? N : 0);
+      constexpr int P = TN / WN;  // weight rows of one wave column
+      const int wv = row / P, m = row % P;
+      const int feat = n0 + wv * (P / 2) + (m % (P / 2));
+      const int grow = feat + (m >= P / 2 ? N : 0);
       woff[j] = feat < N && c * 8 < K ? (WP ? packed_off(grow, c * 8) : (uint32_t)(grow * K + c * 8) * 2u)
                                       : kOutOfRange;
     } else if (WP) {
@@ -909,12 +913,20 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
   // up-projection's XCD groups are 4 token tiles x 8 weight tiles: a token tile's 8 weight tiles
   // then share its gathered rows in one L2 (64-expert fine layer GEMM 1: 395 -> 350 us, collapse
   // 5.20 -> 5.01 ms, mid unchanged; the down-projection keeps 8 x 4).
-  if constexpr (ACT == kActNone)
+  // With 32 experts or more (many experts with few rows), the up-projection takes tiles of 512
+  // features x 128 slots instead: half the token tile, so less padding in each expert's last
+  // tile (lab, same bits: 64-expert fine layer 357 -> 311 us; mid 240 -> 246 us and collapse
+  // 5.16 -> 5.80 ms, so only there).
+  if constexpr (ACT == kActNone) {
     return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
-  else
+  } else {
+    if (E >= 32)
+      return launch_grouped_gemm<512, 128, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4>(
+          A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
     return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
+  }
 }
 
 // the weight layout of the shape picks the kernel
