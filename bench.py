@@ -464,6 +464,29 @@ def main():
     combine_bytes = ((2 * wl.T + n_kept) * dm * inp["x"].itemsize
                      + (4 if dropless else 8) * wl.T * wl.top_k)
 
+    # the optional x_routed output of moe_dispatch (the token rows copied into slot order), an
+    # HBM-bound gather of N_kept rows: K staged dispatch calls without it and K with it, each
+    # bracketed by events; the difference is the gather
+    x_routed_res = None
+    if not padded and not dropless:
+        rt = L.route(d, wl.top_k, cap, ws=ws)
+        plain_ev = [new_events(2) for _ in range(args.steps)]
+        gather_ev = [new_events(2) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for evs, with_x in ((plain_ev, False), (gather_ev, True)):
+            for i in range(args.steps):
+                evs[i][0].record(stream)
+                L.dispatch(shape, rt["ids"], rt["gates"], ws, x=d["x"] if with_x else None)
+                evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_plain = float(np.median([e[0].elapsed_time(e[1]) for e in plain_ev]))
+        t_gather = float(np.median([e[0].elapsed_time(e[1]) for e in gather_ev]))
+        gather_bytes = 2 * n_kept * dm * inp["x"].itemsize
+        x_routed_res = {"dispatch_ms": t_plain, "dispatch_with_x_routed_ms": t_gather,
+                        "gather_bytes": gather_bytes,
+                        "gather_GBps": gather_bytes / max(t_gather - t_plain, 1e-6) * 1e3 / 1e9}
+        del rt
+
     flush_res = None
     if args.flush:
         # cold-cache steps: a 512 MiB write (twice the 256 MiB Infinity Cache) before each one;
@@ -523,6 +546,7 @@ def main():
                                          / PEAK_BF16_TFLOPS,
         "roofline": dict(roof, traffic=traffic),
         "flush": flush_res,
+        "x_routed": x_routed_res,
         "dominant_kernel_ms": dom_ms,
         "dominant_kernel_timing": "start and end of the dominant GEMM's kernel, recorded by its "
                                   "launch in each timed step (moe_set_gemm_timing, "
