@@ -275,8 +275,9 @@ def main():
                          "median and mean per-step time beside the steady-state value")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
-              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer's "
+              "multi-GPU sharding (expert parallel, all-to-all exchange of kept rows) is a "
+              "design, not built", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -60,9 +60,10 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 
 def _cases():
-    """The decode layer (T 64, d_model 2048, d_ff 8192, 8 experts, top-2, capacity 64), then
-    smaller inputs: 40 of its tokens with capacity 8 (drops), a small bf16 layer, the fp32
-    worked example."""
+    """A bf16 layer of 2500 tokens (5000 assignments: the two-launch dispatch), the decode layer
+    (T 64, d_model 2048, d_ff 8192, 8 experts, top-2, capacity 64), then smaller inputs: 40 of
+    its tokens with capacity 8 (drops), a small bf16 layer, the fp32 worked example."""
+    mid = W.make_shape_inputs(2500, 256, 512, 8, "bf16", seed=23, router_bias_std=1.0)
     dec = W.make_inputs("decode")
     wl = dec["workload"]
     cap = O.capacity(wl.T, wl.top_k, wl.n_experts, wl.capacity_factor)
@@ -70,7 +71,8 @@ def _cases():
     part["x"] = dec["x"][:40].copy()
     small = W.make_shape_inputs(300, 128, 256, 8, "bf16", seed=17, router_bias_std=1.0)
     we = W.make_inputs("worked_example")
-    return [("decode T64", dec, 2, cap), ("decode T40 cap 8", part, 2, 8),
+    return [("bf16 T2500", mid, 2, O.capacity(2500, 2, 8, 1.0)), ("decode T64", dec, 2, cap),
+            ("decode T40 cap 8", part, 2, 8),
             ("bf16 T300", small, 2, O.capacity(300, 2, 8, 1.0)), ("worked example", we, 1, 2)]
 
 
@@ -103,7 +105,7 @@ def test_noalloc_matches_layer_forward_on_consecutive_calls():
 def test_noalloc_repeated_and_after_a_larger_call():
     """The scratch keeps the last call's contents: a small call right after a large one, and
     the same call twice, give the workspace path's bits."""
-    big, small = _cases()[0], _cases()[2]
+    big, small = _cases()[1], _cases()[3]
     for name, inp, k, cap in (big, small, small, big):
         dev = L.upload(inp, DEV)
         a = _noalloc(dev, k, cap)
