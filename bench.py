@@ -20,12 +20,18 @@ is the consolidated run's tokens/s.
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
 import hashlib
 import json
 import os
 import re
+import shutil
+import signal
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -72,6 +78,79 @@ def traffic_from_profiles(kernel_tag: str, config_key: str):
     kib = (float(m["fetch_kib_per_dispatch"].group(1)) * float(m["fetch_scale"].group(1)) +
            float(m["write_kib_per_dispatch"].group(1)) * float(m["write_scale"].group(1)))
     return kib * 1024.0
+
+
+def traffic_live(args):
+    """HBM bytes per launch of the two expert GEMMs, measured on this machine: two child runs
+    of this same command under rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE; one warm-up and 3
+    steps, plus a 1 GiB device copy as the calibration), started before this process touches
+    the GPU.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads
+    for the copy.  Returns {"expert_up": bytes, "expert_down": bytes, ...} or None when
+    rocprofv3 is missing, a run fails or times out (its process group is then killed)."""
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(prof):
+        return None
+    base = tempfile.mkdtemp(prefix="moe_bench_pmc_", dir=os.environ.get("TMPDIR", "/tmp"))
+    vals = {}
+    try:
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            out = os.path.join(base, ctr)
+            cmd = [prof, "--pmc", ctr, "-f", "csv", "-d", out, "-o", "run", "--", sys.executable,
+                   os.path.abspath(__file__), "--config", args.config, "--layout", args.layout,
+                   "--weights", args.weights, "--steps", "3", "--warmup", "1",
+                   "--no-cpu-baseline", "--copy-probe", "--traffic", "none"]
+            log(f"[bench] HBM counters: {ctr} child run")
+            # the child's progress lines go to stderr; its JSON line is dropped
+            child = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, start_new_session=True,
+                                     cwd=ROOT)
+            try:
+                rc = child.wait(timeout=240)
+            except subprocess.TimeoutExpired:
+                os.killpg(child.pid, signal.SIGKILL)  # the group this call started
+                child.wait()
+                return None
+            files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
+            if rc != 0 or not files:
+                return None
+            with open(files[0]) as f:
+                vals[ctr] = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                                    float(r["Counter_Value"])) for r in csv.DictReader(f)
+                                   if r["Counter_Name"] == ctr)
+    finally:
+        shutil.rmtree(base, ignore_errors=True)
+
+    return pmc_gemm_traffic(vals)
+
+
+def pmc_gemm_traffic(vals):
+    """Per-launch HBM bytes of the two expert GEMMs from rocprofv3 counter rows.  vals maps
+    "FETCH_SIZE" and "WRITE_SIZE" to (dispatch id, kernel name, grid size, KiB) in dispatch
+    order.  In each layer call GEMM 1 is the first grouped-GEMM launch after the router and
+    GEMM 2 the next one; each counter is scaled by what it reads for the largest device copy
+    (the 1 GiB calibration copy, 1 GiB read and 1 GiB written)."""
+    def scale(ctr):
+        copies = [v for v in vals[ctr] if v[1].startswith("__amd_rocclr_copyBuffer")]
+        big = max(copies, key=lambda v: v[2]) if copies else None
+        return (1 << 30) / (big[3] * 1024.0) if big and big[3] > 0 else None
+
+    def per_gemm(ctr):
+        g = ([], [])
+        state = 0
+        for _, name, _, v in vals[ctr]:
+            if "k_route" in name:
+                state = 1
+            elif "k_grouped_gemm" in name and state in (1, 2):
+                g[state - 1].append(v)
+                state += 1
+        return [float(np.mean(x)) if x else None for x in g]
+
+    fs, ws = scale("FETCH_SIZE"), scale("WRITE_SIZE")
+    f1, f2 = per_gemm("FETCH_SIZE")
+    w1, w2 = per_gemm("WRITE_SIZE")
+    if None in (fs, ws, f1, f2, w1, w2):
+        return None
+    return {"expert_up": (f1 * fs + w1 * ws) * 1024.0, "expert_down": (f2 * fs + w2 * ws) * 1024.0,
+            "fetch_scale": fs, "write_scale": ws}
 
 
 def cpu_baseline(inp, wl, cap, dropless=False):
@@ -269,6 +348,10 @@ def main():
                          "cols]; the results are bit-identical")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic", default="live", choices=["live", "profiles", "none"],
+                    help="roofline.traffic: live = two rocprofv3 --pmc child runs of this "
+                         "command (FETCH_SIZE, WRITE_SIZE) before the measurement; profiles = "
+                         "the committed counter summary of the current kernel code; none")
     ap.add_argument("--flush", action="store_true",
                     help="also time K steps each preceded by a 512 MiB write on the stream (the "
                          "Infinity Cache and the L2s hold none of the step's data), reporting the "
@@ -279,8 +362,15 @@ def main():
               "multi-GPU sharding (expert parallel, all-to-all exchange of kept rows) is a "
               "design, not built", file=sys.stderr)
         sys.exit(2)
+    # live HBM counters of the compact layout's expert GEMMs, taken before this process touches
+    # the GPU (the counter runs are child processes of their own)
+    import torch  # device_count() does not initialise the GPU: the counter runs start first
 
-    import torch
+    live = None
+    if (args.traffic == "live" and args.layout == "compact" and args.config != "decode_pool"
+            and torch.cuda.device_count() > 0):
+        live = traffic_live(args)
+
     from capacity_routing_expert_amd import binding as B
     from capacity_routing_expert_amd import layer as L
     from capacity_routing_expert_amd import workloads as W
@@ -456,9 +546,16 @@ def main():
                 "units_per_launch": f"{active} active experts x {w} B of weights + {act} B of "
                                     f"activations ({rows} rows)",
                 "tflops": achieved}
-    # the committed counter summaries are of the compact layout's launches
-    traffic = None if padded or dropless else traffic_from_profiles(
-        "gemm1" if dom == "expert_up" else "gemm2", args.config)
+    # HBM bytes of the dominant GEMM per launch: the live counter runs, else the committed
+    # counter summary when it is of the current kernel code (both are of the compact layout)
+    traffic, traffic_src = None, None
+    if live is not None:
+        traffic, traffic_src = live[dom], ("live: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE child "
+                                           f"runs, copy scale {live['fetch_scale']:.3f} / "
+                                           f"{live['write_scale']:.3f}")
+    elif not padded and not dropless and args.traffic != "none":
+        traffic = traffic_from_profiles("gemm1" if dom == "expert_up" else "gemm2", args.config)
+        traffic_src = "committed counter summary" if traffic is not None else None
 
     route_bytes = wl.T * dm * inp["x"].itemsize + wl.n_experts * dm * inp["x"].itemsize + 8 * wl.T * wl.top_k
     # combine: x, the kept Y rows, out, gates + slots; moe_sum: x, the T * k pair rows, out, ids
@@ -545,7 +642,7 @@ def main():
         "expert_gemm_tflops": (gemm1_flop + gemm2_flop) / expert_s / 1e12,
         "expert_gemm_frac_of_bf16_peak": (gemm1_flop + gemm2_flop) / expert_s / 1e12
                                          / PEAK_BF16_TFLOPS,
-        "roofline": dict(roof, traffic=traffic),
+        "roofline": dict(roof, traffic=traffic, traffic_source=traffic_src),
         "flush": flush_res,
         "x_routed": x_routed_res,
         "dominant_kernel_ms": dom_ms,
