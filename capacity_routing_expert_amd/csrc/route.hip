@@ -257,51 +257,54 @@ constexpr size_t route_lds_max() { return (size_t)8 * (7 * 2 * 256 + 256 * 16); 
 // per SIMD: 77 TFLOP/s, against 73 for the 16 x 16 x 4 instruction).  Its lane layout (probe):
 // lane l = 16 g + 4 b + r holds row r of block b's A operand and column r of block b's B operand
 // at step g of the 4-deep contraction, and receives row g, column r of block b's result.
-// Blocks b = 2 tg + eg take tokens 4 tg .. 4 tg + 3 and experts 4 eg .. 4 eg + 3, so one
-// instruction computes an 8-token x 8-expert tile with no padding.  As in k_route_mfma, lane l
-// loads 8 consecutive columns of its token and of its expert (chunk 4 cq + g), and MFMA step s
-// pairs column s of both: a permutation of the summation order only.  A block of NW waves takes
-// TT = 8 R tokens, wave w takes chunk quads w, w + NW, ..., and wave 0 adds the other waves'
-// partial tiles in wave order before the block finishes its tokens.  Each block starts its walk
-// over those quads at its own point (block index modulo the quad count) and wraps around, so
-// that the blocks do not all read the same columns of x at once (a fixed order per block: the
-// logits are still reproducible).
-template <typename TIn, int R, int NW, int PF>
+// The four blocks take four groups of 4 tokens (block b: tokens 4 b .. 4 b + 3 of a 16-token
+// row group) and the same 4 experts, and two instructions per step cover experts 0 .. 3 and
+// 4 .. 7.  So every lane loads x chunks that no other lane loads (only the small router weights
+// are loaded by several lanes), and a wave's 16 x 8 tile has no padding.  As in k_route_mfma,
+// lane l loads 8 consecutive columns of its token and of its expert (chunk 4 cq + g), and MFMA
+// step s pairs column s of both: a permutation of the summation order only.  A block of NW
+// waves takes TT = 16 RT tokens, wave w takes chunk quads w, w + NW, ..., and wave 0 adds the
+// other waves' partial tiles in wave order before the block finishes its tokens.  Each block
+// starts its walk over those quads at its own point (block index modulo the quad count) and
+// wraps around, so that the blocks do not all read the same columns of x at once (a fixed
+// order per block: the logits are still reproducible).
+template <typename TIn, int RT, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void k_route_mfma4(
     const TIn* __restrict__ x, const TIn* __restrict__ w, const float* __restrict__ b_router,
     int64_t T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
     float* __restrict__ logits_out) {
-  constexpr int TT = 8 * R, NT = 64 * NW;
-  __shared__ double part[NW > 1 ? NW - 1 : 1][R][64];  // waves 1 .. NW - 1: partial tiles
-  __shared__ double logit[8 * TT];                      // [expert][token of the block]
+  constexpr int TT = 16 * RT, NT = 64 * NW;
+  __shared__ double part[NW > 1 ? NW - 1 : 1][2 * RT][64];  // waves 1 .. NW - 1: partial tiles
+  __shared__ double logit[8 * TT];                          // [expert][token of the block]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, blk = (lane >> 2) & 3, r = lane & 3;
-  const int tg = blk >> 1, eg = blk & 1;
+  const int g = lane >> 4, b = (lane >> 2) & 3, r = lane & 3;
   const int64_t tok0 = (int64_t)blockIdx.x * TT;
   const int d8 = (d + 7) / 8, nq = (d8 + 3) / 4;
   // x and the router weights (< 2 GiB each, host-checked)
   const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x, (uint32_t)(T * d * (int64_t)sizeof(TIn)));
   const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(w, (uint32_t)((int64_t)E * d * sizeof(TIn)));
 
-  // a single tile per wave alternates two accumulators, so that consecutive MFMAs do not wait
-  // on each other (added at the end: a permutation of the summation order only)
-  constexpr int NACC = R == 1 ? 2 : 1;
-  double acc[NACC][R];
+  // acc[eg][rr]: experts 4 eg .. 4 eg + 3 of row group rr (the two expert groups alternate, so
+  // consecutive MFMAs do not wait on each other)
+  double acc[2][RT];
 #pragma unroll
-  for (int a = 0; a < NACC; ++a)
+  for (int eg = 0; eg < 2; ++eg)
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) acc[a][rr] = 0.0;
-  Chunk8<TIn> xr[PF][R], wr[PF];
+    for (int rr = 0; rr < RT; ++rr) acc[eg][rr] = 0.0;
+  Chunk8<TIn> xr[PF][RT], wr[PF][2];
   auto load = [&](int p, int cq) {
     const int c = cq * 4 + g;
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      const int64_t t = tok0 + 8 * rr + 4 * tg + r;
+    for (int rr = 0; rr < RT; ++rr) {
+      const int64_t t = tok0 + 16 * rr + 4 * b + r;
       xr[p][rr].load(xs, cq < nq && t < T, t, c, d);
     }
-    const int e = 4 * eg + r;
-    wr[p].load(ws, cq < nq && e < E, e, c, d);
+#pragma unroll
+    for (int eg = 0; eg < 2; ++eg) {
+      const int e = 4 * eg + r;
+      wr[p][eg].load(ws, cq < nq && e < E, e, c, d);
+    }
   };
   // this wave's n_w quads wave, wave + NW, ..., walked from index j0 on; indices past n_w give
   // quad nq, whose loads read zeros
@@ -313,36 +316,43 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma4(
   for (int i0 = 0; i0 < n_w; i0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      double xa[R][8], wb[8];
+      double xa[RT][8], wb[2][8];
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) xr[p][rr].widen(xa[rr]);
-      wr[p].widen(wb);
+      for (int rr = 0; rr < RT; ++rr) xr[p][rr].widen(xa[rr]);
+      wr[p][0].widen(wb[0]);
+      wr[p][1].widen(wb[1]);
       load(p, quad_of(i0 + p + PF));
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8)
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-          acc[s8 % NACC][rr] =
-              __builtin_amdgcn_mfma_f64_4x4x4f64(xa[rr][s8], wb[s8], acc[s8 % NACC][rr], 0, 0, 0);
+        for (int rr = 0; rr < RT; ++rr)
+#pragma unroll
+          for (int eg = 0; eg < 2; ++eg)
+            acc[eg][rr] =
+                __builtin_amdgcn_mfma_f64_4x4x4f64(xa[rr][s8], wb[eg][s8], acc[eg][rr], 0, 0, 0);
     }
   }
-  double res[R];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) res[rr] = NACC == 2 ? acc[0][rr] + acc[NACC - 1][rr] : acc[0][rr];
-  // lane l holds token 8 rr + 4 tg + g of the block, expert 4 eg + r
+  // lane l holds token 16 rr + 4 b + g of the block, expert 4 eg + r
   if (wave > 0) {
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) part[wave - 1][rr][lane] = res[rr];
+    for (int eg = 0; eg < 2; ++eg)
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr) part[wave - 1][eg * RT + rr][lane] = acc[eg][rr];
   }
   __syncthreads();
   if (wave == 0) {
     for (int ww = 1; ww < NW; ++ww)
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) res[rr] += part[ww - 1][rr][lane];
-    const int e = 4 * eg + r;
+      for (int eg = 0; eg < 2; ++eg)
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-      if (e < E) logit[e * TT + 8 * rr + 4 * tg + g] = res[rr];
+        for (int rr = 0; rr < RT; ++rr) acc[eg][rr] += part[ww - 1][eg * RT + rr][lane];
+#pragma unroll
+    for (int eg = 0; eg < 2; ++eg) {
+      const int e = 4 * eg + r;
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr)
+        if (e < E) logit[e * TT + 16 * rr + 4 * b + g] = acc[eg][rr];
+    }
   }
   __syncthreads();
   finish_group<TT>(logit, b_router, tok0, T, E, k, NT / TT, NT, ids, gates, logits_out);
@@ -383,11 +393,11 @@ hipError_t route_waves(const moe_shape& s, const TIn* x, const TIn* w, const flo
   return route_launch<TIn, EBG, 8>(s, x, w, b_router, ids, gates, logits, st);
 }
 
-template <typename TIn, int R, int NW>
+template <typename TIn, int RT, int NW>
 hipError_t route4_launch(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                          int32_t* ids, float* gates, float* logits, hipStream_t st) {
-  constexpr int TT = 8 * R, PF = 2;
-  hipLaunchKernelGGL((k_route_mfma4<TIn, R, NW, PF>), dim3((unsigned)((s.T + TT - 1) / TT)),
+  constexpr int TT = 16 * RT, PF = 2;
+  hipLaunchKernelGGL((k_route_mfma4<TIn, RT, NW, PF>), dim3((unsigned)((s.T + TT - 1) / TT)),
                      dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts, s.top_k,
                      ids, gates, logits);
   return hipGetLastError();
@@ -396,13 +406,14 @@ hipError_t route4_launch(const moe_shape& s, const TIn* x, const TIn* w, const f
 template <typename TIn>
 hipError_t route_any(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                      int32_t* ids, float* gates, float* logits, hipStream_t st) {
-  // At most 8 experts: 8-token x 8-expert tiles, 4-wave blocks, two chunk quads in flight per
-  // wave.  From 16384 tokens a lane takes 8 tokens (64 per block: the weight loads and widenings
-  // are shared by more tiles); smaller batches 2 (16 per block, more blocks).  Lab, same routing:
-  // collapse layer 97 -> 72 to 78 us against the 16 x 16 tiles, mid 13.0 -> 12.3 us.
+  // At most 8 experts: 16-token x 8-expert tiles, 4-wave blocks, two chunk quads in flight per
+  // wave.  From 16384 tokens a lane takes 4 row groups (64 tokens per block: the weight loads
+  // and widenings are shared by more tiles); smaller batches one (16 per block, more blocks).
+  // Lab, same routing: collapse layer 97 us with the 16 x 16 tiles, 72 to 78 us with 8-token x
+  // 8-expert tiles (two lanes loading each x chunk), 56 us with these; mid 13.0 -> 12.3 us.
   if (s.n_experts <= 8) {
-    if (s.T >= 16384) return route4_launch<TIn, 8, 4>(s, x, w, b_router, ids, gates, logits, st);
-    return route4_launch<TIn, 2, 4>(s, x, w, b_router, ids, gates, logits, st);
+    if (s.T >= 16384) return route4_launch<TIn, 4, 4>(s, x, w, b_router, ids, gates, logits, st);
+    return route4_launch<TIn, 1, 4>(s, x, w, b_router, ids, gates, logits, st);
   }
   if (s.n_experts <= 16) return route_waves<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
   return route_waves<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);
