@@ -251,32 +251,6 @@ __device__ void expert_prefix(const int32_t* __restrict__ counts, int E, int* s_
   __syncthreads();
 }
 
-// 32-bit DPP lane move within rows of 16 lanes (all rows and banks enabled)
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  return ((uint64_t)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
-}
-// The key of lane (lane ^ stride), stride < 64.  Strides 1 and 2 are quad permutations and 8 a
-// rotation by half a row, all DPP moves; stride 4 takes the rotations by 12 and by 4 (lane
-// i reads lane i + 4 or i - 4 of its row) and keeps the one that lands on the partner; 16 and 32
-// go through ds_bpermute.
-__device__ __forceinline__ uint64_t xor_partner(uint64_t v, int stride) {
-  switch (stride) {
-    case 1: return dpp64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-    case 2: return dpp64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-    case 4: {
-      const uint64_t up = dpp64<0x12C>(v), down = dpp64<0x124>(v);  // row_ror 12, row_ror 4
-      return (threadIdx.x & 4) ? down : up;
-    }
-    case 8: return dpp64<0x128>(v);  // row_ror 8
-    default: return __shfl_xor(v, stride, 64);
-  }
-}
-
 // Bitonic sort of n keys (n a power of two, at most NMAX and the workgroup size), one per
 // thread: returns the key that lands at this thread's index in ascending order within its
 // aligned group of n threads.  Partners closer than 64 are in the same wave (xor_partner),

@@ -93,6 +93,51 @@ __device__ void finish_group(double* lds, const float* __restrict__ b_router, in
   }
 }
 
+// The same finish for at most 8 experts, without LDS round trips: 8 lanes per token, lane e
+// (of an aligned group of 8) owns expert e.  The maximum, the sum of exponentials and each
+// top-k round reduce over the 8 lanes with DPP lane moves in the order xor 4, 2, 1, which adds
+// the same pairs as finish_group's butterfly over 16 lanes (its upper 8 lanes hold nothing), so
+// both give the same bits.  bias_e is this lane's b_router entry, loaded by the caller early.
+template <int TB>
+__device__ void finish_e8(const double* lds, bool has_bias, float bias_e, int64_t tok0,
+                          int64_t T, int E, int k, int nthr, int32_t* __restrict__ ids,
+                          float* __restrict__ gates, float* __restrict__ logits_out) {
+  const int e = threadIdx.x & 7;
+  const bool ok = e < E;
+  auto dxor = [](double v, int s) {
+    return __longlong_as_double((long long)xor_partner((uint64_t)__double_as_longlong(v), s));
+  };
+  for (int base = 0; base < TB * 8; base += nthr) {  // whole waves leave together
+    const int ti = (base + (int)threadIdx.x) >> 3;
+    if (ti >= TB) break;
+    const int64_t tt = tok0 + ti;
+    double L = ok ? lds[e * TB + ti] : -INFINITY;
+    if (ok && has_bias) L += (double)bias_e;
+    if (ok && logits_out && tt < T) logits_out[tt * E + e] = (float)L;
+    double m = L;
+    for (int s = 4; s >= 1; s >>= 1) m = fmax(m, dxor(m, s));
+    const double v = ok ? exp(L - m) : 0.0;
+    double z = v;
+    for (int s = 4; s >= 1; s >>= 1) z += dxor(z, s);
+    // (gate descending, expert ascending) keys, as in finish_group; a taken expert's key is 0
+    const float gv = (float)(v / z);
+    uint64_t key = ok ? ((uint64_t)__float_as_uint(gv) << 32) | (0xFFFFFFFFull - (unsigned)e) : 0ull;
+    for (int c = 0; c < k; ++c) {
+      uint64_t best = key;
+      for (int s = 4; s >= 1; s >>= 1) {
+        const uint64_t o = xor_partner(best, s);
+        best = o > best ? o : best;
+      }
+      const int ew = (int)(0xFFFFFFFFull - (best & 0xFFFFFFFFull));
+      if (e == ew) key = 0ull;
+      if (e == 0 && tt < T) {
+        ids[tt * k + c] = ew;
+        gates[tt * k + c] = __uint_as_float((uint32_t)(best >> 32));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- matrix-core router
 // The logit GEMM [T, d] x [d, E] on the fp64 matrix cores: v_mfma_f64_16x16x4f64 multiplies a
 // 16 x 4 tile of tokens by a 4 x 16 tile of experts, fp64 products of the widened inputs
@@ -313,6 +358,10 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma4(
   auto quad_of = [&](int i) { return i < n_w ? wave + NW * ((j0 + i) % n_w) : nq; };
 #pragma unroll
   for (int p = 0; p < PF; ++p) load(p, quad_of(p));
+  // this lane's router bias for the finish, loaded behind the first quads (the waits for those
+  // then do not include it)
+  const float bias_e =
+      b_router && (int)(threadIdx.x & 7) < E ? b_router[threadIdx.x & 7] : 0.0f;
   for (int i0 = 0; i0 < n_w; i0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -355,7 +404,7 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma4(
     }
   }
   __syncthreads();
-  finish_group<TT>(logit, b_router, tok0, T, E, k, NT / TT, NT, ids, gates, logits_out);
+  finish_e8<TT>(logit, b_router != nullptr, bias_e, tok0, T, E, k, NT, ids, gates, logits_out);
 }
 
 namespace {
