@@ -366,14 +366,16 @@ def main():
     # the GPU (the counter runs are child processes of their own)
     import torch  # device_count() does not initialise the GPU: the counter runs start first
 
+    from capacity_routing_expert_amd import workloads as W
+
     live = None
-    if (args.traffic == "live" and args.layout == "compact" and args.config != "decode_pool"
-            and torch.cuda.device_count() > 0):
+    wl0 = W.WORKLOADS.get(args.config)
+    if (args.traffic == "live" and args.layout == "compact" and wl0 is not None
+            and wl0.dtype == "bf16" and not wl0.batch_size and torch.cuda.device_count() > 0):
         live = traffic_live(args)
 
     from capacity_routing_expert_amd import binding as B
     from capacity_routing_expert_amd import layer as L
-    from capacity_routing_expert_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
