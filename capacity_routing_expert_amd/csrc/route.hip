@@ -59,14 +59,18 @@ __device__ void finish_group(double* lds, const float* __restrict__ b_router, in
 
   double m = -INFINITY;
   for (int e = sub; e < E; e += LPT) m = fmax(m, lds[e * TB + ti]);
-  for (int off = LPT >> 1; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+  // lane exchanges: DPP moves for partners up to 8 lanes away, ds_bpermute beyond
+  auto dxor = [](double v, int s) {
+    return __longlong_as_double((long long)xor_partner((uint64_t)__double_as_longlong(v), s));
+  };
+  for (int off = LPT >> 1; off >= 1; off >>= 1) m = fmax(m, dxor(m, off));
   double z = 0.0;
   for (int e = sub; e < E; e += LPT) {
     const double v = exp(lds[e * TB + ti] - m);
     lds[e * TB + ti] = v;
     z += v;
   }
-  for (int off = LPT >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  for (int off = LPT >> 1; off >= 1; off >>= 1) z += dxor(z, off);
   for (int e = sub; e < E; e += LPT) lds[e * TB + ti] = (double)(float)(lds[e * TB + ti] / z);
 
   // k rounds of a group arg-max on (gate descending, expert ascending); gates are >= 0,
@@ -81,7 +85,7 @@ __device__ void finish_group(double* lds, const float* __restrict__ b_router, in
       best = key > best ? key : best;
     }
     for (int off = LPT >> 1; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off, 64);
+      const unsigned long long o = xor_partner(best, off);
       best = o > best ? o : best;
     }
     const int ew = (int)(0xFFFFFFFFull - (best & 0xFFFFFFFFull));
