@@ -306,6 +306,93 @@ def bench_pool(args, wl, inp):
     print(json.dumps(res), flush=True)
 
 
+def bench_shard(args, wl, inp):
+    """One GPU's share under expert parallelism: the expert FFN (moe_expert_ffn, both GEMMs) of
+    the one expert this GPU owns, over the rows it received (x rows in receive order, all kept).
+    The all-to-all exchanges around it are not built; the roofline is the dominant GEMM's kernel
+    time, recorded by its launch in each timed step."""
+    import torch
+    from capacity_routing_expert_amd import binding as B
+    from capacity_routing_expert_amd import layer as L
+
+    dev = torch.device("cuda:0")
+    d = L.upload(inp, dev)
+    if args.weights == "packed":
+        d = L.pack_weights(d)
+    rows = wl.T
+    shape = L.shape_of(d, wl.top_k, rows)
+    ws = L.workspace(shape, dev)
+    row_token = torch.arange(rows, dtype=torch.int32, device=dev)
+    offsets = torch.tensor([0, rows], dtype=torch.int32, device=dev)
+    y = torch.empty((rows, wl.d_model), dtype=d["x"].dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.moe_expert_ffn(shape, d["x"], row_token, offsets, d["w1"], d["b1"], d["w2"], d["b2"],
+                         y, ws)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for ev in evs:
+            ev.record(stream)
+        return evs
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    evsets = [new_events(4) for _ in range(args.steps)]
+    arms = [(ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event) for ev in evs])
+            for evs in evsets]
+    set_timing = B.lib().moe_set_gemm_timing
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if set_timing(arms[i]) != 0:
+            raise RuntimeError(B.last_error())
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evsets]))
+    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evsets]))
+    flop = 2.0 * rows * wl.d_model * wl.d_ff  # per GEMM
+    dom = "expert_up" if up_ms >= down_ms else "expert_down"
+    dom_ms = max(up_ms, down_ms)
+    achieved = flop / (dom_ms / 1e3) / 1e12
+    res = {
+        "metric": "expert FFN rows/s of one GPU's share (expert parallel over 8 GPUs, the hot "
+                  "expert's owner); expert GEMM TFLOP/s as % of MI355X bf16 peak",
+        "value": rows / wall,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
+        "config": {"workload": wl.name, "rows": rows, "d_model": wl.d_model, "d_ff": wl.d_ff,
+                   "n_experts_on_this_gpu": 1, "weights": args.weights,
+                   "step": "moe_expert_ffn: GEMM 1 (gather by row_token + W1 + b1 + SiLU), "
+                           "GEMM 2 (W2 + b2); no routing, dispatch, exchange or combine"},
+        "roofline": {"kernel": "k_grouped_gemm, 8 waves (GEMM 1)" if dom == "expert_up"
+                               else "k_grouped_gemm_loaders (GEMM 2)",
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "units_per_launch": f"{rows} rows x 2*{wl.d_model}*{wl.d_ff} FLOP"},
+        "gemm_kernel_ms": {"expert_up": up_ms, "expert_down": down_ms},
+        "expert_gemm_tflops": 2 * flop / ((up_ms + down_ms) / 1e3) / 1e12,
+        "expert_gemm_frac_of_bf16_peak": 2 * flop / ((up_ms + down_ms) / 1e3) / 1e12
+                                         / PEAK_BF16_TFLOPS,
+        "cpu_baseline": None,
+        "gemm_timing": "start and end of each GEMM's kernel, recorded by its launch in each timed "
+                       "step (moe_set_gemm_timing), averaged over the K steps",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline_pool(inp, wl):
     """The oracle's pooled layer (route, Token Scheduler, per-batch layer) on this host."""
     import oracle.moe_oracle as O
@@ -336,7 +423,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mid",
-                    help="worked_example | mid | fine | decode | collapse | gated | decode_pool")
+                    help="worked_example | mid | fine | decode | collapse | gated | decode_pool | "
+                         "ep8_hot_shard")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", default="compact", choices=["compact", "padded", "dropless"],
                     help="compact: the expert FFN runs over the kept rows only; padded: over "
@@ -371,7 +459,8 @@ def main():
     live = None
     wl0 = W.WORKLOADS.get(args.config)
     if (args.traffic == "live" and args.layout == "compact" and wl0 is not None
-            and wl0.dtype == "bf16" and not wl0.batch_size and torch.cuda.device_count() > 0):
+            and wl0.dtype == "bf16" and not wl0.batch_size and wl0.key != "ep8_hot_shard"
+            and torch.cuda.device_count() > 0):
         live = traffic_live(args)
 
     from capacity_routing_expert_amd import binding as B
@@ -388,6 +477,9 @@ def main():
     inp = W.make_inputs(wl)
     if wl.batch_size:
         bench_pool(args, wl, inp)
+        return
+    if wl.key == "ep8_hot_shard":
+        bench_shard(args, wl, inp)
         return
     d = L.upload(inp, dev)
     if args.weights == "packed" and inp["dtype"] != "bf16":

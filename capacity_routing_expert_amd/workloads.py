@@ -58,6 +58,12 @@ WORKLOADS = {
     # (64 tokens, d 2048, d_ff 8192, 8 experts, top-2, C 4.0, capacity 64 per batch)
     "decode_pool": Workload("decode_pool", "decode_pool_bf16_8x64_d2048_f8192_E8_top2_C4.0", 6,
                             512, 2048, 8192, 8, 2, 4.0, "bf16", "none", 0.02, "ffn", 64),
+    # one GPU's share of the collapse layer under expert parallelism over 8 GPUs: the hot
+    # expert's owner receives its 16384 kept rows (capacity 16384) and runs that one expert's
+    # FFN on them (d_model 4096, d_ff 14336); x holds the received rows, in receive order
+    "ep8_hot_shard": Workload("ep8_hot_shard", "collapse_ep8_hot_expert_shard_bf16_rows16384_"
+                              "d4096_f14336_E1", 7, 16384, 4096, 14336, 1, 1, 1.0, "bf16", "none",
+                              0.02),
 }
 
 

@@ -617,3 +617,30 @@ def test_dispatch_gathers_routed_rows(T, d, E, k, C, dt):
     assert np.array_equal(P.bits(b["x_routed"][:n]), P.bits(want))
     dref = O.dispatch(P.to_np(r["ids"]), P.to_np(r["gates"]), E, cap)
     assert np.array_equal(P.to_np(b["row_token"])[:n], dref["row_token"])
+
+
+# --------------------------------------------------------------------------- one GPU's share
+def test_ep8_hot_shard_expert_ffn():
+    """The collapse layer's hot expert as one GPU's share under expert parallelism (16384
+    received rows through one expert, d_model 4096, d_ff 14336), in the launch configuration
+    bench.py times (packed weights, rows in receive order): every row against the oracle."""
+    wl = W.WORKLOADS["ep8_hot_shard"]
+    say(f"[shard] {wl.name}")
+    inp = W.make_inputs(wl)
+    dt = inp["dtype"]
+    dev = L.pack_weights(L.upload(inp, DEV))
+    rows = wl.T
+    shape = L.shape_of(dev, wl.top_k, rows)
+    row_token = torch.arange(rows, dtype=torch.int32, device=DEV)
+    offsets = torch.tensor([0, rows], dtype=torch.int32, device=DEV)
+    y = L.expert_ffn(shape, dev, row_token, offsets)
+    torch.cuda.synchronize()
+    got = P.to_np(y[:rows])
+    del y, dev
+    torch.cuda.empty_cache()
+    ref = O.expert_ffn_slots(W.to_float64(inp["x"], dt), np.arange(rows), np.array([0, rows]),
+                             F64(inp["w1"], dt), F64(inp["b1"], dt), F64(inp["w2"], dt),
+                             F64(inp["b2"], dt))
+    err, el = P.max_abs_rel(got, ref), P.elementwise_rel(got, ref)
+    say(f"    Y max-abs-rel {err:.3e} (element-wise {el:.3e}) over {rows} rows")
+    assert err <= P.TOL[dt], err
