@@ -10,6 +10,10 @@ router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), e
                  steps record themselves (moe_set_gemm_timing, hipExtLaunchKernel), so the
                  steps `value` is timed on carry no extra marker between launches
   cpu_baseline   the CPU oracle timed on this host on the same workload (a baseline only)
+Before the timed steps: at least --warmup untimed steps, continued until --warmup-ms (100 ms)
+of wall time have passed, since the GPU reaches its steady clocks only after about 30 ms of
+sustained load.  roofline.traffic: HBM bytes per launch of the dominant GEMM from two
+rocprofv3 --pmc child runs of this command (skipped with --traffic none).
 Workload: the mid-size layer (T 4096, d_model 2048, d_ff 8192, 8 experts, top-2, capacity
 factor 1.25) unless --config names another.  --layout dropless times the dropless pair-order
 flow instead (no capacity: pair dispatch, pair-order GEMMs with the top-k weight applied in
@@ -59,6 +63,24 @@ def code_digest(path: str) -> str:
 
 
 GEMM_SOURCE = os.path.join(ROOT, "capacity_routing_expert_amd", "csrc", "gemm_bf16.hip")
+
+
+def warm_up(step, min_steps: int, min_ms: float, sync) -> dict:
+    """Untimed warm-up: at least `min_steps` steps, continued until `min_ms` of wall time have
+    passed (checked every 8 steps, after a sync).  Under sustained load this GPU takes about
+    30 ms to settle: the mid layer's step time falls from about 516 to 400 us over its first
+    60 to 80 steps, and ramps again after two idle seconds."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n >= min_steps and n % 8 == 0:
+            sync()
+            if (time.perf_counter() - t0) * 1e3 >= min_ms:
+                break
+    sync()
+    return {"steps": n, "ms": (time.perf_counter() - t0) * 1e3}
 
 
 def traffic_from_profiles(kernel_tag: str, config_key: str):
@@ -245,9 +267,9 @@ def bench_pool(args, wl, inp):
                                     events=events)
 
     result = {}
+    warm = {}
     for cons in (False, True):
-        for _ in range(args.warmup):
-            run(cons)
+        warm[cons] = warm_up(lambda: run(cons), args.warmup, args.warmup_ms, torch.cuda.synchronize)
         evsets = []
         for _ in range(args.steps):
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -294,6 +316,7 @@ def bench_pool(args, wl, inp):
                      "traffic": None,
                      "units_per_launch": f"{sum(c['active_experts'])} active (batch, expert) "
                                          f"pairs x {w_bytes} B of weights"},
+        "warmup_run": {"consolidated": warm[True], "original": warm[False]},
         "consolidated": c,
         "original": o,
         "speedup_vs_original": c["tokens_per_s"] / o["tokens_per_s"],
@@ -337,9 +360,8 @@ def bench_shard(args, wl, inp):
             ev.record(stream)
         return evs
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    log(f"[bench] warmup {args.warmup} steps, {args.warmup_ms:.0f} ms at least")
+    warm = warm_up(step, args.warmup, args.warmup_ms, torch.cuda.synchronize)
     evsets = [new_events(4) for _ in range(args.steps)]
     arms = [(ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event) for ev in evs])
             for evs in evsets]
@@ -387,6 +409,7 @@ def bench_shard(args, wl, inp):
         "expert_gemm_frac_of_bf16_peak": 2 * flop / ((up_ms + down_ms) / 1e3) / 1e12
                                          / PEAK_BF16_TFLOPS,
         "cpu_baseline": None,
+        "warmup_run": warm,
         "gemm_timing": "start and end of each GEMM's kernel, recorded by its launch in each timed "
                        "step (moe_set_gemm_timing), averaged over the K steps",
     }
@@ -421,7 +444,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="warm-up steps before the timed ones (at least this many; see --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="keep warming up until this much wall time has passed: the GPU needs "
+                         "about 30 ms of sustained load to reach its steady clocks")
     ap.add_argument("--config", default="mid",
                     help="worked_example | mid | fine | decode | collapse | gated | decode_pool | "
                          "ep8_hot_shard")
@@ -548,9 +575,9 @@ def main():
             ev.record(stream)  # creates the underlying hipEvent_t
         return evs
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(max(args.warmup - 1, 0)):
-        step()
+    log(f"[bench] warmup {args.warmup} steps, {args.warmup_ms:.0f} ms at least")
+    warm = warm_up(step, max(args.warmup - 1, 0), args.warmup_ms, torch.cuda.synchronize)
+    warm["steps"] += 1  # and the probe step below
     # the last warm-up step times both expert GEMMs' kernels, to find the dominant one
     probe = new_events(4)
     torch.cuda.synchronize()
@@ -723,6 +750,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": warm,
         "ms_per_step": wall * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
