@@ -192,12 +192,13 @@ int64_t group_grid(int64_t mt_ub, int64_t nt) {
 
 // One TN x TM output tile of expert e: token rows row0 .. row0 + rows - 1 (slots), features
 // n0 .. n0 + TN - 1; NS-deep ring of BK-deep stages.
-template <int TN, int TM, int BK, int NS, bool GATHER, int ACT, int OUT, bool WP, int NWV = 4>
+template <int TN, int TM, int BK, int NS, bool GATHER, int ACT, int OUT, bool WP, int NWV = 4,
+          bool HP = false>
 __device__ __forceinline__ void gemm_tile(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
     const int32_t* __restrict__ out_row, const float* __restrict__ row_scale, int N, int K,
-    int a_rows, int e, int row0, int rows, int n0) {
+    int a_rows, int e, int row0, int rows, int n0, int h_rows) {
   // waves along slots / features: 2 x 2; 4 x 2 for 8 waves (1 x 8 when the tile is at least
   // twice as wide as it is tall: every wave then holds 64 features x all the tile's slots); or
   // 1 x 4 for 32-slot tiles
@@ -482,6 +483,21 @@ __device__ __forceinline__ void gemm_tile(
   __syncthreads();
   constexpr int kChunksPerRow = TNO / 8;
   const int ncols = min(TNO, N - n0);
+  if constexpr (HP) {
+    // H in 32-column blocks (slot order, N a multiple of 32): element (slot r, feature n) at
+    // ((n / 32) h_rows + r) 32 + n % 32.  Thread c writes chunk c % 4 of row (c / 4) % rows of
+    // the tile's 32-column block c / (4 rows), so consecutive threads fill consecutive 16 bytes.
+    static_assert(OUT == kOutSlots && TNO % 32 == 0, "packed H holds slot-order rows");
+    for (int c = threadIdx.x; c < rows * kChunksPerRow; c += kThreads) {
+      const int q = c & 3, rb = c >> 2;
+      const int row = rb % rows, blk = rb / rows;
+      const int n = n0 + blk * 32 + q * 8;
+      if (n < N)
+        *reinterpret_cast<uint4*>(out + ((int64_t)(n >> 5) * h_rows + row0 + row) * 32 + q * 8) =
+            *reinterpret_cast<const uint4*>(stile + row * kPitch + (blk * 32 + q * 8) * 2);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < rows * kChunksPerRow; c += kThreads) {
     const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
     const int64_t orow = OUT != kOutSlots ? (int64_t)srow[row] : (int64_t)(row0 + row);
@@ -495,12 +511,12 @@ __device__ __forceinline__ void gemm_tile(
 // expert_offsets (device memory: the kept-row counts are only known on the device), finds its
 // own (expert, token tile, feature tile) and exits if that tile does not exist.
 template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
-          int NWV = 4, int GM = 8>
+          int NWV = 4, int GM = 8, bool HP = false>
 __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ out, const int32_t* __restrict__ out_row,
-    const float* __restrict__ row_scale, int E, int N, int K, int a_rows) {
+    const float* __restrict__ row_scale, int E, int N, int K, int a_rows, int h_rows) {
   const int lane = threadIdx.x & 63;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;  // output features per tile
   const int NT = (N + TNO - 1) / TNO;
@@ -508,8 +524,9 @@ __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
   int mt, nt, e, row0, rows;
   if (!tile_of_block<GM>(tt.MT, NT, mt, nt)) return;
   tt.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile<TN, TM, BK, NS, GATHER, ACT, OUT, WP, NWV>(
-      A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO);
+  gemm_tile<TN, TM, BK, NS, GATHER, ACT, OUT, WP, NWV, HP>(
+      A, row_token, W, bias, out, out_row, row_scale, N, K, a_rows, e, row0, rows, nt * TNO,
+      h_rows);
 }
 
 // ---------------------------------------------------------------- loader waves
@@ -522,7 +539,7 @@ __global__ __launch_bounds__(64 * NWV, MINB) void k_grouped_gemm(
 // they have read all of stage kt, and right after it the loaders refill the freed slot with
 // stage kt+NS.  The stage layout, swizzle, MFMA blocks and K order are those of gemm_tile, so
 // every output element sums the same products in the same order (bit-identical results).
-template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP>
+template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP, bool AP = false>
 __device__ __forceinline__ void gemm_tile_loaders(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias, bf16_t* __restrict__ out,
@@ -582,6 +599,17 @@ __device__ __forceinline__ void gemm_tile_loaders(
         const int rt = row < rows ? row_token[row0 + row] : -1;  // -1: a zero row (padding)
         xoff[j] = rt >= 0 && c * 8 < K ? (uint32_t)(rt * K + c * 8) * 2u : kOutOfRange;
       }
+    } else if (AP) {
+      // A in 32-column blocks of a_rows rows (written so by the up-projection): each 32-K
+      // stage of the tile's rows is one contiguous run, row r's piece at (r * 32 + c * 8) * 2
+      // bytes past block k0 / 32 (a_rows * 64 bytes each)
+      xsrc = make_srd(A, (uint32_t)a_rows * (uint32_t)K * 2u);
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int row = (lw * kXLoads + j) * kRowsPerLoad + lrow;
+        const int c = pch ^ swz(row);
+        xoff[j] = row < rows ? (uint32_t)((row0 + row) * 32 + c * 8) * 2u : kOutOfRange;
+      }
     } else {
       xsrc = make_srd(A + (int64_t)row0 * K, (uint32_t)(rows * K * 2));
 #pragma unroll
@@ -591,11 +619,13 @@ __device__ __forceinline__ void gemm_tile_loaders(
         xoff[j] = c * 8 < K ? (uint32_t)(row * K + c * 8) * 2u : kOutOfRange;
       }
     }
+    static_assert(!AP || !GATHER, "packed A rows are read in slot order");
     // stage S into slot S % NS; chunks at or past K (K tail, stages past the last) read as zeros
     auto issue = [&](int S) {
       const int k0 = S * BK;
       const uint32_t kb = (uint32_t)k0 * 2u;
       const uint32_t kw = WP ? (uint32_t)(k0 / kPackK) * (uint32_t)N * (kPackK * 2u) : kb;
+      const uint32_t ka = AP ? (uint32_t)(k0 / kPackK) * (uint32_t)a_rows * (kPackK * 2u) : kb;
       const uint32_t sb = lds0 + (uint32_t)((S % NS) * kStageBytes);
 #pragma unroll
       for (int j = 0; j < kWLoads; ++j) {
@@ -609,7 +639,7 @@ __device__ __forceinline__ void gemm_tile_loaders(
         const int g = lw * kXLoads + j;
         const int c = pch ^ swz(g * kRowsPerLoad + lrow);
         lds_dma16(xsrc, sb + (uint32_t)(TN * BK * 2 + g * 1024),
-                  (k0 + c * 8 < K && xoff[j] != kOutOfRange) ? xoff[j] + kb : kOutOfRange);
+                  (k0 + c * 8 < K && xoff[j] != kOutOfRange) ? xoff[j] + ka : kOutOfRange);
       }
     };
     for (int s0 = 0; s0 < NS; ++s0) issue(s0);
@@ -725,7 +755,7 @@ __device__ __forceinline__ void gemm_tile_loaders(
   }
 }
 
-template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP>
+template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP, bool AP = false>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm_loaders(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W,
@@ -737,8 +767,9 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_loaders(
   int mt, nt, e, row0, rows;
   if (!tile_of_block<8>(tt.MT, NT, mt, nt)) return;  // block-uniform
   tt.locate(offsets, lane, mt, e, row0, rows);
-  gemm_tile_loaders<TN, TM, NS, GATHER, ACT, OUT, WP>(A, row_token, W, bias, out, out_row, row_scale,
-                                                 N, K, a_rows, e, row0, rows, nt * TN);
+  gemm_tile_loaders<TN, TM, NS, GATHER, ACT, OUT, WP, AP>(A, row_token, W, bias, out, out_row,
+                                                     row_scale, N, K, a_rows, e, row0, rows,
+                                                     nt * TN);
 }
 
 // ---------------------------------------------------------------- weight packing
@@ -805,7 +836,7 @@ constexpr size_t tile_lds(int TN, int TM, int BK, int NS, bool out_rows) {
 }
 
 template <int TN, int TM, int BK, int NS, int MINB, bool GATHER, int ACT, int OUT, bool WP,
-          int NWV = 4, int GM = 8>
+          int NWV = 4, int GM = 8, bool HP = false>
 hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                                const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N,
                                int K, int a_rows, int64_t rows_ub, hipStream_t st,
@@ -814,7 +845,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   if (rows_ub <= 0) return hipSuccess;
   constexpr size_t lds = tile_lds(TN, TM, BK, NS, OUT != kOutSlots);
   static_assert(lds * MINB <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, GATHER, ACT, OUT, WP, NWV, GM>;
+  auto kern = k_grouped_gemm<TN, TM, BK, NS, MINB, GATHER, ACT, OUT, WP, NWV, GM, HP>;
   static std::atomic<bool> lds_allowed[kMaxDevices];
   if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
       err != hipSuccess)
@@ -823,17 +854,19 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;
   constexpr int TNO = ACT == kActGated ? TN / 2 : TN;
   const int64_t grid = group_grid<GM>(mt_ub, (N + TNO - 1) / TNO);
+  const int h_rows = HP ? (int)rows_ub : 0;  // packed H: the rows of the output array
   hipEvent_t t0, t1;
   if (take_gemm_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, t0, t1, 0, A,
-                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows);
+                          row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows,
+                          h_rows);
   else
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, A, row_token, offsets, W,
-                       bias, out, out_row, row_scale, E, N, K, a_rows);
+                       bias, out, out_row, row_scale, E, N, K, a_rows, h_rows);
   return hipGetLastError();
 }
 
-template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP>
+template <int TN, int TM, int NS, bool GATHER, int ACT, int OUT, bool WP, bool AP = false>
 hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token,
                                        const int32_t* offsets, const bf16_t* W, const bf16_t* bias,
                                        bf16_t* out, int E, int N, int K, int a_rows,
@@ -845,7 +878,7 @@ hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token
   constexpr size_t tile = (size_t)TM * (TN * 2 + 16) + (OUT != kOutSlots ? (size_t)TM * 4 : 0);
   constexpr size_t lds = ring > tile ? ring : tile;
   static_assert(lds <= 160 * 1024, "LDS per compute unit");
-  auto kern = k_grouped_gemm_loaders<TN, TM, NS, GATHER, ACT, OUT, WP>;
+  auto kern = k_grouped_gemm_loaders<TN, TM, NS, GATHER, ACT, OUT, WP, AP>;
   static std::atomic<bool> lds_allowed[kMaxDevices];
   if (hipError_t err = allow_dynamic_lds((const void*)kern, (int)lds, lds_allowed);
       err != hipSuccess)
@@ -883,11 +916,23 @@ static bool skinny(const moe_shape& s, int64_t rows_ub) {
   return rows_ub <= (int64_t)64 * s.n_experts;
 }
 
+// H (GEMM 1's output, GEMM 2's input, slot order) is stored in 32-column blocks, [d_ff / 32,
+// rows, 32], whenever the large tiles run: the down-projection's loader waves then read each
+// 32-K stage of a token tile as one contiguous 16 KiB run instead of 64-byte pieces of rows
+// d_ff * 2 bytes apart (same bits; stage times in the layer: GEMM 2 mid 180 -> 161 us, 64-expert
+// fine 271 -> 235 us, collapse 5.23 -> 4.73 ms, GEMM 1 unchanged by its block-ordered stores).
+// Needs d_ff a multiple of 32 and H within a buffer resource's 32-bit range; the
+// two GEMMs of a call see the same shape and row bound, so they agree on the layout.
+static bool h_packed(const moe_shape& s, int64_t rows_ub) {
+  return s.dtype == MOE_BF16 && !skinny(s, rows_ub) && s.d_ff % 32 == 0 &&
+         rows_ub * (int64_t)s.d_ff * 2 < ((int64_t)1 << 31);
+}
+
 namespace {
 
 // The tile configurations: large batches, and decode-sized ones (skinny); the gated expert's
 // tiles hold a gate row and an up row per output feature.
-template <int ACT, int OUT, bool GATHER, bool WP>
+template <int ACT, int OUT, bool GATHER, bool WP, bool HP = false>
 hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const int32_t* offsets,
                     const bf16_t* W, const bf16_t* bias, bf16_t* out, int E, int N, int K,
                     int a_rows, int64_t rows_ub, hipStream_t st, const int32_t* out_row,
@@ -917,31 +962,44 @@ hipError_t run_gemm(bool small, const bf16_t* A, const int32_t* row_token, const
   // features x 128 slots instead: half the token tile, so less padding in each expert's last
   // tile (lab, same bits: 64-expert fine layer 357 -> 311 us; mid 240 -> 246 us and collapse
   // 5.16 -> 5.80 ms, so only there).
+  // HP: H in 32-column blocks (written by the up-projection, read by the down-projection)
   if constexpr (ACT == kActNone) {
-    return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP>(
+    return launch_grouped_gemm_loaders<256, 192, 4, GATHER, ACT, OUT, WP, HP && !GATHER>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   } else {
     if (E >= 32)
-      return launch_grouped_gemm<512, 128, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4>(
+      return launch_grouped_gemm<512, 128, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4, HP>(
           A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
-    return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4>(
+    return launch_grouped_gemm<256, 256, 32, 4, 1, GATHER, ACT, OUT, WP, 8, 4, HP>(
         A, row_token, offsets, W, bias, out, E, N, K, a_rows, rows_ub, st, out_row, row_scale);
   }
 }
 
-// the weight layout of the shape picks the kernel
+// the weight layout of the shape picks the kernel; hp: H in 32-column blocks (slot order only)
 template <int ACT, int OUT, bool GATHER>
 hipError_t gemm(const moe_shape& s, const void* A, const int32_t* row_token,
                 const int32_t* offsets, const void* W, const void* bias, void* out, int N, int K,
                 int a_rows, int64_t rows_ub, hipStream_t st, const int32_t* out_row = nullptr,
-                const float* row_scale = nullptr) {
+                const float* row_scale = nullptr, bool hp = false) {
   if (s.dtype != MOE_BF16) return hipErrorInvalidValue;
   const bool small = skinny(s, rows_ub);
   auto a = (const bf16_t*)A;
   auto w = (const bf16_t*)W;
   auto b = (const bf16_t*)bias;
   auto o = (bf16_t*)out;
-  if (s.weight_layout == MOE_WEIGHTS_PACKED)
+  const bool packed_w = s.weight_layout == MOE_WEIGHTS_PACKED;
+  if constexpr (OUT == kOutSlots) {
+    if (hp && !small) {
+      if (packed_w)
+        return run_gemm<ACT, OUT, GATHER, true, true>(small, a, row_token, offsets, w, b, o,
+                                                      s.n_experts, N, K, a_rows, rows_ub, st,
+                                                      out_row, row_scale);
+      return run_gemm<ACT, OUT, GATHER, false, true>(small, a, row_token, offsets, w, b, o,
+                                                     s.n_experts, N, K, a_rows, rows_ub, st,
+                                                     out_row, row_scale);
+    }
+  }
+  if (packed_w)
     return run_gemm<ACT, OUT, GATHER, true>(small, a, row_token, offsets, w, b, o, s.n_experts, N,
                                             K, a_rows, rows_ub, st, out_row, row_scale);
   return run_gemm<ACT, OUT, GATHER, false>(small, a, row_token, offsets, w, b, o, s.n_experts, N,
@@ -956,7 +1014,8 @@ hipError_t launch_ffn_up(const moe_shape& s, const void* x, const int32_t* row_t
   if (s.dtype != MOE_BF16)
     return launch_ffn_up_f32(s, x, row_token, offsets, w1, b1, h, rows_ub, st);
   return gemm<kActSilu, kOutSlots, true>(s, x, row_token, offsets, w1, b1, h, s.d_ff, s.d_model,
-                                         (int)s.T, rows_ub, st);
+                                         (int)s.T, rows_ub, st, nullptr, nullptr,
+                                         h_packed(s, rows_ub));
 }
 
 hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* offsets,
@@ -964,24 +1023,27 @@ hipError_t launch_ffn_down(const moe_shape& s, const void* h, const int32_t* off
                            hipStream_t st) {
   if (s.dtype != MOE_BF16) return launch_ffn_down_f32(s, h, offsets, w2, b2, y, rows_ub, st);
   return gemm<kActNone, kOutSlots, false>(s, h, nullptr, offsets, w2, b2, y, s.d_model, s.d_ff,
-                                          (int)rows_ub, rows_ub, st);
+                                          (int)rows_ub, rows_ub, st, nullptr, nullptr,
+                                          h_packed(s, rows_ub));
 }
 
 // Gated expert (fused-MoE flow diagram, GEMM 1 -> SiLU x mul -> GEMM 2): GEMM 1 over the
 // [2 d_ff, d_model] weights of each expert, gate rows first, with SiLU(gate) * up fused into
-// the epilogue; no biases.  Output H [rows, d_ff].
+// the epilogue; no biases.  Output H: rows x d_ff in slot order (32-column blocks, see h_packed).
 hipError_t launch_ffn_up_gated(const moe_shape& s, const void* x, const int32_t* row_token,
                                const int32_t* offsets, const void* w13, void* h, int64_t rows_ub,
                                hipStream_t st) {
   return gemm<kActGated, kOutSlots, true>(s, x, row_token, offsets, w13, nullptr, h, s.d_ff,
-                                          s.d_model, (int)s.T, rows_ub, st);
+                                          s.d_model, (int)s.T, rows_ub, st, nullptr, nullptr,
+                                          h_packed(s, rows_ub));
 }
 
 // GEMM 2 without bias (gated expert): Y = H W2^T
 hipError_t launch_ffn_down_nobias(const moe_shape& s, const void* h, const int32_t* offsets,
                                   const void* w2, void* y, int64_t rows_ub, hipStream_t st) {
   return gemm<kActNone, kOutSlots, false>(s, h, nullptr, offsets, w2, nullptr, y, s.d_model,
-                                          s.d_ff, (int)rows_ub, rows_ub, st);
+                                          s.d_ff, (int)rows_ub, rows_ub, st, nullptr, nullptr,
+                                          h_packed(s, rows_ub));
 }
 
 // ---------------------------------------------------------------- dropless pair order
