@@ -104,9 +104,9 @@ def traffic_from_profiles(kernel_tag: str, config_key: str):
 
 def traffic_live(args):
     """HBM bytes per launch of the two expert GEMMs, measured on this machine: two child runs
-    of this same command under rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE; one warm-up and 3
-    steps, plus a 1 GiB device copy as the calibration), started before this process touches
-    the GPU.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads
+    of this same command under rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE; 8 warm-up and 3
+    timed steps, plus a 1 GiB device copy as the calibration), started before this process
+    touches the GPU.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads
     for the copy.  Returns {"expert_up": bytes, "expert_down": bytes, ...} or None when
     rocprofv3 is missing, a run fails or times out (its process group is then killed)."""
     prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
@@ -120,7 +120,7 @@ def traffic_live(args):
             cmd = [prof, "--pmc", ctr, "-f", "csv", "-d", out, "-o", "run", "--", sys.executable,
                    os.path.abspath(__file__), "--config", args.config, "--layout", args.layout,
                    "--weights", args.weights, "--steps", "3", "--warmup", "1",
-                   "--no-cpu-baseline", "--copy-probe", "--traffic", "none"]
+                   "--warmup-ms", "0", "--no-cpu-baseline", "--copy-probe", "--traffic", "none"]
             log(f"[bench] HBM counters: {ctr} child run")
             # the child's progress lines go to stderr; its JSON line is dropped
             child = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, start_new_session=True,
