@@ -50,3 +50,31 @@ def test_pmc_gemm_traffic_missing_copy_or_gemm_is_none():
     assert b.pmc_gemm_traffic({"FETCH_SIZE": no_copy, "WRITE_SIZE": rows}) is None
     no_gemm = [r for r in rows if "k_grouped_gemm" not in r[1]]
     assert b.pmc_gemm_traffic({"FETCH_SIZE": rows, "WRITE_SIZE": no_gemm}) is None
+
+
+def test_warm_up_runs_min_steps_then_until_the_time_floor():
+    """bench.warm_up: at least min_steps steps, then on (in groups of 8, each ended by a sync)
+    until min_ms of wall time have passed."""
+    import time
+    b = _bench()
+    calls = {"step": 0, "sync": 0}
+
+    def step():
+        calls["step"] += 1
+
+    def sync():
+        calls["sync"] += 1
+
+    r = b.warm_up(step, 5, 0.0, sync)  # no time floor: the first multiple of 8 past 5 steps
+    assert r["steps"] == calls["step"] == 8 and calls["sync"] >= 1
+
+    calls["step"] = 0
+    t0 = time.perf_counter()
+
+    def slow_step():
+        calls["step"] += 1
+        time.sleep(0.002)
+
+    r = b.warm_up(slow_step, 1, 30.0, sync)
+    assert (time.perf_counter() - t0) * 1e3 >= 30.0 and r["ms"] >= 30.0
+    assert r["steps"] == calls["step"] and r["steps"] % 8 == 0
