@@ -358,6 +358,41 @@ __device__ __forceinline__ void gemm_tile(
                                                               acc[i_][j_], 0, 0, 0);           \
   } while (0)
 
+// Fragment q of 16-K step KK of stage S into register set F (q < FN: weight block q, else
+// slot block q - FN).
+#define MOE_READ_FRAG(S, KK, F, q)                                                             \
+  do {                                                                                         \
+    const uint4* sb_ = smem + ((S) % NS) * (kStageBytes / 16);                                 \
+    const int ch_ = (KK) * 2 + half;                                                           \
+    if ((q) < FN) {                                                                            \
+      const int row_ = wn * (TN / WN) + (q) * 32 + r32;                                        \
+      fa[F][(q)] = as_bf16x8(sb_[row_ * kChunks + (ch_ ^ swz(row_))]);                         \
+    } else {                                                                                   \
+      const int row_ = wm * (TM / WM) + ((q) - FN) * 32 + r32;                                 \
+      fb[F][(q) - FN] = as_bf16x8(sb_[TN * kChunks + row_ * kChunks + (ch_ ^ swz(row_))]);     \
+    }                                                                                          \
+  } while (0)
+
+// MFMA step F with the fragments of (S, KK) read into set G between the MFMAs, one after each
+// of the first FN + FM MFMAs, and (LS >= 0) the loads of stage LS spread over the step as in
+// MOE_MFMA_STEP_ISSUE.  Without the scheduling barriers the compiler issues all the reads
+// ahead of the MFMAs, and the LDS then takes each wave's fragment reads in one burst.
+#define MOE_MFMA_STEP_READ(F, S, KK, G, LS)                                                    \
+  do {                                                                                         \
+    MOE_STAGE_BASE((LS) < 0 ? 0 : (LS));                                                       \
+    _Pragma("unroll") for (int m_ = 0; m_ < FN * FM; ++m_) {                                   \
+      const int i_ = m_ / FM, j_ = m_ % FM;                                                    \
+      acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i_], fb[F][j_], acc[i_][j_], \
+                                                            0, 0, 0);                          \
+      if (m_ < FN + FM) MOE_READ_FRAG(S, KK, G, m_);                                           \
+      if ((LS) >= 0) {                                                                         \
+        _Pragma("unroll") for (int q_ = 0; q_ < kLoads; ++q_)                                  \
+          if (q_ * FN * FM / kLoads == m_) MOE_ISSUE_LOAD(q_);                                 \
+      }                                                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+    }                                                                                          \
+  } while (0)
+
 // MFMA step F with the loads of stage S spread between the MFMAs (load q after MFMA
 // floor(q * FN * FM / kLoads)), so that the wave never stalls on the load queue while its
 // matrix core has nothing queued.  The scheduling barriers keep this order.
@@ -394,11 +429,19 @@ __device__ __forceinline__ void gemm_tile(
   __syncthreads();
   MOE_READ_FRAGS(0, 0, 0);
 
+  // one fragment read between consecutive MFMAs needs at least as many MFMAs as reads per step
+  constexpr bool kSpread = FN * FM >= FN + FM;
+  static_assert(KS % 2 == 0, "the last step of a stage reads into set 0");
   for (int kt = 0; kt < nk; ++kt) {
     // 16-K steps 0 .. KS-2 of stage kt; fragments of the next step are read during each
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
-      if (kk % 2 == 0) {
+      if constexpr (kSpread) {
+        if (kk % 2 == 0)
+          MOE_MFMA_STEP_READ(0, kt, kk + 1, 1, -1);
+        else
+          MOE_MFMA_STEP_READ(1, kt, kk + 1, 0, -1);
+      } else if (kk % 2 == 0) {
         MOE_READ_FRAGS(kt, kk + 1, 1);
         MOE_MFMA_STEP(0);
       } else {
@@ -410,9 +453,14 @@ __device__ __forceinline__ void gemm_tile(
     // after the barrier every wave has read all of stage kt
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kLoads));
     __syncthreads();
-    MOE_READ_FRAGS(kt + 1, 0, 0);  // past the last stage this reads a slot nobody uses
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_MFMA_STEP_ISSUE((KS - 1) % 2, kt + NS);
+    // past the last stage the reads of stage kt+1 touch a slot nobody uses
+    if constexpr (kSpread) {
+      MOE_MFMA_STEP_READ(1, kt + 1, 0, 0, kt + NS);
+    } else {
+      MOE_READ_FRAGS(kt + 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_MFMA_STEP_ISSUE((KS - 1) % 2, kt + NS);
+    }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the zero-fill loads land before the LDS reuse
 #undef MOE_STAGE_BASE
@@ -421,6 +469,8 @@ __device__ __forceinline__ void gemm_tile(
 #undef MOE_READ_FRAGS
 #undef MOE_MFMA_STEP
 #undef MOE_MFMA_STEP_ISSUE
+#undef MOE_READ_FRAG
+#undef MOE_MFMA_STEP_READ
 
   // ---- epilogue.  Lane (r32, half) holds, for block (i, j), features
   // 32 i + 8 (v / 4) + 4 half + v % 4 of slot column 32 j + r32.  Bias + activation (+ row
