@@ -411,6 +411,116 @@ __global__ __launch_bounds__(64 * NW) void k_route_mfma4(
   finish_e8<TT>(logit, b_router != nullptr, bias_e, tok0, T, E, k, NT, ids, gates, logits_out);
 }
 
+// The same 16-token x 8-expert tile with the four blocks of v_mfma_f64_4x4x4f64 on four
+// slices of d instead of four token groups.  Block b's 4 x 4 product then takes tokens 4 tg ..
+// 4 tg + 3 and experts 4 eg .. 4 eg + 3 (one instruction per token group tg and expert group eg)
+// over the columns of slice b, and lane l = 16 g + 4 b + r loads chunk 16 cq + 4 b + g of token
+// 4 tg + r and of expert 4 eg + r.  No two lanes load or widen the same router weights (in
+// k_route_mfma4 the four blocks share them: twice as many widenings per product), and a wave
+// covers 128 columns per chunk quad.  MFMA step s pairs column s of both chunks, as there.  Lane
+// (g, b, r) ends with slice b's partial logit of token 4 tg + g, expert 4 eg + r; the four slices
+// are added over the lanes b = 0 .. 3 (xor 4, then xor 8: every lane of the four gets the same
+// sum), then the waves' tiles in wave order.  Only the summation order differs from
+// k_route_mfma4.
+template <typename TIn, int NW, int PF>
+__global__ __launch_bounds__(64 * NW) void k_route_mfma4k(
+    const TIn* __restrict__ x, const TIn* __restrict__ w, const float* __restrict__ b_router,
+    int64_t T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates,
+    float* __restrict__ logits_out) {
+  constexpr int TT = 16, NT = 64 * NW;
+  __shared__ double part[NW > 1 ? NW - 1 : 1][8][64];  // waves 1 .. NW - 1: partial tiles
+  __shared__ double logit[8 * TT];                     // [expert][token of the block]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, b = (lane >> 2) & 3, r = lane & 3;
+  const int64_t tok0 = (int64_t)blockIdx.x * TT;
+  const int d8 = (d + 7) / 8, nq = (d8 + 15) / 16;
+  const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x, (uint32_t)(T * d * (int64_t)sizeof(TIn)));
+  const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(w, (uint32_t)((int64_t)E * d * sizeof(TIn)));
+
+  double acc[4][2];  // [token group][expert group]
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg) acc[tg][0] = acc[tg][1] = 0.0;
+  Chunk8<TIn> xr[PF][4], wr[PF][2];
+  auto load = [&](int p, int cq) {
+    const int c = cq * 16 + b * 4 + g;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int64_t t = tok0 + 4 * tg + r;
+      xr[p][tg].load(xs, cq < nq && t < T, t, c, d);
+    }
+#pragma unroll
+    for (int eg = 0; eg < 2; ++eg) {
+      const int e = 4 * eg + r;
+      wr[p][eg].load(ws, cq < nq && e < E, e, c, d);
+    }
+  };
+  // this wave's n_w quads wave, wave + NW, ..., walked from a per-block point on (as in
+  // k_route_mfma4); indices past n_w give quad nq, whose loads read zeros
+  const int n_w = wave < nq ? (nq - wave + NW - 1) / NW : 0;
+  const int j0 = n_w ? (int)(blockIdx.x % (unsigned)n_w) : 0;
+  auto quad_of = [&](int i) { return i < n_w ? wave + NW * ((j0 + i) % n_w) : nq; };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(p, quad_of(p));
+  const float bias_e =
+      b_router && (int)(threadIdx.x & 7) < E ? b_router[threadIdx.x & 7] : 0.0f;
+  for (int i0 = 0; i0 < n_w; i0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      double xa[4][8], wb[2][8];
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) xr[p][tg].widen(xa[tg]);
+      wr[p][0].widen(wb[0]);
+      wr[p][1].widen(wb[1]);
+      load(p, quad_of(i0 + p + PF));
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+          for (int eg = 0; eg < 2; ++eg)
+            acc[tg][eg] =
+                __builtin_amdgcn_mfma_f64_4x4x4f64(xa[tg][s8], wb[eg][s8], acc[tg][eg], 0, 0, 0);
+    }
+  }
+  // slices: lanes b = 0 .. 3 of (g, r)
+  auto dxor = [](double v, int st) {
+    return __longlong_as_double((long long)xor_partner((uint64_t)__double_as_longlong(v), st));
+  };
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+    for (int eg = 0; eg < 2; ++eg) {
+      acc[tg][eg] += dxor(acc[tg][eg], 4);
+      acc[tg][eg] += dxor(acc[tg][eg], 8);
+    }
+  if (wave > 0) {
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int eg = 0; eg < 2; ++eg) part[wave - 1][tg * 2 + eg][lane] = acc[tg][eg];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int ww = 1; ww < NW; ++ww)
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+        for (int eg = 0; eg < 2; ++eg) acc[tg][eg] += part[ww - 1][tg * 2 + eg][lane];
+    if (b == 0) {
+#pragma unroll
+      for (int eg = 0; eg < 2; ++eg) {
+        const int e = 4 * eg + r;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+          if (e < E) logit[e * TT + 4 * tg + g] = acc[tg][eg];
+      }
+    }
+  }
+  __syncthreads();
+  finish_e8<TT>(logit, b_router != nullptr, bias_e, tok0, T, E, k, NT, ids, gates, logits_out);
+}
+
 namespace {
 
 template <typename TIn, int EBG, int NW>
@@ -461,12 +571,19 @@ hipError_t route_any(const moe_shape& s, const TIn* x, const TIn* w, const float
                      int32_t* ids, float* gates, float* logits, hipStream_t st) {
   // At most 8 experts: 16-token x 8-expert tiles, 4-wave blocks, two chunk quads in flight per
   // wave.  From 16384 tokens a lane takes 4 row groups (64 tokens per block: the weight loads
-  // and widenings are shared by more tiles); smaller batches one (16 per block, more blocks).
-  // Lab, same routing: collapse layer 97 us with the 16 x 16 tiles, 72 to 78 us with 8-token x
-  // 8-expert tiles (two lanes loading each x chunk), 56 us with these; mid 13.0 -> 12.3 us.
+  // and widenings are shared by more tiles); smaller batches take 16 tokens per block (more
+  // blocks) with the four MFMA blocks on four slices of d, so that no two lanes widen the same
+  // weights (k_route_mfma4k).  Lab, same routing: collapse layer 97 us with the 16 x 16 tiles,
+  // 72 to 78 us with 8-token x 8-expert tiles (two lanes loading each x chunk), 56 us with these;
+  // mid 13.0 -> 12.3 us.  Same-box stage times of the d slices against the token groups: mid
+  // 13.6-13.8 -> 12.1-12.8 us, decode (64 tokens) 11.6-11.7 -> 9.6-9.9 us.
   if (s.n_experts <= 8) {
     if (s.T >= 16384) return route4_launch<TIn, 4, 4>(s, x, w, b_router, ids, gates, logits, st);
-    return route4_launch<TIn, 1, 4>(s, x, w, b_router, ids, gates, logits, st);
+    constexpr int NW = 4, PF = 2;
+    hipLaunchKernelGGL((k_route_mfma4k<TIn, NW, PF>), dim3((unsigned)((s.T + 15) / 16)),
+                       dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts,
+                       s.top_k, ids, gates, logits);
+    return hipGetLastError();
   }
   if (s.n_experts <= 16) return route_waves<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
   return route_waves<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);
