@@ -560,6 +560,13 @@ ROUTE_SHAPES = [
     (16384, 512, 1, 1, "bf16"),
     (20000, 264, 8, 8, "bf16"),
     (16400, 24, 6, 2, "f32"),
+    # at most 8 experts below 16384 tokens (MFMA blocks on four slices of d): several 128-column
+    # quads per wave with a partial last quad (d 2056: 17 quads over 4 waves), a d with a
+    # partial last chunk in fp32, fewer experts than a group, a single token
+    (1001, 2056, 8, 2, "bf16"),
+    (3000, 1000, 5, 3, "bf16"),
+    (777, 130, 8, 4, "f32"),
+    (1, 512, 8, 2, "bf16"),
 ]
 
 
