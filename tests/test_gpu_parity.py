@@ -247,6 +247,11 @@ SMALL = [
     (333, 24, 40, 64, 8, 1.0, "f32"),
     (200, 16, 16, 200, 3, 2.0, "f32"),
     (8200, 8, 12, 24, 2, 1.0, "f32"),
+    # the layer's one-launch mid-size dispatch: just past the one-workgroup limit (3 runs, the
+    # last of 2 keys), a single expert with half the assignments dropped, 256 experts
+    (513, 8, 8, 4, 2, 1.0, "bf16"),
+    (1030, 8, 16, 1, 1, 0.5, "f32"),
+    (3000, 16, 24, 256, 4, 1.0, "bf16"),
 ]
 
 
