@@ -10,6 +10,10 @@ router, dispatch (capacity cut, slot assignment), expert GEMM 1 (+bias, SiLU), e
                  steps record themselves (moe_set_gemm_timing, hipExtLaunchKernel), so the
                  steps `value` is timed on carry no extra marker between launches
   cpu_baseline   the CPU oracle timed on this host on the same workload (a baseline only)
+  route_kernel_GBps, combine_kernel_GBps
+                 the router's and the combine's bytes over their own kernel time (events that
+                 their launches record, moe_set_stage_timing), from a run of plain steps after
+                 the timed ones; route_GBps / combine_GBps use the stage events (gaps included)
 Before the timed steps: at least --warmup untimed steps, continued until --warmup-ms (100 ms)
 of wall time have passed, since the GPU reaches its steady clocks only after about 30 ms of
 sustained load.  roofline.traffic: HBM bytes per launch of the dominant GEMM from two
@@ -619,6 +623,19 @@ def main():
     for i in range(args.steps):
         step_profiled(evsets[i])
     torch.cuda.synchronize()
+    # the router's and the combine's own kernels, timed by their launches (moe_set_stage_timing,
+    # hipExtLaunchKernel) over a third run of plain steps: the stage events above include
+    # launch gaps
+    route_kernel_ms = combine_kernel_ms = None
+    if not dropless:
+        kev = [new_events(4) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            B.moe_set_stage_timing(kev[i])
+            step()
+        torch.cuda.synchronize()
+        route_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+        combine_kernel_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in kev]))
 
     stage_ms = {s: float(np.mean([evs[j].elapsed_time(evs[j + 1]) for evs in evsets]))
                 for j, s in enumerate(STAGES)}
@@ -779,6 +796,14 @@ def main():
         "event_step_ms": step_ms,
         "route_GBps": route_bytes / (stage_ms["route"] / 1e3) / 1e9,
         "combine_GBps": combine_bytes / (stage_ms["combine"] / 1e3) / 1e9,
+        # the same bytes over the kernels' own durations (recorded by their launches in a third
+        # run of plain steps)
+        "route_kernel_ms": route_kernel_ms,
+        "route_kernel_GBps": (route_bytes / (route_kernel_ms / 1e3) / 1e9
+                              if route_kernel_ms else None),
+        "combine_kernel_ms": combine_kernel_ms,
+        "combine_kernel_GBps": (combine_bytes / (combine_kernel_ms / 1e3) / 1e9
+                                if combine_kernel_ms else None),
         "n_kept": n_kept,
         "expert_rows_computed": wl.n_experts * cap if padded else n_kept,
         "combine_stage": "moe_sum over pair rows" if dropless else "combine (slot gather)",

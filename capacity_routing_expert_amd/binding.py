@@ -31,7 +31,8 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_max_kept_rows", "moe_stat
            "moe_dispatch_pairs", "moe_expert_ffn_pairs", "moe_sum", "moe_layer_forward_dropless",
            "moe_layer_forward_dropless_gated", "moe_workspace_bytes_batches",
            "moe_schedule_batches", "moe_layer_forward_batches", "moe_packed_weights_bytes",
-           "moe_pack_weights", "moe_set_gemm_timing", "moe_layer_forward_noalloc")
+           "moe_pack_weights", "moe_set_gemm_timing", "moe_set_stage_timing",
+           "moe_layer_forward_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_batches.argtypes = [SP, I32, I32] + [P] * 13 + [SZ, P, P]
         L.moe_set_gemm_timing.argtypes = [P]
         L.moe_set_gemm_timing.restype = I32
+        L.moe_set_stage_timing.argtypes = [P]
+        L.moe_set_stage_timing.restype = I32
         for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                      "moe_layer_forward", "moe_layer_forward_profiled", "moe_layer_forward_padded",
                      "moe_layer_forward_noalloc",
@@ -323,6 +326,19 @@ def moe_set_gemm_timing(events):
     handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event if ev is not None else None)
                                       for ev in events])
     _check(lib().moe_set_gemm_timing(handles), "moe_set_gemm_timing")
+
+
+def moe_set_stage_timing(events):
+    """Arms kernel timing of the router and the combine for the next layer call on this thread:
+    `events` are 4 torch.cuda.Event(enable_timing=True) objects (or None in place of one
+    kernel's pair), already recorded once, receiving the router kernel's start and end and the
+    combine kernel's start and end; None disarms."""
+    if events is None:
+        _check(lib().moe_set_stage_timing(None), "moe_set_stage_timing")
+        return
+    handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(ev.cuda_event if ev is not None else None)
+                                      for ev in events])
+    _check(lib().moe_set_stage_timing(handles), "moe_set_stage_timing")
 
 
 def moe_layer_forward_padded(shape, x, w_router, b_router, w1, b1, w2, b2, out, topk_ids=None,

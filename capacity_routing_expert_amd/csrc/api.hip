@@ -46,6 +46,19 @@ bool take_timing(hipEvent_t (&ev)[4]) {
   return true;
 }
 
+// Router and combine kernel timing armed by moe_set_stage_timing for the next layer call on this
+// thread: router start / stop, combine start / stop.
+thread_local hipEvent_t g_stage_timing[4] = {nullptr, nullptr, nullptr, nullptr};
+
+bool take_stage_timing(hipEvent_t (&ev)[4]) {
+  if (!g_stage_timing[0] && !g_stage_timing[2]) return false;
+  for (int i = 0; i < 4; ++i) {
+    ev[i] = g_stage_timing[i];
+    g_stage_timing[i] = nullptr;
+  }
+  return true;
+}
+
 // The events of one GEMM (pair 0: up-projection, 1: down-projection), or NULL if not timed.
 const hipEvent_t* timing_pair(bool timed, const hipEvent_t (&ev)[4], int pair) {
   return timed && ev[2 * pair] ? ev + 2 * pair : nullptr;
@@ -61,15 +74,15 @@ moe_status record_now(const hipEvent_t* ev, int n, hipStream_t st) {
   return MOE_OK;
 }
 
-// One expert GEMM launch, with its kernel start and stop recorded in ev[0], ev[1] when `ev` is
-// given (the events ride on the launch itself); a launch that turns out empty records them
-// back to back.
+// One timed launch (an expert GEMM, the router or the combine), with its kernel start and stop
+// recorded in ev[0], ev[1] when `ev` is given (the events ride on the launch itself); a launch
+// that turns out empty records them back to back.
 template <typename F>
-moe_status run_gemm_stage(const hipEvent_t* ev, hipStream_t st, const char* what, F launch) {
-  if (ev) arm_gemm_events(ev[0], ev[1]);
+moe_status run_timed_stage(const hipEvent_t* ev, hipStream_t st, const char* what, F launch) {
+  if (ev) arm_launch_events(ev[0], ev[1]);
   const hipError_t err = launch();
   hipEvent_t a, b;
-  const bool unused = ev && take_gemm_events(&a, &b);  // not taken: nothing was launched
+  const bool unused = ev && take_launch_events(&a, &b);  // not taken: nothing was launched
   if (err != hipSuccess) return device_error(err, what);
   return unused ? record_now(ev, 2, st) : MOE_OK;
 }
@@ -242,8 +255,9 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
                          int32_t* slot_of, uint8_t* drop_mask, int32_t* expert_counts, void* ws,
                          size_t ws_bytes, hipStream_t st, moe_event_t const* events,
                          bool padded = false, void* y_rows = nullptr, bool gated = false) {
-  hipEvent_t tev[4];
-  const bool timed = take_timing(tev);  // consumed by this call even if it fails
+  hipEvent_t tev[4], sev[4];
+  const bool timed = take_timing(tev);  // both consumed by this call even if it fails
+  const bool stimed = take_stage_timing(sev);
   MOE_TRY(check_shape(shape));
   const moe_shape& s = *shape;
   auto rec = [&](int i) -> moe_status {
@@ -253,6 +267,7 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   };
   if (s.T == 0) {  // empty batch: nothing to check or enqueue
     for (int i = 0; i < 6; ++i) MOE_TRY(rec(i));
+    if (stimed) MOE_TRY(record_now(sev, 4, st));
     return timed ? record_now(tev, 4, st) : MOE_OK;
   }
   if (gated) {
@@ -280,7 +295,9 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
   int64_t rows = max_rows(s);
 
   MOE_TRY(rec(0));
-  MOE_TRY(do_route(s, x, w_router, b_router, ids, gates, nullptr, st));
+  MOE_TRY(run_timed_stage(timing_pair(stimed, sev, 0), st, "route", [&] {
+    return launch_route(s, x, w_router, b_router, ids, gates, nullptr, st);
+  }));
   MOE_TRY(rec(1));
   MOE_TRY(do_dispatch(s, ids, gates, counts, offsets, slots, row_token, drop, ws, st));
   if (padded) {  // every expert's buffer is computed whole: rows e * cap .. (e + 1) * cap - 1
@@ -293,18 +310,18 @@ moe_status layer_forward(const moe_shape* shape, const void* x, const void* w_ro
     rows = (int64_t)s.n_experts * s.capacity;
   }
   MOE_TRY(rec(2));
-  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
+  MOE_TRY(run_timed_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
     return gated ? launch_ffn_up_gated(s, x, row_token, offsets, w1, h, rows, st)
                  : launch_ffn_up(s, x, row_token, offsets, w1, b1, h, rows, st);
   }));
   MOE_TRY(rec(3));
-  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
+  MOE_TRY(run_timed_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
     return gated ? launch_ffn_down_nobias(s, h, offsets, w2, y, rows, st)
                  : launch_ffn_down(s, h, offsets, w2, b2, y, rows, st);
   }));
   MOE_TRY(rec(4));
-  hipError_t err = launch_combine(s, x, gates, slots, y, out, st);
-  if (err != hipSuccess) return device_error(err, "combine");
+  MOE_TRY(run_timed_stage(timing_pair(stimed, sev, 1), st, "combine",
+                          [&] { return launch_combine(s, x, gates, slots, y, out, st); }));
   MOE_TRY(rec(5));
   return MOE_OK;
 }
@@ -326,7 +343,7 @@ moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pa
                      bool gated, void* h, void* pair_rows, hipStream_t st,
                      moe_event_t const* events, const hipEvent_t* tev) {
   const int64_t rows = s.T * (int64_t)s.top_k;
-  MOE_TRY(run_gemm_stage(tev && tev[0] ? tev : nullptr, st,
+  MOE_TRY(run_timed_stage(tev && tev[0] ? tev : nullptr, st,
                          "expert up-projection (pair order)", [&] {
     return launch_ffn_up_pairs(s, x, row_token, sorted_pairs, offsets, w1, gated ? nullptr : b1,
                                h, rows, gated, st);
@@ -334,7 +351,7 @@ moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pa
   hipError_t err;
   if (events && (err = hipEventRecord((hipEvent_t)events[3], st)) != hipSuccess)
     return device_error(err, "hipEventRecord");
-  MOE_TRY(run_gemm_stage(tev && tev[2] ? tev + 2 : nullptr, st,
+  MOE_TRY(run_timed_stage(tev && tev[2] ? tev + 2 : nullptr, st,
                          "expert down-projection (pair order)", [&] {
     return launch_ffn_down_pairs(s, h, sorted_pairs, offsets, w2, gated ? nullptr : b2, weights,
                                  pair_rows, rows, st);
@@ -754,10 +771,10 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   if (max_rows(s) == 0) return timed ? record_now(tev, 4, st) : MOE_OK;
   const Workspace L = layout(s);
   void* h = at<void>(ws, L.h);
-  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
+  MOE_TRY(run_timed_stage(timing_pair(timed, tev, 0), st, "expert up-projection", [&] {
     return launch_ffn_up(s, x, row_token, expert_offsets, w1, b1, h, max_rows(s), st);
   }));
-  MOE_TRY(run_gemm_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
+  MOE_TRY(run_timed_stage(timing_pair(timed, tev, 1), st, "expert down-projection", [&] {
     return launch_ffn_down(s, h, expert_offsets, w2, b2, y_rows, max_rows(s), st);
   }));
   return MOE_OK;
@@ -822,6 +839,21 @@ moe_status moe_set_gemm_timing(const moe_event_t* events) {
   if (!events[0] && !events[2])
     return fail(MOE_ERR_INVALID_ARGUMENT, "events: no GEMM to time (all four NULL)");
   for (int i = 0; i < 4; ++i) g_timing[i] = (hipEvent_t)events[i];
+  return MOE_OK;
+}
+
+moe_status moe_set_stage_timing(const moe_event_t* events) {
+  if (!events) {
+    for (int i = 0; i < 4; ++i) g_stage_timing[i] = nullptr;
+    return MOE_OK;
+  }
+  for (int p = 0; p < 2; ++p)
+    if (!events[2 * p] != !events[2 * p + 1])
+      return fail(MOE_ERR_INVALID_ARGUMENT, "events[%d] and events[%d]: both or neither NULL",
+                  2 * p, 2 * p + 1);
+  if (!events[0] && !events[2])
+    return fail(MOE_ERR_INVALID_ARGUMENT, "events: no kernel to time (all four NULL)");
+  for (int i = 0; i < 4; ++i) g_stage_timing[i] = (hipEvent_t)events[i];
   return MOE_OK;
 }
 

@@ -318,12 +318,10 @@ hipError_t launch_combine(const moe_shape& s, const void* x, const float* gates,
                           const int32_t* slot_of, const void* y, void* out, hipStream_t st) {
   const int64_t grid = (s.T + 3) / 4;
   if (s.dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_combine_bf16, dim3((unsigned)grid), dim3(256), 0, st, (const bf16_t*)x,
-                       gates, slot_of, (const bf16_t*)y, (bf16_t*)out, s.T, s.d_model, s.top_k);
-  else
-    hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)grid), dim3(256), 0, st, (const float*)x,
-                       gates, slot_of, (const float*)y, (float*)out, s.T, s.d_model, s.top_k);
-  return hipGetLastError();
+    return launch_timed(k_combine_bf16, dim3((unsigned)grid), dim3(256), 0, st, (const bf16_t*)x,
+                        gates, slot_of, (const bf16_t*)y, (bf16_t*)out, s.T, s.d_model, s.top_k);
+  return launch_timed(k_combine_f32, dim3((unsigned)grid), dim3(256), 0, st, (const float*)x,
+                      gates, slot_of, (const float*)y, (float*)out, s.T, s.d_model, s.top_k);
 }
 
 }  // namespace moe

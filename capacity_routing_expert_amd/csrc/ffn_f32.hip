@@ -69,7 +69,7 @@ hipError_t launch_ffn_up_f32(const moe_shape& s, const void* x, const int32_t* r
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   hipEvent_t t0, t1;
-  if (take_gemm_events(&t0, &t1))
+  if (take_launch_events(&t0, &t1))
     hipExtLaunchKernelGGL(k_ffn_up_f32, grid, dim3(256), 0, st, t0, t1, 0, (const float*)x,
                           row_token, offsets, s.n_experts, (const float*)w1, (const float*)b1,
                           (float*)h, s.d_model, s.d_ff, rows);
@@ -87,7 +87,7 @@ hipError_t launch_ffn_down_f32(const moe_shape& s, const void* h, const int32_t*
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   hipEvent_t t0, t1;
-  if (take_gemm_events(&t0, &t1))
+  if (take_launch_events(&t0, &t1))
     hipExtLaunchKernelGGL(k_ffn_down_f32, grid, dim3(256), 0, st, t0, t1, 0, (const float*)h,
                           offsets, s.n_experts, (const float*)w2, (const float*)b2, (float*)y,
                           s.d_model, s.d_ff, rows);

@@ -40,7 +40,7 @@
 // coalesced 16-byte stores of whole output rows.
 //
 // Timing: a launch can record its own kernel start and end in two events handed over with
-// arm_gemm_events (hipExtLaunchKernel), so nothing is queued between launches to time them.
+// arm_launch_events (hipExtLaunchKernel), so nothing is queued between launches to time them.
 //
 // Scheduling: the grid is an upper bound (the number of kept rows is only known on the
 // device).  Workgroups are dealt round-robin over the 8 XCDs, so block b runs on XCD b % 8;
@@ -49,8 +49,6 @@
 // operands' streams.  Each block finds the
 // expert of its token tile from expert_offsets with a wave prefix scan and exits if its tile
 // does not exist.
-#include <hip/hip_ext.h>
-
 #include "moe_internal.h"
 
 namespace moe {
@@ -880,12 +878,12 @@ namespace {
 thread_local hipEvent_t g_gemm_start = nullptr, g_gemm_stop = nullptr;
 }  // namespace
 
-void arm_gemm_events(hipEvent_t start, hipEvent_t stop) {
+void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
   g_gemm_start = start;
   g_gemm_stop = stop;
 }
 
-bool take_gemm_events(hipEvent_t* start, hipEvent_t* stop) {
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
   if (!g_gemm_start && !g_gemm_stop) return false;
   *start = g_gemm_start;
   *stop = g_gemm_stop;
@@ -923,7 +921,7 @@ hipError_t launch_grouped_gemm(const bf16_t* A, const int32_t* row_token, const 
   const int64_t grid = group_grid<GM>(mt_ub, (N + TNO - 1) / TNO);
   const int h_rows = HP ? (int)rows_ub : 0;  // packed H: the rows of the output array
   hipEvent_t t0, t1;
-  if (take_gemm_events(&t0, &t1))
+  if (take_launch_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NWV), lds, st, t0, t1, 0, A,
                           row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows,
                           h_rows);
@@ -953,7 +951,7 @@ hipError_t launch_grouped_gemm_loaders(const bf16_t* A, const int32_t* row_token
   const int64_t mt_ub = (rows_ub + TM - 1) / TM + E;  // token tiles <= rows_ub / TM + E
   const int64_t grid = group_grid<8>(mt_ub, (N + TN - 1) / TN);
   hipEvent_t t0, t1;
-  if (take_gemm_events(&t0, &t1))
+  if (take_launch_events(&t0, &t1))
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, t0, t1, 0, A,
                           row_token, offsets, W, bias, out, out_row, row_scale, E, N, K, a_rows);
   else

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include <atomic>
@@ -145,11 +146,24 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, const float* 
 hipError_t launch_gather_rows(const moe_shape& s, const void* x, const int32_t* row_token,
                               const int32_t* offsets, void* x_routed, hipStream_t st);
 
-// Kernel timing for the expert GEMMs: arm_gemm_events(start, stop) makes the next expert-GEMM
-// launch on this thread record its own start and stop in the two events (hipExtLaunchKernel,
-// no marker between launches); take_gemm_events hands them to that launch and disarms.
-void arm_gemm_events(hipEvent_t start, hipEvent_t stop);
-bool take_gemm_events(hipEvent_t* start, hipEvent_t* stop);
+// Kernel timing: arm_launch_events(start, stop) makes the next timed launch on this thread (an
+// expert GEMM, the router or the combine) record its own start and stop in the two events
+// (hipExtLaunchKernel, no marker between launches); take_launch_events hands them to that
+// launch and disarms.
+void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// One kernel launch that takes the armed events, if any.
+template <typename Kernel, typename... Args>
+hipError_t launch_timed(Kernel kern, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                        Args... args) {
+  hipEvent_t t0, t1;
+  if (take_launch_events(&t0, &t1))
+    hipExtLaunchKernelGGL(kern, grid, block, lds, st, t0, t1, 0, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, st, args...);
+  return hipGetLastError();
+}
 
 // rows_ub: an upper bound on the slot rows of the layout (max_rows(s) compact, E * capacity
 // padded); row_token entries < 0 are zero rows

@@ -537,9 +537,8 @@ hipError_t route_launch(const moe_shape& s, const TIn* x, const TIn* w, const fl
       err != hipSuccess)
     return err;
   const int64_t blocks = (s.T + TT - 1) / TT;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, x, w, b_router, s.T,
-                     s.d_model, s.n_experts, s.top_k, ids, gates, logits);
-  return hipGetLastError();
+  return launch_timed(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, x, w, b_router, s.T,
+                      s.d_model, s.n_experts, s.top_k, ids, gates, logits);
 }
 
 // Tile plan: 16 tokens per block; one or two tiles of 16 experts per pass over x, more experts
@@ -560,10 +559,9 @@ template <typename TIn, int RT, int NW>
 hipError_t route4_launch(const moe_shape& s, const TIn* x, const TIn* w, const float* b_router,
                          int32_t* ids, float* gates, float* logits, hipStream_t st) {
   constexpr int TT = 16 * RT, PF = 2;
-  hipLaunchKernelGGL((k_route_mfma4<TIn, RT, NW, PF>), dim3((unsigned)((s.T + TT - 1) / TT)),
-                     dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts, s.top_k,
-                     ids, gates, logits);
-  return hipGetLastError();
+  return launch_timed(k_route_mfma4<TIn, RT, NW, PF>, dim3((unsigned)((s.T + TT - 1) / TT)),
+                      dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts,
+                      s.top_k, ids, gates, logits);
 }
 
 template <typename TIn>
@@ -580,10 +578,9 @@ hipError_t route_any(const moe_shape& s, const TIn* x, const TIn* w, const float
   if (s.n_experts <= 8) {
     if (s.T >= 16384) return route4_launch<TIn, 4, 4>(s, x, w, b_router, ids, gates, logits, st);
     constexpr int NW = 4, PF = 2;
-    hipLaunchKernelGGL((k_route_mfma4k<TIn, NW, PF>), dim3((unsigned)((s.T + 15) / 16)),
-                       dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts,
-                       s.top_k, ids, gates, logits);
-    return hipGetLastError();
+    return launch_timed(k_route_mfma4k<TIn, NW, PF>, dim3((unsigned)((s.T + 15) / 16)),
+                        dim3(64 * NW), 0, st, x, w, b_router, s.T, s.d_model, s.n_experts,
+                        s.top_k, ids, gates, logits);
   }
   if (s.n_experts <= 16) return route_waves<TIn, 1>(s, x, w, b_router, ids, gates, logits, st);
   return route_waves<TIn, 2>(s, x, w, b_router, ids, gates, logits, st);

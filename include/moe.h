@@ -236,6 +236,20 @@ moe_status moe_layer_forward_profiled(const moe_shape* shape, const void* x,
  * disarms.  Errors: MOE_ERR_INVALID_ARGUMENT for a half-NULL pair or four NULL handles. */
 moe_status moe_set_gemm_timing(const moe_event_t* events);
 
+/* Router and combine kernel timing, for measurement: the kernel time of step 1 (router logits,
+ * softmax and top-k: "Dynamic Token Routing AI", "How it works") and of step 4 (the
+ * gate-weighted combine and residual: Worked Example, trace of token 0), without the launch
+ * gaps that events recorded between stages include.  Arms the NEXT call on this thread of
+ * moe_layer_forward (or its _profiled, _padded, _gated or _noalloc form):
+ *   events[0], [1]  start and end of the router's kernel
+ *   events[2], [3]  start and end of the combine's kernel
+ * recorded by those launches themselves (hipExtLaunchKernel).  The events are the caller's
+ * (hipEventCreate, timing enabled); a pair may be NULL (both handles).  An empty batch (T = 0)
+ * gets the events recorded back to back on the stream.  That next call consumes the arm even
+ * if it fails; other calls leave it armed.  events == NULL disarms.  Errors:
+ * MOE_ERR_INVALID_ARGUMENT for a half-NULL pair or four NULL handles. */
+moe_status moe_set_stage_timing(const moe_event_t* events);
+
 /* ---- Padded fixed-buffer layout.  "Some Tokens Do Not Get In", "Why there is a buffer": each
  * expert gets a buffer of `capacity` slots whether it fills it or not, and the empty slots are
  * computed anyway.  Same layer and same result as moe_layer_forward; only the layout of the

@@ -126,6 +126,19 @@ def test_gemm_timing_arm_checks_on_the_host(lib):
     assert lib.moe_set_gemm_timing(None) == 0  # disarmed before any layer call
 
 
+def test_stage_timing_arm_checks_on_the_host(lib):
+    """moe_set_stage_timing (router and combine kernels) only stores the handles, with the same
+    rules as the GEMM timing: a half-NULL pair or four NULLs are refused, one kernel's pair may
+    be NULL, NULL disarms."""
+    half = (ctypes.c_void_p * 4)(0, 2, 3, 4)
+    assert lib.moe_set_stage_timing(half) == 1
+    assert "events[0] and events[1]" in B.last_error()
+    assert lib.moe_set_stage_timing((ctypes.c_void_p * 4)(0, 0, 0, 0)) == 1
+    for ok in ((1, 2, 3, 4), (1, 2, 0, 0), (0, 0, 3, 4)):
+        assert lib.moe_set_stage_timing((ctypes.c_void_p * 4)(*ok)) == 0
+    assert lib.moe_set_stage_timing(None) == 0  # disarmed before any layer call
+
+
 def test_dispatch_gather_argument_checks(lib):
     """moe_dispatch takes x and x_routed together or not at all, and refuses overlapping ones,
     before anything is launched."""

@@ -1,5 +1,6 @@
-"""Kernel timing of the expert GEMMs (moe_set_gemm_timing): the timed call returns the untimed
-call's bits, and the four events bracket the two GEMM kernels in order."""
+"""Kernel timing of the expert GEMMs (moe_set_gemm_timing) and of the router and the combine
+(moe_set_stage_timing): the timed call returns the untimed call's bits, and the events bracket
+the kernels in order."""
 from __future__ import annotations
 
 import sys
@@ -29,6 +30,7 @@ def _gpu():
     B.lib()  # loud failure if the library is missing
     yield
     B.moe_set_gemm_timing(None)
+    B.moe_set_stage_timing(None)
     torch.cuda.synchronize()
 
 
@@ -135,3 +137,49 @@ def test_timed_layer_without_kept_rows():
     torch.cuda.synchronize()
     assert torch.equal(bits(res["out"]), bits(dev["x"]))  # every token dropped: out is x
     check_events(evs, empty=True)
+
+
+@pytest.mark.parametrize("T,d,f,E,k,C,dt", [
+    (1000, 136, 264, 8, 2, 1.0, "bf16"),   # router for at most 8 experts (d slices)
+    (3000, 64, 96, 40, 4, 1.0, "bf16"),    # 16 x 16 router tiles, mid-size dispatch
+    (65, 12, 20, 8, 2, 0.75, "f32"),       # fp32 inputs
+])
+def test_stage_timed_layer_same_bits(T, d, f, E, k, C, dt):
+    """Router and combine kernels timed together with both GEMMs: same bits as an untimed call,
+    and the eight events in launch order (router, up-projection, down-projection, combine)."""
+    say(f"[stage timing] layer T={T} d={d} f={f} E={E} k={k} {dt}")
+    inp = W.make_shape_inputs(T, d, f, E, dt, seed=T * 3 + E, router_bias_std=1.0)
+    dev = L.upload(inp, DEV)
+    cap = O.capacity(T, k, E, C)
+    a = L.layer_forward(dev, k, cap)
+    gev, sev = new_events(), new_events()
+    B.moe_set_gemm_timing(gev)
+    B.moe_set_stage_timing(sev)
+    b = L.layer_forward(dev, k, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a["out"]), bits(b["out"]))
+    assert torch.equal(a["ids"], b["ids"]) and torch.equal(a["slot_of"], b["slot_of"])
+    route = sev[0].elapsed_time(sev[1])
+    combine = sev[2].elapsed_time(sev[3])
+    say(f"    route {route * 1e3:.1f} us, combine {combine * 1e3:.1f} us")
+    assert route > 0.0 and combine > 0.0
+    assert sev[1].elapsed_time(gev[0]) >= 0.0  # the router ends before the up-projection starts
+    assert gev[3].elapsed_time(sev[2]) >= 0.0  # the down-projection ends before the combine
+    # the arm was consumed
+    t_before = sev[0].elapsed_time(sev[3])
+    L.layer_forward(dev, k, cap)
+    torch.cuda.synchronize()
+    assert sev[0].elapsed_time(sev[3]) == t_before
+
+
+def test_stage_timing_of_an_empty_batch():
+    """T = 0 launches nothing: the router and combine events are recorded back to back."""
+    inp = W.make_shape_inputs(4, 64, 64, 4, "bf16", seed=3)
+    dev = L.upload(inp, DEV)
+    dev["x"] = dev["x"][:0]
+    sev = new_events()
+    B.moe_set_stage_timing(sev)
+    res = L.layer_forward(dev, 2, 0)
+    torch.cuda.synchronize()
+    assert res["out"].shape == (0, 64)
+    assert sev[0].elapsed_time(sev[1]) >= 0.0 and sev[2].elapsed_time(sev[3]) >= 0.0
