@@ -344,7 +344,7 @@ moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pa
                      moe_event_t const* events, const hipEvent_t* tev) {
   const int64_t rows = s.T * (int64_t)s.top_k;
   MOE_TRY(run_timed_stage(tev && tev[0] ? tev : nullptr, st,
-                         "expert up-projection (pair order)", [&] {
+                          "expert up-projection (pair order)", [&] {
     return launch_ffn_up_pairs(s, x, row_token, sorted_pairs, offsets, w1, gated ? nullptr : b1,
                                h, rows, gated, st);
   }));
@@ -352,7 +352,7 @@ moe_status ffn_pairs(const moe_shape& s, const void* x, const int32_t* sorted_pa
   if (events && (err = hipEventRecord((hipEvent_t)events[3], st)) != hipSuccess)
     return device_error(err, "hipEventRecord");
   MOE_TRY(run_timed_stage(tev && tev[2] ? tev + 2 : nullptr, st,
-                         "expert down-projection (pair order)", [&] {
+                          "expert down-projection (pair order)", [&] {
     return launch_ffn_down_pairs(s, h, sorted_pairs, offsets, w2, gated ? nullptr : b2, weights,
                                  pair_rows, rows, st);
   }));
